@@ -1,0 +1,360 @@
+"""Pins of the fp64 oracle against things other than itself: a hand-derived
+worked example, pure-Python brute force, closed forms, invariants, a library
+routine the fill case reduces to (torch SDPA in float64), and exact rational
+arithmetic for the quantisers.  CPU only."""
+
+import json
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import h2o_oracle as O
+from h2o_kv_cache_sdpa_amd import workloads as W
+from tests.bruteforce_h2o import BruteCache
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# worked example (tests/golden)
+# ---------------------------------------------------------------------------
+
+def _val(s):
+    s = str(s)
+    if s.startswith("ln:"):
+        return math.log(int(s[3:]))
+    if "+" in s:
+        a, b = s.split("+")
+        return float(Fraction(a) + Fraction(b))
+    return float(Fraction(s))
+
+
+def test_worked_example_golden():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example_h2o_step.json")))
+    sh, inp, exp = ex["shape"], ex["inputs"], ex["expected"]
+    B, Hq, Hkv, D, C, T = (sh[k] for k in ("B", "Hq", "Hkv", "D", "C", "T"))
+    oc = O.OracleCache(B, Hq, Hkv, D, C, scale=sh["scale"])
+    oc.k[0, 0, :, 0] = [_val(x) for x in inp["k_cache"]]
+    oc.v[0, 0, :, 0] = [_val(x) for x in inp["v_cache"]]
+    oc.phi[0, 0] = [_val(x) for x in inp["phi_prior"]]
+    oc.token_pos[0, 0] = inp["token_pos_prior"]
+    oc.n_occ, oc.pos = sh["n_occ"], sh["pos"]
+    q = np.zeros((1, 2, 2, 1))
+    q[0, 0, :, 0] = [_val(x) for x in inp["q_head0"]]
+    q[0, 1, :, 0] = [_val(x) for x in inp["q_head1"]]
+    kn = np.array([_val(x) for x in inp["k_new"]]).reshape(1, 1, 2, 1)
+    vn = np.array([_val(x) for x in inp["v_new"]]).reshape(1, 1, 2, 1)
+    r = oc.step(q, kn, vn)
+    close = lambda a, b: np.testing.assert_allclose(a, [_val(x) for x in b], rtol=1e-13, atol=1e-13)
+    close(r["w"][0, 0], exp["w"])
+    close(r["out"][0, 0, :, 0], exp["out_head0"])
+    close(r["out"][0, 1, :, 0], exp["out_head1"])
+    close(r["lse"][0, 0], exp["lse_head0"])
+    close(r["lse"][0, 1], exp["lse_head1"])
+    close(r["phi_updated"][0, 0], exp["phi_updated"])
+    assert r["slots"][0, 0].tolist() == exp["slots"]
+    close(oc.phi[0, 0], exp["phi_after"])
+    close(oc.k[0, 0, :, 0], exp["k_cache_after"])
+    close(oc.v[0, 0, :, 0], exp["v_cache_after"])
+    assert oc.token_pos[0, 0].tolist() == exp["token_pos_after"]
+
+
+# ---------------------------------------------------------------------------
+# brute force on a tiny stream with evictions
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_bruteforce_tiny_stream(seed):
+    B, Hq, Hkv, D, C, T = 2, 4, 2, 4, 8, 2
+    scale = float(np.float32(1 / math.sqrt(D)))
+    oc = O.OracleCache(B, Hq, Hkv, D, C, scale=scale)
+    bc = BruteCache(B, Hq, Hkv, D, C, scale)
+    for step in range(8):  # 4 fill + 4 evicting steps
+        ch = W.random_chunk([100 + seed, step], B, Hq, Hkv, T, D, "f32", hh_frac=0.5)
+        q, kn, vn = ch["q"].f64, ch["k"].f64, ch["v"].f64
+        r = oc.step(q, kn, vn)
+        out_b, w_b, slots_b = bc.step(q.tolist(), kn.tolist(), vn.tolist())
+        np.testing.assert_allclose(r["out"], np.array(out_b), rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(r["w"], np.array(w_b), rtol=1e-12, atol=1e-13)
+        assert r["slots"].tolist() == slots_b
+        np.testing.assert_allclose(oc.phi, np.array(bc.phi), rtol=1e-12, atol=1e-13)
+        np.testing.assert_array_equal(oc.k, np.array(bc.k))
+        np.testing.assert_array_equal(oc.v, np.array(bc.v))
+        assert oc.token_pos.tolist() == bc.tpos
+    assert oc.n_occ == C and oc.pos == 8 * T
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms
+# ---------------------------------------------------------------------------
+
+def _random_state(seed, B, Hq, Hkv, D, C, n_occ, dtype="f32", hh=0.0):
+    k, v, sc, tp, _ = W.random_cache(seed, B, Hkv, C, D, n_occ, dtype, hh_frac=hh)
+    oc = O.OracleCache(B, Hq, Hkv, D, C)
+    oc.k[:], oc.v[:] = k.f64, v.f64
+    oc.phi[:] = sc.astype(np.float64)
+    oc.token_pos[:] = tp
+    oc.n_occ, oc.pos = n_occ, n_occ
+    return oc
+
+
+@pytest.mark.parametrize("n_occ", [0, 24, 64])
+def test_weight_sums_total_and_sign(n_occ):
+    B, Hq, Hkv, D, C, T = 2, 6, 2, 16, 64, 8
+    oc = _random_state([7, n_occ], B, Hq, Hkv, D, C, n_occ, hh=0.1)
+    ch = W.random_chunk([8, n_occ], B, Hq, Hkv, T, D, "bf16", hh_frac=0.25)
+    out, w, lse = O.attend_chunk(ch["q"].f64, oc.k, oc.v, n_occ, ch["k"].f64, ch["v"].f64, oc.scale)
+    qg = Hq // Hkv
+    # every query's weights sum to one, so the group total is T * q_g
+    np.testing.assert_allclose(w.sum(axis=-1), T * qg, rtol=1e-12)
+    assert (w >= 0).all()
+    # a new key t' is seen by queries t'..T-1 only: its sum is at most q_g*(T - t')
+    assert (w[..., n_occ:] <= qg * (T - np.arange(T)) + 1e-12).all()
+
+
+@pytest.mark.parametrize("n_occ", [0, 5, 32])
+def test_zero_queries_closed_form(n_occ):
+    """Q = 0: every visible key gets weight 1/(n_occ + i + 1) in row i."""
+    B, Hq, Hkv, D, C, T = 1, 4, 2, 8, 32, 8
+    oc = _random_state([9, n_occ], B, Hq, Hkv, D, C, n_occ)
+    ch = W.random_chunk([10, n_occ], B, Hq, Hkv, T, D, "f32", q_zero=True)
+    out, w, lse = O.attend_chunk(ch["q"].f64, oc.k, oc.v, n_occ, ch["k"].f64, ch["v"].f64, oc.scale)
+    qg = Hq // Hkv
+    harm = lambda n: sum(1.0 / k for k in range(1, n + 1))
+    np.testing.assert_allclose(w[..., :n_occ], qg * (harm(n_occ + T) - harm(n_occ)), rtol=1e-13)
+    for t in range(T):
+        expect = qg * sum(1.0 / (n_occ + i + 1) for i in range(t, T))
+        np.testing.assert_allclose(w[..., n_occ + t], expect, rtol=1e-13)
+    for h in range(Hq):
+        g = h // qg
+        for i in range(T):
+            vis = np.concatenate([oc.v[0, g, :n_occ], ch["v"].f64[0, g, :i + 1]])
+            np.testing.assert_allclose(out[0, h, i], vis.mean(axis=0), rtol=1e-12, atol=1e-14)
+            np.testing.assert_allclose(lse[0, h, i], math.log(n_occ + i + 1), rtol=1e-13)
+
+
+def test_fill_stream_equals_causal_sdpa():
+    """While the cache is filling, the step is exact causal attention over the
+    whole prefix (torch SDPA, float64, CPU; GQA by repeating KV heads)."""
+    B, Hq, Hkv, D, C, T = 2, 8, 2, 32, 64, 16
+    qg = Hq // Hkv
+    oc = O.OracleCache(B, Hq, Hkv, D, C)
+    ks, vs = [], []
+    for step in range(C // T):
+        ch = W.random_chunk([11, step], B, Hq, Hkv, T, D, "bf16", hh_frac=0.1)
+        r = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        ks.append(ch["k"].f64)
+        vs.append(ch["v"].f64)
+        K = torch.from_numpy(np.concatenate(ks, axis=2)).repeat_interleave(qg, dim=1)
+        V = torch.from_numpy(np.concatenate(vs, axis=2)).repeat_interleave(qg, dim=1)
+        Q = torch.from_numpy(ch["q"].f64)
+        n = K.shape[2]
+        mask = torch.arange(n)[None, :] <= (n - T + torch.arange(T))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask, scale=oc.scale)
+        np.testing.assert_allclose(r["out"], ref.numpy(), rtol=1e-11, atol=1e-12)
+        assert r["slots"].tolist() == [[list(range(step * T, step * T + T))] * Hkv] * B
+
+
+def test_score_conservation_on_evict():
+    B, Hq, Hkv, D, C, T = 1, 4, 2, 16, 48, 8
+    oc = _random_state([12], B, Hq, Hkv, D, C, C, hh=0.05)
+    before = oc.phi.copy()
+    ch = W.random_chunk([13], B, Hq, Hkv, T, D, "bf16", hh_frac=0.25)
+    r = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+    qg = Hq // Hkv
+    for b in range(B):
+        for g in range(Hkv):
+            R = r["slots"][b, g]
+            lost = (before[b, g, R] + r["w"][b, g, R]).sum()
+            np.testing.assert_allclose(oc.phi[b, g].sum(), before[b, g].sum() + T * qg - lost, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def test_bottom_t_matches_tuple_sort_with_ties():
+    rng = np.random.default_rng(14)
+    B, Hkv, C, T = 3, 2, 200, 37
+    # few distinct values -> many exact ties
+    phi = rng.integers(0, 9, size=(B, Hkv, C)).astype(np.float64) * 0.25
+    got = O.bottom_t(phi, C, C, T)
+    for b in range(B):
+        for g in range(Hkv):
+            ranked = sorted((phi[b, g, j], j) for j in range(C))
+            assert got[b, g].tolist() == sorted(j for _, j in ranked[:T])
+
+
+def test_all_tied_zero_queries_evict_lowest_indices():
+    """Q = 0 and equal prior scores: every old slot receives an identical sum, so
+    all are tied and the lowest T indices are evicted."""
+    B, Hq, Hkv, D, C, T = 1, 4, 2, 8, 32, 8
+    oc = _random_state([15], B, Hq, Hkv, D, C, C)
+    oc.phi[:] = 1.5
+    ch = W.random_chunk([16], B, Hq, Hkv, T, D, "f32", q_zero=True)
+    r = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+    assert (r["slots"] == np.arange(T)).all()
+
+
+def test_fill_then_evict_straddle_rejected():
+    with pytest.raises(ValueError):
+        O.bottom_t(np.zeros((1, 1, 10)), 6, 10, 8)
+
+
+# ---------------------------------------------------------------------------
+# quantisers: exact rational arithmetic (Fraction) and bounds
+# ---------------------------------------------------------------------------
+
+def _f32(x):
+    """Round a Python float (already correctly rounded from the exact value) to
+    float32.  Double rounding exact -> fp64 -> fp32 is innocuous for + - * /
+    (53 >= 2*24 + 2; S. Figueroa, 'When is double rounding innocuous?', 1995)."""
+    return struct.unpack("f", struct.pack("f", x))[0]
+
+
+def _rne(x):
+    return int(round(x))  # Python rounds half to even
+
+
+def _all_finite_bf16():
+    bits = np.arange(65536, dtype=np.uint32)
+    vals = (bits << 16).view(np.float32)
+    return vals[np.isfinite(vals)]
+
+
+@pytest.mark.parametrize("s_val", [0.0078125, 0.01, 0.0371, 1.0, 3.5e-5, 0.5])
+def test_int8_codes_exhaustive_bf16(s_val):
+    s16 = np.float16(s_val)
+    s = Fraction(float(s16))
+    A = np.float32(127 * float(s16))  # exact: 7-bit x 11-bit product
+    xs = _all_finite_bf16()
+    xs = xs[np.abs(xs) <= A]
+    rows = np.stack([xs, np.full_like(xs, A)], axis=1)
+    codes, scales = O.quantize_int8(rows)
+    assert (scales == s16).all()
+    for x, c in zip(xs[::7].tolist(), codes[::7, 0].tolist()):
+        q = _f32(float(Fraction(x) / s))
+        assert c == max(-127, min(127, _rne(q))), (x, c)
+    assert (codes[:, 1] == 127).all()
+
+
+def test_int8_scale_rounding_and_bounds():
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((4000, 64)) * rng.uniform(0.01, 30, (4000, 1))).astype(np.float32)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+    codes, s16 = O.quantize_int8(x)
+    a = np.abs(x).max(axis=1)
+    for ai, si in zip(a[:500].tolist(), s16[:500].tolist()):
+        # fp16(fp32(a/127)) == fp16(exact a/127): innocuous double rounding (24 >= 2*11 + 2)
+        assert float(np.float16(float(Fraction(ai) / 127))) == si
+    xh = O.dequantize_int8(codes, s16)
+    s = s16.astype(np.float64)[:, None]
+    assert (np.abs(x - xh) <= s / 2 * (1 + 1e-6)).all()
+    am = np.argmax(np.abs(x), axis=1)
+    assert (np.abs(codes[np.arange(len(x)), am]) == 127).all()
+
+
+@pytest.mark.parametrize("lo,s_val", [(-2.0, 0.25), (-1.375, 0.3), (0.5, 0.0625), (-3.0, 1.0)])
+def test_int4_codes_exhaustive_bf16(lo, s_val):
+    s16, z16 = np.float16(s_val), np.float16(lo)
+    s, z = Fraction(float(s16)), Fraction(float(z16))
+    hi = float(z + 15 * s)
+    assert np.float32(hi) == hi
+    xs = _all_finite_bf16()
+    xs = xs[(xs >= np.float32(float(z16))) & (xs <= np.float32(hi))]
+    rows = np.stack([xs, np.full_like(xs, float(z16)), np.full_like(xs, hi)], axis=1)
+    rows = np.concatenate([rows, rows[:, :1]], axis=1)  # even D
+    packed, scales, zeros = O.quantize_int4(rows)
+    assert (scales == s16).all() and (zeros == z16).all()
+    codes = O.unpack_nibbles(packed)
+    for x, c in zip(xs.tolist(), codes[:, 0].tolist()):
+        d = _f32(float(Fraction(x) - z))
+        q = _f32(float(Fraction(d) / s))
+        assert c == max(0, min(15, _rne(q))), (x, c)
+    assert (codes[:, 1] == 0).all() and (codes[:, 2] == 15).all()
+
+
+def test_int4_bounds_and_nibble_order():
+    rng = np.random.default_rng(18)
+    x = (rng.standard_normal((3000, 128)) * 2).astype(np.float32)
+    x = W.bf16_bits_to_f32(W.f32_to_bf16_bits(x))
+    packed, s16, z16 = O.quantize_int4(x)
+    c = O.unpack_nibbles(packed)
+    assert c.max() <= 15
+    # element 2k sits in the low nibble of byte k
+    assert (packed[:, 0] & 0x0F == c[:, 0]).all() and (packed[:, 0] >> 4 == c[:, 1]).all()
+    xh = O.dequantize_int4(packed, s16, z16)
+    s = s16.astype(np.float64)[:, None]
+    z = z16.astype(np.float64)[:, None]
+    # unclamped elements are within half a step; the zero point rounding can push
+    # the row minimum below z by at most |z - min|
+    inside = (x >= z) & (x <= z + 15 * s)
+    assert (np.abs(x - xh)[inside] <= s.repeat(128, 1)[inside] / 2 * (1 + 1e-6)).all()
+    assert (c[np.arange(len(x)), np.argmin(x, axis=1)] == 0).all()
+
+
+def test_quantisers_constant_rows_give_zero_codes():
+    x = np.zeros((3, 16), np.float32)
+    c8, s8 = O.quantize_int8(x)
+    assert (c8 == 0).all() and (s8 == 0).all()
+    x[:] = 1.25
+    p4, s4, z4 = O.quantize_int4(x)
+    assert (p4 == 0).all() and (s4 == 0).all() and (z4 == np.float16(1.25)).all()
+    np.testing.assert_array_equal(O.dequantize_int4(p4, s4, z4), x)
+
+
+def test_quantised_stream_attends_dequantised_values():
+    """A quantised cache holds codes; later chunks attend to c*s (+z).  The
+    chunk attends to its own keys at input precision (reading R9)."""
+    B, Hq, Hkv, D, C, T = 1, 4, 2, 16, 16, 8
+    for fmt in ("int8", "int4"):
+        oc = O.OracleCache(B, Hq, Hkv, D, C, fmt=fmt)
+        ch0 = W.random_chunk([19, 0], B, Hq, Hkv, T, D, "bf16")
+        oc.step(ch0["q"].f64, ch0["k"].f64, ch0["v"].f64)
+        if fmt == "int8":
+            kh = O.dequantize_int8(*O.quantize_int8(ch0["k"].f32))
+        else:
+            kh = O.dequantize_int4(*O.quantize_int4(ch0["k"].f32))
+        np.testing.assert_array_equal(oc.k[:, :, :T], kh)
+        assert not np.array_equal(kh, ch0["k"].f64)
+
+
+def _f16(x):
+    """Round a Python float to fp16 (struct 'e' rounds to nearest even)."""
+    return struct.unpack("e", struct.pack("e", x))[0]
+
+
+@pytest.mark.parametrize("fmt", ["int8", "int4"])
+def test_quantisers_fp32_rows_by_fractions(fmt):
+    """fp32 rows whose extremes are not fp16-exact: every step of the quantiser
+    recomputed with exact rationals and explicit fp32 / fp16 rounding."""
+    rng = np.random.default_rng(20)
+    x = (rng.standard_normal((60, 32)) * rng.uniform(0.1, 9, (60, 1))).astype(np.float32)
+    if fmt == "int8":
+        codes, s16 = O.quantize_int8(x)
+        for r in range(len(x)):
+            row = [float(v) for v in x[r]]
+            a = max(abs(v) for v in row)
+            s = _f16(_f32(float(Fraction(a) / 127)))
+            assert float(s16[r]) == s
+            for v, c in zip(row, codes[r].tolist()):
+                assert c == max(-127, min(127, _rne(_f32(float(Fraction(v) / Fraction(s))))))
+    else:
+        packed, s16, z16 = O.quantize_int4(x)
+        codes = O.unpack_nibbles(packed)
+        for r in range(len(x)):
+            row = [float(v) for v in x[r]]
+            lo, hi = min(row), max(row)
+            z = _f16(lo)
+            assert z != lo  # the zero point really is rounded here
+            span = _f32(float(Fraction(hi) - Fraction(lo)))
+            s = _f16(_f32(float(Fraction(span) / 15)))
+            assert float(z16[r]) == z and float(s16[r]) == s
+            for v, c in zip(row, codes[r].tolist()):
+                d = _f32(float(Fraction(v) - Fraction(z)))
+                assert c == max(0, min(15, _rne(_f32(float(Fraction(d) / Fraction(s))))))
