@@ -1,0 +1,171 @@
+"""ctypes binding of libh2o.so (declared in include/h2o.h).
+
+Argument marshalling only: every step of the chunk step runs in the HIP
+library.  Tensors are torch tensors on the GPU (PyTorch supplies device memory
+and streams); their data pointers and the current stream's handle are passed
+through unchanged.  If the library is missing, loading raises -- there is no
+fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libh2o.so")
+
+H2O_OK, H2O_EINVAL, H2O_EUNSUPPORTED, H2O_EWORKSPACE, H2O_EHIP = 0, -1, -2, -3, -4
+H2O_F32, H2O_BF16 = 0, 1
+H2O_CACHE_NATIVE, H2O_CACHE_INT8, H2O_CACHE_INT4 = 0, 1, 2
+H2O_POLICY_H2O = 0
+
+DTYPES = {"f32": H2O_F32, "bf16": H2O_BF16}
+FORMATS = {"native": H2O_CACHE_NATIVE, "int8": H2O_CACHE_INT8, "int4": H2O_CACHE_INT4}
+
+EXPORTS = (
+    "h2o_abi_version", "h2o_status_str", "h2o_last_hip_error", "h2o_workspace_bytes",
+    "h2o_sdpa_scoresum", "h2o_evict_topk", "kv_scatter", "kv_quant_pack",
+    "kv_dequant_unpack", "h2o_chunk_step",
+)
+
+
+class H2ODims(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("D", ctypes.c_int32), ("C", ctypes.c_int32), ("T", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("cache_fmt", ctypes.c_int32), ("policy", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+    ]
+
+
+class H2OCacheBufs(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
+        ("k_zero", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("scores", ctypes.c_void_p), ("token_pos", ctypes.c_void_p),
+    ]
+
+
+class H2OError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = f"{fn} failed: {status_str(status)} ({status})"
+        if status == H2O_EHIP:
+            msg += f", hipError {lib().h2o_last_hip_error()}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib():
+    """Load libh2o.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} not built: run __graft_entry__.build() "
+                           "or python -m h2o_kv_cache_sdpa_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, S, I32, I64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_int64
+    pd, pc = ctypes.POINTER(H2ODims), ctypes.POINTER(H2OCacheBufs)
+    L.h2o_abi_version.restype = ctypes.c_int
+    L.h2o_abi_version.argtypes = []
+    L.h2o_status_str.restype = ctypes.c_char_p
+    L.h2o_status_str.argtypes = [ctypes.c_int]
+    L.h2o_last_hip_error.restype = ctypes.c_int
+    L.h2o_last_hip_error.argtypes = []
+    L.h2o_workspace_bytes.restype = S
+    L.h2o_workspace_bytes.argtypes = [pd]
+    L.h2o_sdpa_scoresum.restype = ctypes.c_int
+    L.h2o_sdpa_scoresum.argtypes = [pd, pc, I32, P, P, P, P, P, P, P, S, P]
+    L.h2o_evict_topk.restype = ctypes.c_int
+    L.h2o_evict_topk.argtypes = [pd, pc, I32, I64, P, P, P, S, P]
+    for name in ("kv_scatter", "kv_quant_pack"):
+        f = getattr(L, name)
+        f.restype = ctypes.c_int
+        f.argtypes = [pd, pc, P, P, P, P]
+    L.kv_dequant_unpack.restype = ctypes.c_int
+    L.kv_dequant_unpack.argtypes = [pd, pc, I32, P, P, P]
+    L.h2o_chunk_step.restype = ctypes.c_int
+    L.h2o_chunk_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, P, S, P]
+    _lib = L
+    return L
+
+
+def status_str(status):
+    return lib().h2o_status_str(int(status)).decode()
+
+
+def make_dims(B, Hq, Hkv, D, C, T, dtype="bf16", cache_fmt="native", scale=0.0, policy=0):
+    return H2ODims(B, Hq, Hkv, D, C, T, DTYPES.get(dtype, dtype), FORMATS.get(cache_fmt, cache_fmt),
+                   policy, float(scale))
+
+
+def workspace_bytes(dims):
+    return int(lib().h2o_workspace_bytes(ctypes.byref(dims)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def cache_struct(k, v, scores=None, token_pos=None, k_scale=None, v_scale=None, k_zero=None,
+                 v_zero=None):
+    f = lambda t: None if t is None else t.data_ptr()
+    return H2OCacheBufs(f(k), f(v), f(k_scale), f(v_scale), f(k_zero), f(v_zero), f(scores),
+                        f(token_pos))
+
+
+def _check(fn, st):
+    if st != H2O_OK:
+        raise H2OError(fn, st)
+
+
+def h2o_sdpa_scoresum(dims, cache, n_occ, q, k_new, v_new, out, wsum, lse, ws, stream=None):
+    st = lib().h2o_sdpa_scoresum(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), _ptr(q),
+                                 _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(wsum), _ptr(lse),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("h2o_sdpa_scoresum", st)
+
+
+def h2o_evict_topk(dims, cache, n_occ, pos, wsum, slot_log, ws=None, stream=None):
+    nb = 0 if ws is None else ws.numel() * ws.element_size()
+    st = lib().h2o_evict_topk(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
+                              _ptr(wsum), _ptr(slot_log), _ptr(ws), nb, _stream(stream))
+    _check("h2o_evict_topk", st)
+
+
+def kv_scatter(dims, cache, k_new, v_new, slot_log, stream=None):
+    st = lib().kv_scatter(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
+                          _ptr(slot_log), _stream(stream))
+    _check("kv_scatter", st)
+
+
+def kv_quant_pack(dims, cache, k_new, v_new, slot_log, stream=None):
+    st = lib().kv_quant_pack(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
+                             _ptr(slot_log), _stream(stream))
+    _check("kv_quant_pack", st)
+
+
+def kv_dequant_unpack(dims, cache, n_slots, k_out, v_out, stream=None):
+    st = lib().kv_dequant_unpack(ctypes.byref(dims), ctypes.byref(cache), int(n_slots),
+                                 _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check("kv_dequant_unpack", st)
+
+
+def h2o_chunk_step(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, ws, stream=None):
+    st = lib().h2o_chunk_step(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
+                              _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(wsum),
+                              _ptr(slot_log), _ptr(ws), ws.numel() * ws.element_size(),
+                              _stream(stream))
+    _check("h2o_chunk_step", st)

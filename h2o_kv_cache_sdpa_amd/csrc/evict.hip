@@ -1,0 +1,208 @@
+// Score accumulate + slot selection + replay log + seeding, one workgroup of
+// 1024 threads per (b, KV head).
+//
+// H2O score = cumulative sum of attention weights; the lowest-scoring slots are
+// overwritten (aimodeling article on KeysAndValues; "Learning how to Forget",
+// §3.1.1).  While the cache has room it fills left to right (§3.1).  Every
+// decision goes to the replay log (§3.2).
+//
+// Selection of the T smallest keys under (score, slot index) is an MSB-first
+// radix select over the order-preserving uint32 image of the fp32 scores
+// (4 passes of 8 bits, LDS histograms with wave-aggregated increments), then
+// an index-ordered compaction: a slot is taken if its key is below the
+// threshold key, or equal to it and among the first k such slots.  The replay
+// log row comes out in ascending slot order; chunk token t goes to the t-th
+// entry.  Each thread owns ITEMS consecutive slots held in registers, so no
+// thread reads a slot another thread writes.
+
+#include "device_util.hpp"
+#include "h2o_internal.hpp"
+
+namespace h2o {
+namespace {
+
+constexpr int NT = 1024;
+constexpr int NWAVES = NT / 64;
+
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0 ranks with +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Block-wide exclusive scan of two counters; returns the prefixes for this thread.
+__device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb,
+                                            uint32_t *sh_a, uint32_t *sh_b) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t na = __shfl_up(ia, o), nb = __shfl_up(ib, o);
+    if (lane >= o) {
+      ia += na;
+      ib += nb;
+    }
+  }
+  if (lane == 63) {
+    sh_a[wave] = ia;
+    sh_b[wave] = ib;
+  }
+  __syncthreads();
+  uint32_t pa = 0, pb = 0;
+  for (int w = 0; w < wave; ++w) {
+    pa += sh_a[w];
+    pb += sh_b[w];
+  }
+  ea = pa + ia - a;
+  eb = pb + ib - b;
+}
+
+template <int ITEMS>
+__global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_sel, sh_k;
+  __shared__ uint32_t sh_a[NWAVES], sh_b[NWAVES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int grp = blockIdx.x;
+  const int C = a.C, T = a.T, n_occ = a.n_occ;
+  const int n_keys = n_occ + T;
+  float *phi = a.scores + static_cast<size_t>(grp) * C;
+  const float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
+  int32_t *log = a.slot_log + static_cast<size_t>(grp) * T;
+  int32_t *tp = a.token_pos ? a.token_pos + static_cast<size_t>(grp) * C : nullptr;
+
+  if (n_occ + T <= C) {  // filling: left to right
+    for (int j = tid; j < n_occ; j += NT) phi[j] = phi[j] + w[j];
+    for (int t = tid; t < T; t += NT) {
+      const int slot = n_occ + t;
+      log[t] = slot;
+      phi[slot] = w[n_occ + t];
+      if (tp) tp[slot] = static_cast<int32_t>(a.pos + t);
+    }
+    return;
+  }
+
+  // evicting: n_occ == C
+  const int base = tid * ITEMS;
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int j = base + k;
+    key[k] = 0xffffffffu;
+    if (j < C) {
+      const float f = phi[j] + w[j];
+      phi[j] = f;
+      key[k] = ordered_key(f);
+    }
+  }
+
+  uint32_t prefix = 0, pmask = 0, need = static_cast<uint32_t>(T);
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int e = tid; e < 256; e += NT) hist[e] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const bool act = (base + k < C) && ((key[k] & pmask) == prefix);
+      const uint32_t digit = (key[k] >> shift) & 255u;
+      uint64_t pending = __ballot(act);
+      while (pending) {
+        const int leader = __builtin_ctzll(pending);
+        const uint32_t ld = __shfl(digit, leader);
+        const uint64_t same = __ballot(act && digit == ld) & pending;
+        if (lane == leader) atomicAdd(&hist[ld], static_cast<uint32_t>(__popcll(same)));
+        pending &= ~same;
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1];
+      const uint32_t c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+      const uint32_t s = c0 + c1 + c2 + c3;
+      uint32_t inc = s;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t n = __shfl_up(inc, o);
+        if (tid >= o) inc += n;
+      }
+      const uint32_t excl = inc - s;
+      if (excl < need && need <= inc) {
+        uint32_t c = excl;
+        uint32_t d = 4u * tid;
+        if (c + c0 < need) {
+          c += c0;
+          ++d;
+          if (c + c1 < need) {
+            c += c1;
+            ++d;
+            if (c + c2 < need) {
+              c += c2;
+              ++d;
+            }
+          }
+        }
+        sh_sel = d;
+        sh_k = need - c;
+      }
+    }
+    __syncthreads();
+    prefix |= sh_sel << shift;
+    pmask |= 255u << shift;
+    need = sh_k;
+    __syncthreads();
+  }
+  const uint32_t theta = prefix;  // key of the T-th smallest slot
+  const uint32_t take_eq = need;  // how many slots with key == theta are taken
+
+  uint32_t nl = 0, ne = 0;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    if (base + k < C) {
+      nl += key[k] < theta;
+      ne += key[k] == theta;
+    }
+  }
+  uint32_t less_before, eq_before;
+  block_scan2(nl, ne, less_before, eq_before, sh_a, sh_b);
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const int j = base + k;
+    if (j >= C) break;
+    int out = -1;
+    if (key[k] < theta) {
+      out = static_cast<int>(less_before + min(eq_before, take_eq));
+      ++less_before;
+    } else if (key[k] == theta) {
+      if (eq_before < take_eq) out = static_cast<int>(less_before + eq_before);
+      ++eq_before;
+    }
+    if (out >= 0) {
+      log[out] = j;
+      phi[j] = w[C + out];
+      if (tp) tp[j] = static_cast<int32_t>(a.pos + out);
+    }
+  }
+}
+
+template <int ITEMS>
+hipError_t launch_items(const EvictArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(evict_kernel<ITEMS>, dim3(a.groups), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_evict(const EvictArgs &a, hipStream_t s) {
+  const int per = (a.C + NT - 1) / NT;
+  if (per <= 1) return launch_items<1>(a, s);
+  if (per <= 2) return launch_items<2>(a, s);
+  if (per <= 4) return launch_items<4>(a, s);
+  if (per <= 8) return launch_items<8>(a, s);
+  if (per <= 16) return launch_items<16>(a, s);
+  if (per <= 32) return launch_items<32>(a, s);
+  return launch_items<64>(a, s);
+}
+
+}  // namespace h2o

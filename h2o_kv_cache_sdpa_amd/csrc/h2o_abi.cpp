@@ -1,0 +1,284 @@
+// C ABI of libh2o.so: host-side validation and dispatch.  Every argument is
+// checked before anything is enqueued; no entry point allocates, frees or
+// synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/h2o.h"
+#include "h2o_internal.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validates sizes and enums.  Returns H2O_OK, H2O_EINVAL or H2O_EUNSUPPORTED.
+int check_dims(const h2o_dims *d) {
+  if (!d) return H2O_EINVAL;
+  if (d->B < 1 || d->Hq < 1 || d->Hkv < 1 || d->C < 1 || d->T < 1 || d->D < 1) return H2O_EINVAL;
+  if (d->Hq % d->Hkv != 0) return H2O_EINVAL;
+  if (d->dtype != H2O_F32 && d->dtype != H2O_BF16) return H2O_EINVAL;
+  if (d->cache_fmt < H2O_CACHE_NATIVE || d->cache_fmt > H2O_CACHE_INT4) return H2O_EINVAL;
+  if (!(std::isfinite(d->scale) && d->scale >= 0.f)) return H2O_EINVAL;
+  if (d->policy != H2O_POLICY_H2O) return H2O_EUNSUPPORTED;
+  if (d->D != 64 && d->D != 128) return H2O_EUNSUPPORTED;
+  // index arithmetic inside the kernels uses 32-bit row counts
+  const int64_t rows = static_cast<int64_t>(d->Hq / d->Hkv) * d->T;
+  const int64_t keys = static_cast<int64_t>(d->C) + d->T;
+  const int64_t groups = static_cast<int64_t>(d->B) * d->Hkv;
+  if (rows > (1 << 26) || keys > (1 << 26) || groups > (1 << 20)) return H2O_EUNSUPPORTED;
+  return H2O_OK;
+}
+
+// Workspace of the attention passes: two fp32 planes of (B,Hq,T) -- the
+// log2-domain row normaliser and, for INT4 caches, the per-row sum of q.
+size_t lse_bytes(const h2o_dims *d) {
+  return align_up(2 * sizeof(float) * static_cast<size_t>(d->B) * d->Hq * d->T);
+}
+
+size_t wsum_bytes(const h2o_dims *d, int n_occ) {
+  return align_up(sizeof(float) * static_cast<size_t>(d->B) * d->Hkv * (n_occ + d->T));
+}
+
+int check_cache_buffers(const h2o_dims *d, const h2o_cache *c) {
+  if (!c || !c->k || !c->v) return H2O_EINVAL;
+  if (!aligned16(c->k) || !aligned16(c->v)) return H2O_EINVAL;
+  if (d->cache_fmt != H2O_CACHE_NATIVE) {
+    if (!c->k_scale || !c->v_scale) return H2O_EINVAL;
+    if (d->cache_fmt == H2O_CACHE_INT4 && (!c->k_zero || !c->v_zero)) return H2O_EINVAL;
+  }
+  return H2O_OK;
+}
+
+float softmax_scale(const h2o_dims *d) {
+  return d->scale > 0.f ? d->scale : static_cast<float>(1.0 / std::sqrt(static_cast<double>(d->D)));
+}
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return H2O_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return H2O_EHIP;
+}
+
+int check_sdpa(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
+               const void *k_new, const void *v_new, const void *out, const float *wsum,
+               const float *lse, const void *ws, size_t ws_bytes) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
+  if (!q || !k_new || !v_new || !out || !wsum) return H2O_EINVAL;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
+      !aligned16(wsum) || (lse && !aligned16(lse)))
+    return H2O_EINVAL;
+  if (n_occ > 0) {
+    st = check_cache_buffers(d, cache);
+    if (st != H2O_OK) return st;
+  }
+  if (!ws || !aligned16(ws) || ws_bytes < lse_bytes(d)) return H2O_EWORKSPACE;
+  return H2O_OK;
+}
+
+int check_evict(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, int64_t pos,
+                const float *wsum, const int32_t *slot_log) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (!cache || !cache->scores || !wsum || !slot_log) return H2O_EINVAL;
+  if (n_occ < 0 || n_occ > d->C || pos < 0) return H2O_EINVAL;
+  if (cache->token_pos && pos + d->T > INT32_MAX) return H2O_EINVAL;
+  if (!(n_occ + static_cast<int64_t>(d->T) <= d->C || n_occ == d->C)) return H2O_EUNSUPPORTED;
+  if (n_occ == d->C && d->T > d->C) return H2O_EUNSUPPORTED;  // cannot evict more than C slots
+  if (d->C > 65536) return H2O_EUNSUPPORTED;
+  return H2O_OK;
+}
+
+int check_write(const h2o_dims *d, const h2o_cache *cache, const void *k_new, const void *v_new,
+                const int32_t *slot_log) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (!k_new || !v_new || !slot_log || !aligned16(k_new) || !aligned16(v_new)) return H2O_EINVAL;
+  return check_cache_buffers(d, cache);
+}
+
+h2o::AttnArgs attn_args(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
+                        const void *k_new, const void *v_new, void *out, float *wsum, float *lse,
+                        void *ws) {
+  h2o::AttnArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.kn = k_new;
+  a.vn = v_new;
+  if (cache) {
+    a.kc = cache->k;
+    a.vc = cache->v;
+    a.ks = cache->k_scale;
+    a.vs = cache->v_scale;
+    a.kz = cache->k_zero;
+    a.vz = cache->v_zero;
+  }
+  a.out = out;
+  a.wsum = wsum;
+  a.lse2 = static_cast<float *>(ws);
+  a.lse_nat = lse;
+  a.B = d->B;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.D = d->D;
+  a.C = d->C;
+  a.T = d->T;
+  a.qg = d->Hq / d->Hkv;
+  a.n_occ = n_occ;
+  a.dtype = d->dtype;
+  a.cache_fmt = d->cache_fmt;
+  a.sl2 = static_cast<float>(static_cast<double>(softmax_scale(d)) * 1.4426950408889634074);
+  return a;
+}
+
+int launch_sdpa(const h2o::AttnArgs &a, hipStream_t s) {
+  if (a.dtype == h2o::DT_BF16) return from_hip(h2o::launch_attn_mfma(a, s));
+  return from_hip(h2o::launch_attn_simple(a, s));
+}
+
+h2o::KvWriteArgs write_args(const h2o_dims *d, h2o_cache *cache, const void *k_new,
+                            const void *v_new, const int32_t *slot_log) {
+  h2o::KvWriteArgs w;
+  std::memset(&w, 0, sizeof(w));
+  w.kc = cache->k;
+  w.vc = cache->v;
+  w.ks = cache->k_scale;
+  w.vs = cache->v_scale;
+  w.kz = cache->k_zero;
+  w.vz = cache->v_zero;
+  w.kn = k_new;
+  w.vn = v_new;
+  w.slot_log = slot_log;
+  w.groups = d->B * d->Hkv;
+  w.C = d->C;
+  w.T = d->T;
+  w.D = d->D;
+  w.dtype = d->dtype;
+  w.cache_fmt = d->cache_fmt;
+  return w;
+}
+
+h2o::EvictArgs evict_args(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                          const float *wsum, int32_t *slot_log) {
+  h2o::EvictArgs e;
+  e.scores = cache->scores;
+  e.token_pos = cache->token_pos;
+  e.wsum = wsum;
+  e.slot_log = slot_log;
+  e.groups = d->B * d->Hkv;
+  e.C = d->C;
+  e.T = d->T;
+  e.n_occ = n_occ;
+  e.pos = pos;
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h2o_abi_version(void) { return H2O_ABI_VERSION; }
+
+const char *h2o_status_str(int status) {
+  switch (status) {
+    case H2O_OK: return "ok";
+    case H2O_EINVAL: return "invalid argument";
+    case H2O_EUNSUPPORTED: return "unsupported configuration";
+    case H2O_EWORKSPACE: return "workspace missing or too small";
+    case H2O_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int h2o_last_hip_error(void) { return g_last_hip_error; }
+
+size_t h2o_workspace_bytes(const h2o_dims *d) {
+  if (check_dims(d) != H2O_OK) return 0;
+  return lse_bytes(d) + wsum_bytes(d, d->C);
+}
+
+int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
+                      const void *k_new, const void *v_new, void *out, float *wsum, float *lse,
+                      void *ws, size_t ws_bytes, void *stream) {
+  const int st = check_sdpa(d, cache, n_occ, q, k_new, v_new, out, wsum, lse, ws, ws_bytes);
+  if (st != H2O_OK) return st;
+  const h2o::AttnArgs a = attn_args(d, cache, n_occ, q, k_new, v_new, out, wsum, lse, ws);
+  return launch_sdpa(a, static_cast<hipStream_t>(stream));
+}
+
+int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                   const float *wsum, int32_t *slot_log, void *ws, size_t ws_bytes,
+                   void *stream) {
+  (void)ws;
+  (void)ws_bytes;
+  const int st = check_evict(d, cache, n_occ, pos, wsum, slot_log);
+  if (st != H2O_OK) return st;
+  return from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, wsum, slot_log),
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int kv_scatter(const h2o_dims *d, h2o_cache *cache, const void *k_new, const void *v_new,
+               const int32_t *slot_log, void *stream) {
+  const int st = check_write(d, cache, k_new, v_new, slot_log);
+  if (st != H2O_OK) return st;
+  if (d->cache_fmt != H2O_CACHE_NATIVE) return H2O_EINVAL;
+  return from_hip(h2o::launch_kv_write(write_args(d, cache, k_new, v_new, slot_log),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int kv_quant_pack(const h2o_dims *d, h2o_cache *cache, const void *k_new, const void *v_new,
+                  const int32_t *slot_log, void *stream) {
+  const int st = check_write(d, cache, k_new, v_new, slot_log);
+  if (st != H2O_OK) return st;
+  if (d->cache_fmt == H2O_CACHE_NATIVE) return H2O_EINVAL;
+  return from_hip(h2o::launch_kv_write(write_args(d, cache, k_new, v_new, slot_log),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+int kv_dequant_unpack(const h2o_dims *d, const h2o_cache *cache, int32_t n_slots, float *k_out,
+                      float *v_out, void *stream) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (n_slots < 1 || n_slots > d->C || !k_out || !v_out) return H2O_EINVAL;
+  st = check_cache_buffers(d, cache);
+  if (st != H2O_OK) return st;
+  h2o::KvWriteArgs w = write_args(d, const_cast<h2o_cache *>(cache), nullptr, nullptr, nullptr);
+  return from_hip(h2o::launch_dequant(w, n_slots, k_out, v_out, static_cast<hipStream_t>(stream)));
+}
+
+int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,
+                   const void *k_new, const void *v_new, void *out, float *wsum,
+                   int32_t *slot_log, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
+  const size_t need = lse_bytes(d) + (wsum ? 0 : wsum_bytes(d, n_occ));
+  if (!ws || !aligned16(ws) || ws_bytes < need) return H2O_EWORKSPACE;
+  float *w = wsum ? wsum : reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d));
+  st = check_sdpa(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws, ws_bytes);
+  if (st != H2O_OK) return st;
+  st = check_evict(d, cache, n_occ, pos, w, slot_log);
+  if (st != H2O_OK) return st;
+  st = check_write(d, cache, k_new, v_new, slot_log);
+  if (st != H2O_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_sdpa(attn_args(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws), s);
+  if (st != H2O_OK) return st;
+  st = from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, w, slot_log), s));
+  if (st != H2O_OK) return st;
+  return from_hip(h2o::launch_kv_write(write_args(d, cache, k_new, v_new, slot_log), s));
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal launch interface of libh2o.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace h2o {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+enum : int { FMT_NATIVE = 0, FMT_INT8 = 1, FMT_INT4 = 2 };
+
+// Everything the attention passes read or write.  Shapes (row-major):
+//   q (B,Hq,T,D)  kn, vn (B,Hkv,T,D)  kc, vc cache (B,Hkv,C,D) or codes
+//   out (B,Hq,T,D)  wsum (B,Hkv,n_occ+T)  lse2 (B,Hq,T) log2-domain normaliser
+struct AttnArgs {
+  const void *q, *kn, *vn;
+  const void *kc, *vc;
+  const uint16_t *ks, *vs, *kz, *vz;  // fp16 scale / zero bit patterns (B,Hkv,C)
+  void *out;
+  float *wsum;
+  float *lse2;     // workspace: m + log2(l) with logits measured in units of log2
+  float *lse_nat;  // optional natural-log copy for the caller (may be null)
+  int B, Hq, Hkv, D, C, T, qg, n_occ;
+  int dtype, cache_fmt;
+  float sl2;  // softmax scale * log2(e)
+};
+
+struct EvictArgs {
+  float *scores;        // (B,Hkv,C)
+  int32_t *token_pos;   // (B,Hkv,C) or null
+  const float *wsum;    // (B,Hkv,n_occ+T)
+  int32_t *slot_log;    // (B,Hkv,T)
+  int groups, C, T, n_occ;
+  long long pos;
+};
+
+struct KvWriteArgs {
+  void *kc, *vc;
+  uint16_t *ks, *vs, *kz, *vz;
+  const void *kn, *vn;
+  const int32_t *slot_log;
+  int groups, C, T, D;
+  int dtype, cache_fmt;
+};
+
+hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
+hipError_t launch_evict(const EvictArgs &a, hipStream_t s);
+hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
+hipError_t launch_dequant(const KvWriteArgs &a, int n_slots, float *kout, float *vout, hipStream_t s);
+
+}  // namespace h2o

@@ -1,0 +1,181 @@
+/*
+ * h2o.h -- C ABI of libh2o.so: one chunk step of H2O sparse attention over a
+ * fixed-capacity KV cache, on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Learning how to Forget: Fine-tuning for Long-Context Sparse
+ * Attention", paper text page, §3.1, §3.1.1, §3.2, §A.1, §A.7; aimodeling.com
+ * article on the KeysAndValues release):
+ *
+ *   A chunk of T queries under grouped-query attention (H_q = H_kv * q_g; query
+ *   head h reads KV head floor(h / q_g)) attends to the n_occ occupied slots of
+ *   a cache of capacity C plus its own T keys, causally.  The step returns the
+ *   attention output and the attention weights summed over the chunk's queries
+ *   and over the q_g query heads of each KV group, for every occupied slot and
+ *   chunk position.  It then adds those sums to the running H2O scores, picks
+ *   the slots that receive the chunk (left-to-right fill while the cache has
+ *   room; otherwise the T lowest-scoring slots, ties to the lower slot index),
+ *   logs them (replay log), overwrites them with the chunk's keys and values
+ *   (quantising them for 8-bit / 4-bit caches) and seeds their scores with
+ *   their own summed weights.
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers to contiguous row-major memory,
+ *     16-byte aligned; the caller allocates and owns all of them and keeps them
+ *     alive until the work on `stream` has completed.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work
+ *     is enqueued asynchronously; no entry point synchronises, allocates or
+ *     frees device memory, or keeps a pointer after it returns.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is enqueued and a negative h2o_status is returned.
+ *   - Results are deterministic bit for bit (fixed-order reductions, no
+ *     floating-point atomics).
+ *   - Thread safety: entry points may be called from several host threads;
+ *     h2o_last_hip_error() is per host thread.
+ *   - Calls that overlap on the same cache buffers race; order them on one
+ *     stream.
+ */
+#ifndef H2O_H_
+#define H2O_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define H2O_ABI_VERSION 1
+
+/* Status codes. */
+enum h2o_status {
+  H2O_OK = 0,
+  H2O_EINVAL = -1,       /* null / misaligned pointer, bad sizes, n_occ out of range */
+  H2O_EUNSUPPORTED = -2, /* valid but not implemented: D not in {64,128}, chunk straddling capacity, ... */
+  H2O_EWORKSPACE = -3,   /* ws_bytes smaller than h2o_workspace_bytes() or ws NULL */
+  H2O_EHIP = -4          /* a HIP launch failed; see h2o_last_hip_error() */
+};
+
+/* Element type of q, k_new, v_new and out, and of a NATIVE cache. */
+enum h2o_dtype { H2O_F32 = 0, H2O_BF16 = 1 };
+
+/* Cache buffer format. */
+enum h2o_cache_fmt {
+  H2O_CACHE_NATIVE = 0, /* k, v: (B,Hkv,C,D) of `dtype` */
+  H2O_CACHE_INT8 = 1,   /* k, v: int8 codes (B,Hkv,C,D); k_scale, v_scale: fp16 (B,Hkv,C) */
+  H2O_CACHE_INT4 = 2    /* k, v: uint8 (B,Hkv,C,D/2), element 2i in the low nibble of byte i;
+                           k_scale, v_scale, k_zero, v_zero: fp16 (B,Hkv,C) */
+};
+
+/* Score used to choose the slots to overwrite once the cache is full. */
+enum h2o_policy {
+  H2O_POLICY_H2O = 0 /* cumulative summed attention weights per (b, KV head, slot) */
+};
+
+/* Problem sizes.  B batch, Hq query heads, Hkv KV heads (Hq % Hkv == 0),
+ * D head dimension (64 or 128), C cache capacity in slots, T chunk length.
+ * scale: softmax scale applied to q.k; 0 selects 1/sqrt(D). */
+typedef struct {
+  int32_t B, Hq, Hkv, D, C, T;
+  int32_t dtype;     /* enum h2o_dtype */
+  int32_t cache_fmt; /* enum h2o_cache_fmt */
+  int32_t policy;    /* enum h2o_policy */
+  float scale;
+} h2o_dims;
+
+/* One layer's cache state.  Caller-owned device buffers.
+ *   k, v        see enum h2o_cache_fmt
+ *   k_scale...  fp16 bit patterns (B,Hkv,C); NULL for NATIVE; zeros only for INT4
+ *   scores      fp32 (B,Hkv,C): running H2O scores of the occupied slots
+ *   token_pos   int32 (B,Hkv,C): absolute token position held by each slot, or NULL
+ *               when the caller does not track positions */
+typedef struct {
+  void *k, *v;
+  uint16_t *k_scale, *v_scale;
+  uint16_t *k_zero, *v_zero;
+  float *scores;
+  int32_t *token_pos;
+} h2o_cache;
+
+/* Library and error reporting. */
+int h2o_abi_version(void);
+const char *h2o_status_str(int status);
+/* hipError_t of the last failed launch on this host thread (0 if none). */
+int h2o_last_hip_error(void);
+
+/* Device workspace needed by h2o_sdpa_scoresum / h2o_evict_topk /
+ * h2o_chunk_step for these sizes, in bytes (covers every n_occ <= C).
+ * Returns 0 when `d` is invalid. */
+size_t h2o_workspace_bytes(const h2o_dims *d);
+
+/* Attention of one chunk with exact summed weights; changes no cache state.
+ * ("Learning how to Forget", §A.7: softmax(mask(scale Q K^T)) and the summed
+ * weights it names; §A.1: causal mask by token position -- with the chunk
+ * attending before it is written, every occupied slot is visible and the
+ * chunk's own keys are causal.)
+ *   n_occ   occupied slots, 0 <= n_occ <= C; slots 0..n_occ-1 are attended
+ *   q       (B,Hq,T,D) dtype          k_new, v_new (B,Hkv,T,D) dtype
+ *   out     (B,Hq,T,D) dtype: attention output
+ *   wsum    fp32 (B,Hkv,n_occ+T): column j < n_occ is slot j, column n_occ+t is
+ *           chunk token t; each is sum over the chunk's queries and the q_g
+ *           heads of the group of the softmax weight on that key
+ *   lse     fp32 (B,Hq,T) natural-log softmax normaliser, or NULL
+ *   ws      workspace of at least h2o_workspace_bytes(d) bytes */
+int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ,
+                      const void *q, const void *k_new, const void *v_new,
+                      void *out, float *wsum, float *lse,
+                      void *ws, size_t ws_bytes, void *stream);
+
+/* Score update, slot selection and replay log (aimodeling article: H2O score =
+ * cumulative attention-weight sums, lowest evicted; "Learning how to Forget",
+ * §3.1: left-to-right fill, B*Hkv*T slots per chunk; §3.2: replay log).
+ *   scores[j] += wsum[j] for j < n_occ.
+ *   If n_occ + T <= C: slot_log[b,g,t] = n_occ + t.
+ *   If n_occ == C:     slot_log[b,g,:] = the T slots with the smallest updated
+ *                      score under (score, slot index), in ascending slot order.
+ *   Then for each t: scores[slot_log[t]] = wsum[n_occ+t] and, if token_pos is
+ *   not NULL, token_pos[slot_log[t]] = pos + t.  K/V buffers are not touched.
+ *   n_occ < C < n_occ + T, or T > C when n_occ == C, returns H2O_EUNSUPPORTED.
+ *   C must be <= 65536.
+ *   slot_log: int32 (B,Hkv,T). */
+int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                   const float *wsum, int32_t *slot_log,
+                   void *ws, size_t ws_bytes, void *stream);
+
+/* Write the chunk's keys and values into the slots of slot_log, unchanged
+ * ("Learning how to Forget", §A.8: scatter along the slot axis with the head
+ * dimension contiguous).  NATIVE caches only (H2O_EINVAL otherwise).  Rows
+ * whose slot_log entry lies outside [0, C) are skipped. */
+int kv_scatter(const h2o_dims *d, h2o_cache *cache, const void *k_new, const void *v_new,
+               const int32_t *slot_log, void *stream);
+
+/* Quantise the chunk's keys and values per row and write codes, scales (and
+ * zero points) into the slots of slot_log.  INT8 or INT4 caches only
+ * (H2O_EINVAL for NATIVE).  The pages name 8-bit and 4-bit buffers without a
+ * scheme; this library uses, per slot and KV head, with IEEE fp32 operations:
+ *   INT8: a = max|x|; s = fp16(a/127); c = clamp(rne(x/s), -127, 127)
+ *   INT4: z = fp16(min x); s = fp16((max x - min x)/15);
+ *         c = clamp(rne((x - z)/s), 0, 15)
+ *   with all codes 0 when s == 0.  Dequantised value: c*s (+ z).  Rows whose
+ *   slot_log entry lies outside [0, C) are skipped. */
+int kv_quant_pack(const h2o_dims *d, h2o_cache *cache, const void *k_new, const void *v_new,
+                  const int32_t *slot_log, void *stream);
+
+/* Inspection helper: dequantise (or widen) the first n_slots slots of every
+ * (b, g) of the cache into fp32 k_out, v_out of shape (B,Hkv,n_slots,D). */
+int kv_dequant_unpack(const h2o_dims *d, const h2o_cache *cache, int32_t n_slots,
+                      float *k_out, float *v_out, void *stream);
+
+/* The whole chunk step: h2o_sdpa_scoresum, then h2o_evict_topk, then
+ * kv_scatter (NATIVE) or kv_quant_pack (INT8/INT4), enqueued on `stream`.
+ * wsum may be NULL (the sums then live in the workspace).  After the call the
+ * caller's occupancy is min(n_occ + T, C) and its position pos + T. */
+int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                   const void *q, const void *k_new, const void *v_new,
+                   void *out, float *wsum, int32_t *slot_log,
+                   void *ws, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* H2O_H_ */

@@ -1,0 +1,137 @@
+"""CPU-only checks of the C ABI: the library loads, exports every function
+include/h2o.h declares, and rejects bad arguments on the host before touching
+the GPU (no call here gets past validation, so no kernel is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from h2o_kv_cache_sdpa_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "h2o.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(api.LIB_PATH), reason="libh2o.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z][a-z0-9_]*)\s*\(", text)) - {"sizeof"})
+
+
+def test_exports_every_declared_function():
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    lib = api.lib()
+    missing = [f for f in declared if not hasattr(lib, f)]
+    assert not missing, missing
+    assert set(declared) == set(api.EXPORTS)
+
+
+def test_version_and_status_strings():
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define H2O_ABI_VERSION (\d+)", text).group(1))
+    assert api.lib().h2o_abi_version() == ver
+    for st in (0, -1, -2, -3, -4):
+        assert api.status_str(st) != "unknown status"
+    assert api.status_str(7) == "unknown status"
+    assert api.lib().h2o_last_hip_error() == 0
+
+
+def test_workspace_bytes():
+    d = api.make_dims(1, 32, 8, 128, 32768, 2048)
+    nb = api.workspace_bytes(d)
+    lse = 2 * 4 * 32 * 2048
+    wsum = 4 * 8 * (32768 + 2048)
+    assert nb >= lse + wsum and nb <= lse + wsum + 512
+    assert api.workspace_bytes(api.make_dims(1, 32, 8, 96, 1024, 64)) == 0  # D unsupported
+    assert api.workspace_bytes(api.make_dims(1, 30, 8, 128, 1024, 64)) == 0  # Hq % Hkv
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation
+
+
+def _cache(**kw):
+    c = api.H2OCacheBufs(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def _sdpa(d, cache=None, n_occ=0, ws_bytes=1 << 30, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, wsum=FAKE, lse=None, ws=FAKE)
+    p.update(ptrs)
+    cache = cache or _cache()
+    return api.lib().h2o_sdpa_scoresum(ctypes.byref(d), ctypes.byref(cache), n_occ, p["q"], p["k"],
+                                       p["v"], p["out"], p["wsum"], p["lse"], p["ws"], ws_bytes, None)
+
+
+def test_sdpa_validation():
+    d = api.make_dims(1, 8, 2, 128, 256, 64)
+    assert _sdpa(d, q=None) == api.H2O_EINVAL
+    assert _sdpa(d, out=FAKE + 4) == api.H2O_EINVAL  # misaligned
+    assert _sdpa(d, n_occ=257) == api.H2O_EINVAL
+    assert _sdpa(d, n_occ=-1) == api.H2O_EINVAL
+    assert _sdpa(d, n_occ=64, cache=_cache(k=None)) == api.H2O_EINVAL
+    assert _sdpa(d, ws_bytes=16) == api.H2O_EWORKSPACE
+    assert _sdpa(d, ws=None) == api.H2O_EWORKSPACE
+    assert _sdpa(api.make_dims(1, 8, 2, 80, 256, 64)) == api.H2O_EUNSUPPORTED
+    assert _sdpa(api.make_dims(1, 8, 3, 128, 256, 64)) == api.H2O_EINVAL
+    assert _sdpa(api.make_dims(0, 8, 2, 128, 256, 64)) == api.H2O_EINVAL
+    assert _sdpa(api.make_dims(1, 8, 2, 128, 256, 64, dtype=5)) == api.H2O_EINVAL
+    assert _sdpa(api.make_dims(1, 8, 2, 128, 256, 64, policy=9)) == api.H2O_EUNSUPPORTED
+    q8 = api.make_dims(1, 8, 2, 128, 256, 64, cache_fmt="int8")
+    assert _sdpa(q8, n_occ=64, cache=_cache(k_scale=None)) == api.H2O_EINVAL
+    q4 = api.make_dims(1, 8, 2, 128, 256, 64, cache_fmt="int4")
+    assert _sdpa(q4, n_occ=64, cache=_cache(v_zero=None)) == api.H2O_EINVAL
+
+
+def test_evict_validation():
+    L = api.lib()
+    d = api.make_dims(1, 8, 2, 128, 256, 64)
+
+    def ev(dims, n_occ, pos=0, cache=None, wsum=FAKE, slots=FAKE):
+        c = cache or _cache()
+        return L.h2o_evict_topk(ctypes.byref(dims), ctypes.byref(c), n_occ, pos, wsum, slots, None, 0,
+                                None)
+
+    assert ev(d, 224) == api.H2O_EUNSUPPORTED  # 224 < 256 < 224 + 64: straddles capacity
+    assert ev(d, 0, wsum=None) == api.H2O_EINVAL
+    assert ev(d, 0, slots=None) == api.H2O_EINVAL
+    assert ev(d, 0, cache=_cache(scores=None)) == api.H2O_EINVAL
+    assert ev(d, 0, pos=-1) == api.H2O_EINVAL
+    assert ev(d, 0, pos=2**31 - 10) == api.H2O_EINVAL  # token_pos would overflow int32
+    big = api.make_dims(1, 8, 2, 128, 70000, 64)
+    assert ev(big, 70000) == api.H2O_EUNSUPPORTED
+
+
+def test_write_validation():
+    L = api.lib()
+    nat = api.make_dims(1, 8, 2, 128, 256, 64)
+    q8 = api.make_dims(1, 8, 2, 128, 256, 64, cache_fmt="int8")
+    c = _cache()
+    assert L.kv_quant_pack(ctypes.byref(nat), ctypes.byref(c), FAKE, FAKE, FAKE, None) == api.H2O_EINVAL
+    assert L.kv_scatter(ctypes.byref(q8), ctypes.byref(c), FAKE, FAKE, FAKE, None) == api.H2O_EINVAL
+    assert L.kv_scatter(ctypes.byref(nat), ctypes.byref(c), FAKE, FAKE, None, None) == api.H2O_EINVAL
+    assert L.kv_dequant_unpack(ctypes.byref(nat), ctypes.byref(c), 0, FAKE, FAKE, None) == api.H2O_EINVAL
+    assert L.kv_dequant_unpack(ctypes.byref(nat), ctypes.byref(c), 257, FAKE, FAKE, None) == api.H2O_EINVAL
+
+
+def test_chunk_step_validation_enqueues_nothing():
+    L = api.lib()
+    d = api.make_dims(1, 8, 2, 128, 256, 64)
+    c = _cache()
+
+    def step(n_occ, ws_bytes=1 << 30, wsum=FAKE, slots=FAKE):
+        return L.h2o_chunk_step(ctypes.byref(d), ctypes.byref(c), n_occ, 0, FAKE, FAKE, FAKE, FAKE,
+                                wsum, slots, FAKE, ws_bytes, None)
+
+    assert step(224) == api.H2O_EUNSUPPORTED
+    assert step(0, slots=None) == api.H2O_EINVAL
+    # without a caller wsum buffer the sums need workspace room
+    need_lse = 2 * 4 * 8 * 64
+    assert step(0, ws_bytes=need_lse, wsum=None) == api.H2O_EWORKSPACE
+    assert L.h2o_last_hip_error() == 0

@@ -1,0 +1,188 @@
+"""Chunk-step streams through h2o_chunk_step against the fp64 oracle, step by
+step, for the five workloads: tiny fp32 stream and the single bf16 step at full
+size, the long bf16 / int8 / int4 streams with their structure (fill then
+evict, heavy hitters, B) at reduced cache and chunk sizes, and one evicting
+step of each big workload at full size checked on whole KV groups.
+
+When the GPU picks a different slot than the oracle inside the tie band, the
+GPU cache is reloaded from the oracle's state (inputs flow oracle -> GPU only)
+so both continue from the same state; such steps are counted and reported."""
+
+import numpy as np
+import pytest
+import torch
+
+from h2o_kv_cache_sdpa_amd import workloads as W
+from h2o_kv_cache_sdpa_amd.cache import H2OCache
+from oracle import h2o_oracle as O
+from tests.gpu_support import DEV, check_out, check_rel, check_selection, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _dev_bf16(x64):
+    return to_dev(W.to_storage(x64, "bf16"))
+
+
+def _load_gpu_from_oracle(gc: H2OCache, oc: O.OracleCache):
+    """Copy the oracle's state into the GPU cache buffers (oracle -> GPU)."""
+    if oc.fmt == "native":
+        gc.k.copy_(to_dev(W.to_storage(oc.k, gc.dtype)))
+        gc.v.copy_(to_dev(W.to_storage(oc.v, gc.dtype)))
+    else:
+        gc.k.copy_(torch.from_numpy(oc.k_codes).to(DEV))
+        gc.v.copy_(torch.from_numpy(oc.v_codes).to(DEV))
+        gc.k_scale.copy_(torch.from_numpy(oc.k_scale).to(DEV))
+        gc.v_scale.copy_(torch.from_numpy(oc.v_scale).to(DEV))
+        if oc.fmt == "int4":
+            gc.k_zero.copy_(torch.from_numpy(oc.k_zero).to(DEV))
+            gc.v_zero.copy_(torch.from_numpy(oc.v_zero).to(DEV))
+    gc.scores.copy_(torch.from_numpy(oc.phi.astype(np.float32)).to(DEV))
+    gc.token_pos.copy_(torch.from_numpy(oc.token_pos.astype(np.int32)).to(DEV))
+    gc.n_occ, gc.pos = oc.n_occ, oc.pos
+
+
+def _check_state(gc: H2OCache, oc: O.OracleCache, T, qg):
+    n = oc.n_occ
+    if oc.fmt == "native":
+        for name in ("k", "v"):
+            got = getattr(gc, name).float().cpu().numpy()[:, :, :n]
+            np.testing.assert_array_equal(got, getattr(oc, name)[:, :, :n], err_msg=name)
+    else:
+        for name in ("k", "v"):
+            np.testing.assert_array_equal(getattr(gc, name).cpu().numpy()[:, :, :n],
+                                          getattr(oc, name + "_codes")[:, :, :n])
+            np.testing.assert_array_equal(getattr(gc, name + "_scale").cpu().numpy()[:, :, :n].view(np.uint16),
+                                          getattr(oc, name + "_scale")[:, :, :n].view(np.uint16))
+            if oc.fmt == "int4":
+                np.testing.assert_array_equal(getattr(gc, name + "_zero").cpu().numpy()[:, :, :n].view(np.uint16),
+                                              getattr(oc, name + "_zero")[:, :, :n].view(np.uint16))
+    np.testing.assert_array_equal(gc.token_pos.cpu().numpy()[:, :, :n], oc.token_pos[:, :, :n])
+    check_rel(gc.scores.cpu().numpy()[:, :, :n], oc.phi[:, :, :n], T, qg, "scores")
+
+
+def _run_stream(w: W.Workload, steps=None):
+    gc = H2OCache(w.B, w.Hq, w.Hkv, w.D, w.C, w.T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=DEV)
+    oc = O.OracleCache(w.B, w.Hq, w.Hkv, w.D, w.C, fmt=w.cache_fmt)
+    if w.start_full:
+        k, v, scores, tp, n = W.prefilled_cache(w)
+        oc.k[:], oc.v[:] = k.f64, v.f64
+        oc.phi[:] = scores.astype(np.float64)
+        oc.token_pos[:] = tp
+        oc.n_occ = oc.pos = n
+        _load_gpu_from_oracle(gc, oc)
+    resync = 0
+    n_steps = w.steps if steps is None else steps
+    for step in range(n_steps):
+        ch = W.chunk(w, step)
+        n_occ = oc.n_occ
+        out, wsum, slots = gc.step(to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"]))
+        ref = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        torch.cuda.synchronize()
+        err = check_out(out, ref["out"], w.dtype, f"step {step} out")
+        werr = check_rel(wsum.cpu().numpy(), ref["w"], w.T, w.qg, f"step {step} wsum")
+        differ = check_selection(slots.cpu().numpy(), ref["slots"], ref["phi_updated"], n_occ, w.C, w.T)
+        print(f"{w.name} step {step} n_occ {n_occ}: out err {err:.2e} wsum rel {werr:.2e} "
+              f"in-band differ {differ}", flush=True)
+        if differ:
+            resync += 1
+            _load_gpu_from_oracle(gc, oc)
+        else:
+            _check_state(gc, oc, w.T, w.qg)
+    return resync
+
+
+def test_stream_cfg1_tiny_f32_full():
+    assert _run_stream(W.WORKLOADS[1]) == 0
+
+
+def test_stream_cfg2_single_step_full():
+    _run_stream(W.WORKLOADS[2])
+
+
+def test_stream_cfg3_bf16_reduced():
+    _run_stream(W.WORKLOADS[3].scaled(C=1024, T=64, n_fill=16, n_evict=12))
+
+
+def test_stream_cfg4_int8_reduced():
+    _run_stream(W.WORKLOADS[4].scaled(C=1024, T=64, n_fill=16, n_evict=12))
+
+
+def test_stream_cfg5_int4_reduced():
+    _run_stream(W.WORKLOADS[5].scaled(C=1024, T=32, n_fill=32, n_evict=10))
+
+
+# ---------------------------------------------------------------------------
+# one evicting step at full size, checked on whole KV groups
+# ---------------------------------------------------------------------------
+
+def _full_step(w: W.Workload, groups_checked):
+    """Prefilled full cache of the workload's size; one evicting step; the
+    oracle recomputes the listed (b, g) groups completely."""
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+    qg = w.qg
+    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=DEV)
+    seed = [w.cfg_id, 777]
+    if w.cache_fmt == "native":
+        k, v, scores, tp, _ = W.random_cache(seed, B, Hkv, C, D, C, w.dtype, hh_frac=0.02)
+        gc.k.copy_(to_dev(k))
+        gc.v.copy_(to_dev(v))
+        k64, v64 = k.f64, v.f64
+    else:
+        arr = W.random_quant_cache(seed, B, Hkv, C, D, C, w.cache_fmt)
+        scores, tp = arr["scores"], arr["token_pos"]
+        for name in ("k", "v"):
+            getattr(gc, name).copy_(torch.from_numpy(arr[name + "_codes"]).to(DEV))
+            getattr(gc, name + "_scale").copy_(torch.from_numpy(arr[name + "_scale"]).to(DEV))
+            if w.cache_fmt == "int4":
+                getattr(gc, name + "_zero").copy_(torch.from_numpy(arr[name + "_zero"]).to(DEV))
+        if w.cache_fmt == "int8":
+            k64 = O.dequantize_int8(arr["k_codes"], arr["k_scale"])
+            v64 = O.dequantize_int8(arr["v_codes"], arr["v_scale"])
+        else:
+            k64 = O.dequantize_int4(arr["k_codes"], arr["k_scale"], arr["k_zero"])
+            v64 = O.dequantize_int4(arr["v_codes"], arr["v_scale"], arr["v_zero"])
+    gc.scores.copy_(torch.from_numpy(scores).to(DEV))
+    gc.token_pos.copy_(torch.from_numpy(tp).to(DEV))
+    gc.n_occ, gc.pos = C, C
+    ch = W.chunk(w, w.n_fill)  # the first evicting chunk of the stream
+    out, wsum, slots = gc.step(to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"]))
+    torch.cuda.synchronize()
+    wsum_np = wsum.cpu().numpy()
+    # every query's weights sum to one: T*q_g per group, for all groups
+    np.testing.assert_allclose(wsum_np.astype(np.float64).sum(-1), T * qg, rtol=1e-4)
+    slots_np = slots.cpu().numpy()
+    for (b, g) in groups_checked:
+        print(f"{w.name}: oracle on group ({b},{g})", flush=True)
+        sl = slice(g * qg, (g + 1) * qg)
+        ref_o, ref_w, _ = O.attend_chunk(ch["q"].f64[b:b + 1, sl], k64[b:b + 1, g:g + 1],
+                                         v64[b:b + 1, g:g + 1], C, ch["k"].f64[b:b + 1, g:g + 1],
+                                         ch["v"].f64[b:b + 1, g:g + 1], float(np.float32(1 / np.sqrt(D))))
+        check_out(out[b:b + 1, sl], ref_o, w.dtype, f"group ({b},{g}) out")
+        check_rel(wsum_np[b:b + 1, g:g + 1], ref_w, T, qg, f"group ({b},{g}) wsum")
+        phi_upd = O.update_scores(scores[b:b + 1, g:g + 1].astype(np.float64), ref_w, C, C, T)
+        ref_slots = O.bottom_t(phi_upd, C, C, T)
+        differ = check_selection(slots_np[b:b + 1, g:g + 1], ref_slots, phi_upd, C, C, T)
+        print(f"group ({b},{g}) in-band differ {differ}", flush=True)
+
+
+def test_full_step_cfg2():
+    _full_step(W.WORKLOADS[2], [(0, 0), (0, 7)])
+
+
+def test_full_step_cfg3():
+    _full_step(W.WORKLOADS[3], [(0, 0), (0, 5)])
+
+
+def test_full_step_cfg4():
+    _full_step(W.WORKLOADS[4], [(0, 3)])
+
+
+def test_full_step_cfg5():
+    _full_step(W.WORKLOADS[5], [(0, 0), (3, 7)])
