@@ -1,0 +1,209 @@
+"""Throughput of the H2O chunk step on one MI355X.
+
+A step is one h2o_chunk_step call on a full cache (the evicting regime of the
+long bf16 stream: B=1, Hq=32, Hkv=8, D=128, C=32768 slots, chunks of T=2048):
+attention with exact summed weights, score update, bottom-T selection with
+replay log, and slot overwrite.  Inputs (cache state and a rotation of chunks)
+are synthetic, seeded, and resident in HBM before timing starts.
+
+Prints one JSON line.  `value` is chunk tokens per second; `roofline` covers
+the dominant kernel (attention pass A) from its average launch duration
+measured with HIP events on the launch stream over the timed region;
+`cpu_baseline` times the fp64 oracle on a bounded sample of the same step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+       [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector / matrix peak
+PEAK_HBM_GBS = 8000.0
+N_CHUNKS = 4                # distinct chunks rotated through the timed steps
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_a_traffic.json")
+
+
+def kernel_sources_digest():
+    """Digest of the sources the attention kernels are built from; a stored
+    HBM-traffic measurement is only reported while it still matches."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "h2o_kv_cache_sdpa_amd", "csrc")
+    for name in ("attn_mfma.hip", "device_util.hpp", "h2o_internal.hpp"):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def pairs_visible(B, Hq, T, n_occ):
+    """(query head, key) pairs the softmax sees in one step."""
+    return B * Hq * (T * n_occ + T * (T + 1) // 2)
+
+
+def cpu_baseline(w, groups=2):
+    """Time the fp64 oracle on `groups` KV groups of one evicting step and
+    scale to the whole step (the B*Hkv groups are independent)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    from oracle import h2o_oracle as O
+
+    k, v, scores, _, _ = W.random_cache([w.cfg_id, 777], 1, groups, w.C, w.D, w.C, w.dtype, hh_frac=0.02)
+    ch = W.random_chunk([w.cfg_id, 778], 1, groups * w.qg, groups, w.T, w.D, w.dtype, w.hh_new)
+    scale = float(np.float32(1.0 / np.sqrt(w.D)))
+    t0 = time.perf_counter()
+    out, wsum, _ = O.attend_chunk(ch["q"].f64, k.f64, v.f64, w.C, ch["k"].f64, ch["v"].f64, scale)
+    phi = O.update_scores(scores.astype(np.float64), wsum, w.C, w.C, w.T)
+    O.bottom_t(phi, w.C, w.C, w.T)
+    dt = time.perf_counter() - t0
+    step_s = dt * (w.B * w.Hkv) / groups
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {
+        "value": w.B * w.T / step_s,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{groups} of {w.B * w.Hkv} KV groups of one evicting step "
+                  f"({w.qg} heads x {w.T} queries x {w.C + w.T} keys each) in {dt:.1f} s, "
+                  f"scaled by {w.B * w.Hkv / groups:g} to the full step",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the chunk step shards "
+                          "over (batch, KV head) groups with no exchange, but no multi-GPU "
+                          "path is built", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from h2o_kv_cache_sdpa_amd import api
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    from h2o_kv_cache_sdpa_amd.cache import H2OCache
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = W.WORKLOADS[args.workload]
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+
+    # ---- resident inputs: a full cache and a rotation of chunks ----
+    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=dev)
+    seed = [w.cfg_id, 777]
+    if w.cache_fmt == "native":
+        k, v, scores, tp, _ = W.random_cache(seed, B, Hkv, C, D, C, w.dtype, hh_frac=0.02)
+        for name, st in (("k", k), ("v", v)):
+            getattr(gc, name).copy_(torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16))
+                                    .view(torch.bfloat16))
+    else:
+        arr = W.random_quant_cache(seed, B, Hkv, C, D, C, w.cache_fmt)
+        scores, tp = arr["scores"], arr["token_pos"]
+        for key, val in arr.items():
+            if key.endswith(("_codes", "_scale", "_zero")):
+                name = key.replace("_codes", "")
+                getattr(gc, name).copy_(torch.from_numpy(val))
+    gc.scores.copy_(torch.from_numpy(scores))
+    gc.token_pos.copy_(torch.from_numpy(tp))
+    gc.n_occ, gc.pos = C, C
+    chunks = []
+    for s in range(N_CHUNKS):
+        ch = W.chunk(w, w.n_fill + s)
+        to_dev = lambda st: torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+        chunks.append((to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"])))
+    out, wsum, slot_log = gc.new_outputs(C)
+    bufs = gc.bufs()
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q, kn, vn = chunks[i % N_CHUNKS]
+        api.h2o_chunk_step(gc.dims, bufs, C, gc.pos, q, kn, vn, out, wsum, slot_log, gc.ws, stream)
+        gc.pos += T
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    api.profile_reset()
+    api.profile_enable(True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    api.profile_enable(False)
+    prof = api.profile_read()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+
+    pairs = pairs_visible(B, Hq, T, C)
+    flops_a = 4 * D * pairs       # QK^T and PV of pass A
+    flops_b = 2 * D * pairs       # QK^T recomputed in pass B
+    a_ms = prof["attn_a"][0] / max(prof["attn_a"][1], 1)
+    b_ms = prof["attn_b"][0] / max(prof["attn_b"][1], 1)
+    achieved_a = flops_a / (a_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE))
+        if rec.get("sources") == kernel_sources_digest() and rec.get("workload") == w.name:
+            traffic = rec.get("bytes_per_launch")
+    line = {
+        "metric": "H2O chunk-step tokens/s (S=32K,T=2048,bf16); % of MFMA/HBM roofline",
+        "value": B * T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: evicting chunk step", "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "D": D, "cache_slots": C, "chunk": T, "cache_fmt": w.cache_fmt},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_a_mfma (output + row normalisers)",
+            "achieved": achieved_a,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_a / PEAK_BF16_TFLOPS,
+            "traffic": traffic,
+        },
+        "step_mfma_frac_6d": 6 * D * pairs / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "step_mfma_frac_4d": 4 * D * pairs / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()},
+        "attn_b_tflops": flops_b / (b_ms * 1e-3) / 1e12,
+        "wall_s_timed": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

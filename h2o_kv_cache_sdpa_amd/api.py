@@ -26,8 +26,10 @@ FORMATS = {"native": H2O_CACHE_NATIVE, "int8": H2O_CACHE_INT8, "int4": H2O_CACHE
 EXPORTS = (
     "h2o_abi_version", "h2o_status_str", "h2o_last_hip_error", "h2o_workspace_bytes",
     "h2o_sdpa_scoresum", "h2o_evict_topk", "kv_scatter", "kv_quant_pack",
-    "kv_dequant_unpack", "h2o_chunk_step",
+    "kv_dequant_unpack", "h2o_chunk_step", "h2o_profile_enable", "h2o_profile_read",
+    "h2o_profile_reset",
 )
+KERNEL_KINDS = ("attn_a", "attn_b", "evict", "kv_write")
 
 
 class H2ODims(ctypes.Structure):
@@ -91,6 +93,13 @@ def lib():
     L.kv_dequant_unpack.argtypes = [pd, pc, I32, P, P, P]
     L.h2o_chunk_step.restype = ctypes.c_int
     L.h2o_chunk_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, P, S, P]
+    L.h2o_profile_enable.restype = ctypes.c_int
+    L.h2o_profile_enable.argtypes = [ctypes.c_int]
+    L.h2o_profile_read.restype = ctypes.c_int
+    L.h2o_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
+                                   ctypes.c_int]
+    L.h2o_profile_reset.restype = ctypes.c_int
+    L.h2o_profile_reset.argtypes = []
     _lib = L
     return L
 
@@ -169,3 +178,20 @@ def h2o_chunk_step(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log
                               _ptr(slot_log), _ptr(ws), ws.numel() * ws.element_size(),
                               _stream(stream))
     _check("h2o_chunk_step", st)
+
+
+def profile_enable(on=True):
+    _check("h2o_profile_enable", lib().h2o_profile_enable(1 if on else 0))
+
+
+def profile_reset():
+    _check("h2o_profile_reset", lib().h2o_profile_reset())
+
+
+def profile_read():
+    """{kind: (total_ms, launches)} for the kernels timed since the last reset."""
+    n = len(KERNEL_KINDS)
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _check("h2o_profile_read", lib().h2o_profile_read(ms, cnt, n))
+    return {k: (ms[i], cnt[i]) for i, k in enumerate(KERNEL_KINDS)}

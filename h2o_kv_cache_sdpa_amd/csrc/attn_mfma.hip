@@ -644,11 +644,17 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   if (attr != hipSuccess) return attr;
   auto ka = attn_a_mfma<FMT, D>;
   auto kb = attn_b_mfma<FMT, D>;
-  hipLaunchKernelGGL(ka, dim3(nA), dim3(256), lds_a, s, a);
+  {
+    KernelTimer timer(H2O_K_ATTN_A, s);
+    hipLaunchKernelGGL(ka, dim3(nA), dim3(256), lds_a, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nB = groups * ((a.n_occ + a.T + B_KEYS - 1) / B_KEYS);
-  hipLaunchKernelGGL(kb, dim3(nB), dim3(256), lds_b, s, a);
+  {
+    KernelTimer timer(H2O_K_ATTN_B, s);
+    hipLaunchKernelGGL(kb, dim3(nB), dim3(256), lds_b, s, a);
+  }
   return hipGetLastError();
 }
 

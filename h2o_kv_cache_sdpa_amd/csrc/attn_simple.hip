@@ -195,12 +195,18 @@ hipError_t launch_simple_t(const AttnArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
   const int rows = a.qg * a.T;
   dim3 ga((rows + ROWS_A - 1) / ROWS_A, groups);
-  hipLaunchKernelGGL((attn_a_simple<DT, FMT, D>), ga, dim3(ROWS_A), 0, s, a);
+  {
+    KernelTimer timer(H2O_K_ATTN_A, s);
+    hipLaunchKernelGGL((attn_a_simple<DT, FMT, D>), ga, dim3(ROWS_A), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int n_keys = a.n_occ + a.T;
   dim3 gb((n_keys + KEYS_B - 1) / KEYS_B, groups);
-  hipLaunchKernelGGL((attn_b_simple<DT, FMT, D>), gb, dim3(KEYS_B), 0, s, a);
+  {
+    KernelTimer timer(H2O_K_ATTN_B, s);
+    hipLaunchKernelGGL((attn_b_simple<DT, FMT, D>), gb, dim3(KEYS_B), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -188,6 +188,7 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
 
 template <int ITEMS>
 hipError_t launch_items(const EvictArgs &a, hipStream_t s) {
+  KernelTimer timer(H2O_K_EVICT, s);
   hipLaunchKernelGGL(evict_kernel<ITEMS>, dim3(a.groups), dim3(NT), 0, s, a);
   return hipGetLastError();
 }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/h2o.h"
+
 namespace h2o {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1 };
@@ -41,6 +43,21 @@ struct KvWriteArgs {
   const int32_t *slot_log;
   int groups, C, T, D;
   int dtype, cache_fmt;
+};
+
+// Brackets one kernel launch with hipEvents on `s` while timing is enabled
+// (h2o_profile_enable); kind is an enum h2o_kernel_kind value.
+class KernelTimer {
+ public:
+  KernelTimer(int kind, hipStream_t s);
+  ~KernelTimer();
+  KernelTimer(const KernelTimer &) = delete;
+  KernelTimer &operator=(const KernelTimer &) = delete;
+
+ private:
+  int kind_;
+  hipStream_t stream_;
+  hipEvent_t start_ = nullptr;
 };
 
 hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);

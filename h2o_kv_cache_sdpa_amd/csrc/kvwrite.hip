@@ -153,6 +153,7 @@ hipError_t launch_dequant_dt(const KvWriteArgs &a, int n_slots, float *kout, flo
 }  // namespace
 
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s) {
+  KernelTimer timer(H2O_K_KV_WRITE, s);
   if (a.cache_fmt == FMT_NATIVE) {
     const int row_bytes = a.D * (a.dtype == DT_F32 ? 4 : 2);
     const size_t chunks = static_cast<size_t>(a.groups) * a.T * (row_bytes / 16);

@@ -174,6 +174,23 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
                    void *out, float *wsum, int32_t *slot_log,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* Kernel timing, for measurement.  While enabled, every kernel the library
+ * launches is bracketed by two hipEvents recorded on the caller's stream (the
+ * events come from a pool the library owns; no device memory is allocated).
+ * h2o_profile_read waits for the recorded events, adds their elapsed times to
+ * per-kind totals and copies the totals (milliseconds) and launch counts into
+ * arrays of at least H2O_K_COUNT entries (H2O_EINVAL otherwise). */
+enum h2o_kernel_kind {
+  H2O_K_ATTN_A = 0,   /* attention output and row normalisers */
+  H2O_K_ATTN_B = 1,   /* summed weights */
+  H2O_K_EVICT = 2,    /* score update, selection, replay log */
+  H2O_K_KV_WRITE = 3, /* slot overwrite / quantise */
+  H2O_K_COUNT = 4
+};
+int h2o_profile_enable(int on);
+int h2o_profile_read(double *total_ms, int64_t *launches, int n);
+int h2o_profile_reset(void);
+
 #ifdef __cplusplus
 }
 #endif
