@@ -667,6 +667,7 @@ hipError_t launch_f(const AttnArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s) {
+  if (a.cache_fmt == FMT_NATIVE && a.D == 128) return launch_attn_native_d128(a, s);
   switch (a.cache_fmt) {
     case FMT_INT8: return launch_f<FMT_INT8>(a, s);
     case FMT_INT4: return launch_f<FMT_INT4>(a, s);

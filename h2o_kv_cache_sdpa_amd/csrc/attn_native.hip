@@ -1,0 +1,514 @@
+// bf16 attention passes for a native bf16 cache with head dimension 128 --
+// the shape of the 16K/32K-slot workloads -- software-pipelined for gfx950.
+//
+// Same mathematics as attn_mfma.hip ("Learning how to Forget", §A.7: softmax
+// of mask(d_h^{-1/2} Q K^T), output Y = m V, summed weights sum_i m_ij; §A.1
+// mask with the chunk attending before it is written: cache slots visible,
+// chunk keys causal), organised for throughput:
+//
+//  * K, V and Q tiles move HBM -> LDS with global_load_lds_dwordx4 (no
+//    staging registers, no VALU).  Each lane's 16 bytes land at
+//    segment_base + 16*lane, so a tile's XOR swizzle is produced by choosing
+//    which global chunk each lane fetches.
+//  * V stays row-major [key][d] in LDS; the A operand of O^T = V^T P^T (keys
+//    contiguous per lane) comes from ds_read_b64_tr_b16: within a 16-lane
+//    group, lane k supplies V[kb + k/4][c0 + 4(k%4) .. +3] and lane i receives
+//    V[kb + e][c0 + i], e = 0..3.
+//  * Pass A keeps S for two tiles in flight: while the MFMAs of S(t+1) =
+//    K(t+1) Q^T run, the VALU works on the softmax of S(t); then O^T +=
+//    V(t)^T P(t)^T.  K tiles run one step ahead of V tiles in two LDS buffers
+//    each; one barrier per tile.
+//  * Pass B gives each wavefront 64 keys (two B-operand sets), so every Q
+//    A-operand read from LDS feeds two MFMAs, and processes the exponentials
+//    of one 32-row block while the next block's MFMAs run.
+//
+// LDS buffers are separate static arrays and every access names its buffer at
+// compile time (loops are unrolled by the buffer parity), so the compiler can
+// tell an in-flight DMA target from the buffer being read.
+
+#include <type_traits>
+
+#include "device_util.hpp"
+#include "h2o_internal.hpp"
+
+namespace h2o {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(1))) void gbl_void;
+
+constexpr int D = 128;
+constexpr int ROW_BYTES = D * 2;    // 256
+constexpr int TILE_BYTES = 64 * ROW_BYTES;  // 64 rows x 128 bf16 = 16 KB
+constexpr float RESCALE_SLACK = 8.f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ void dma16(const void *src, char *lds_segment) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)(src), (lds_void *)(lds_segment), 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(const void *src, char *lds_segment) {
+  __builtin_amdgcn_global_load_lds((gbl_void *)(src), (lds_void *)(lds_segment), 4, 0, 0);
+}
+
+__device__ __forceinline__ void wait_dma_and_sync() {
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's loads (incl. LDS DMA) are done
+  __syncthreads();                // ... and everybody else's
+}
+
+// K / Q tile: chunk c of row r at r*256 + 16*(c ^ (r & 15)) -- 16 consecutive
+// rows read at one chunk index touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kq_off(int row, int chunk) {
+  return row * ROW_BYTES + ((chunk ^ (row & 15)) << 4);
+}
+__device__ __forceinline__ int kq_chunk_at(int row, int pos) { return pos ^ (row & 15); }
+
+// V tile: chunk c of row r at r*256 + 16*(c ^ 4*(r & 3)) -- the 4 rows x 4
+// chunks a transpose read touches per half-wave land on 16 distinct groups.
+__device__ __forceinline__ int v_off(int row, int chunk) {
+  return row * ROW_BYTES + ((chunk ^ ((row & 3) << 2)) << 4);
+}
+__device__ __forceinline__ int v_chunk_at(int row, int pos) { return pos ^ ((row & 3) << 2); }
+
+__device__ __forceinline__ bf16x8 lds16(const char *p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
+}
+
+__device__ __forceinline__ i16x4 lds_tr(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
+}
+
+__device__ __forceinline__ int perm_key(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// Address of key row j of one KV group: cache slot j < n_occ, else chunk key
+// j - n_occ (clamped to row 0 of the chunk beyond T; such keys are masked).
+__device__ __forceinline__ const char *key_row(const void *cache, const void *chunk, size_t cache_row0,
+                                               size_t new_row0, int n_occ, int T, int j) {
+  if (j < n_occ) return static_cast<const char *>(cache) + (cache_row0 + j) * ROW_BYTES;
+  const int t = j - n_occ;
+  return static_cast<const char *>(chunk) + (new_row0 + (t < T ? t : 0)) * ROW_BYTES;
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
+// ---------------------------------------------------------------------------
+// Pass A: 128 packed query rows per block, 4 wavefronts x 32 rows
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hl = lane >> 5;
+  const int R = a.qg * a.T;
+  const int tiles_per_grp = (R + 127) / 128;
+  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
+  const int g = grp % a.Hkv, b = grp / a.Hkv;
+  const int row0 = rt * 128;
+  const int wrow0 = row0 + wave * 32;
+  const int my_row = wrow0 + n;
+  const bool row_ok = my_row < R;
+  const int i_q = row_ok ? my_row / a.qg : 0;
+  const int h_q = g * a.qg + (row_ok ? my_row % a.qg : 0);
+  const int n_occ = a.n_occ;
+  const float sl2 = a.sl2;
+  // wave-uniform: smallest chunk position of the wave's rows, and ragged rows
+  const int wave_i_min = wrow0 / a.qg;
+  const bool wave_ragged = wrow0 + 31 >= R;
+
+  bf16x8 qf[8];
+  {
+    const uint16_t *qrow =
+        static_cast<const uint16_t *>(a.q) + ((static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q) * D;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_ok) v = *reinterpret_cast<const uint4 *>(qrow + 16 * st + 8 * hl);
+      qf[st] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  const int last_row = min(R, row0 + 128) - 1;
+  const int key_end = n_occ + last_row / a.qg + 1;
+  const int ntiles = (key_end + 63) / 64;
+  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
+  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
+
+  // DMA of one 64-row tile: 16 segments of 1 KB (4 rows), 4 per wavefront.
+  auto issue_k = [&](int tile, char *dst) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int seg = wave * 4 + q;
+      const int row = seg * 4 + (lane >> 4);
+      const int c = kq_chunk_at(row, lane & 15);
+      dma16(key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, tile * 64 + row) + 16 * c,
+            dst + seg * 1024);
+    }
+  };
+  auto issue_v = [&](int tile, char *dst) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int seg = wave * 4 + q;
+      const int row = seg * 4 + (lane >> 4);
+      const int c = v_chunk_at(row, lane & 15);
+      dma16(key_row(a.vc, a.vn, cache_row0, new_row0, n_occ, a.T, tile * 64 + row) + 16 * c,
+            dst + seg * 1024);
+    }
+  };
+
+  const int prow = perm_key(n);
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  f32x16 o[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) o[k] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // S(0) alone (nothing to overlap with yet)
+  auto s_only = [&](const char *kb, f32x16 &s0, f32x16 &s1) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 k0 = lds16(kb + kq_off(prow, 2 * st + hl));
+      const bf16x8 k1 = lds16(kb + kq_off(32 + prow, 2 * st + hl));
+      s0 = mfma32(k0, qf[st], s0);
+      s1 = mfma32(k1, qf[st], s1);
+    }
+  };
+
+  // Tile t: mask (diagonal tiles only), running max, lazy rescale; then, in
+  // one straight-line block, the MFMAs of S(t+1) = K(t+1) Q^T from kb_next
+  // interleaved with the exponentials of tile t, and O^T += V(t)^T P(t)^T.
+  auto tile_step = [&](int t, f32x16 c0, f32x16 c1, const char *kb_next, f32x16 &n0, f32x16 &n1,
+                       const char *vb) {
+    const int j0 = t * 64;
+    if (wave_ragged || j0 + 63 - n_occ > wave_i_min) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ja = j0 + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index, < 0 for cache
+        c0[r] = (row_ok && ja <= i_q) ? c0[r] : -INFINITY;
+        c1[r] = (row_ok && ja + 32 <= i_q) ? c1[r] : -INFINITY;
+      }
+    }
+    float mx = __builtin_fmaxf(__builtin_fmaxf(c0[0], c0[1]), c0[2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, c0[r]), c0[r + 1]);
+    mx = __builtin_fmaxf(mx, c0[15]);
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, c1[r]), c1[r + 1]);
+    mx *= sl2;
+    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    if (__ballot(mx > m_run + RESCALE_SLACK)) {
+      const float m_new = __builtin_fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[k] *= alpha;
+      m_run = m_new;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+
+    bf16x8 pb[4];
+    float ls0 = 0.f, ls1 = 0.f;
+    n0 = f32x16{};
+    n1 = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      {
+        const bf16x8 k0 = lds16(kb_next + kq_off(prow, 2 * st + hl));
+        const bf16x8 k1 = lds16(kb_next + kq_off(32 + prow, 2 * st + hl));
+        n0 = mfma32(k0, qf[st], n0);
+        n1 = mfma32(k1, qf[st], n1);
+      }
+      const float p00 = __builtin_amdgcn_exp2f(fmaf(c0[st], sl2, neg_m));
+      const float p01 = __builtin_amdgcn_exp2f(fmaf(c0[8 + st], sl2, neg_m));
+      const float p10 = __builtin_amdgcn_exp2f(fmaf(c1[st], sl2, neg_m));
+      const float p11 = __builtin_amdgcn_exp2f(fmaf(c1[8 + st], sl2, neg_m));
+      ls0 += p00 + p01;
+      ls1 += p10 + p11;
+      pb[0][st] = static_cast<__bf16>(p00);
+      pb[1][st] = static_cast<__bf16>(p01);
+      pb[2][st] = static_cast<__bf16>(p10);
+      pb[3][st] = static_cast<__bf16>(p11);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 14, 0);
+    }
+    l_run += ls0 + ls1;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        // keys 16ks + 8h + 0..3 and + 4..7 at d = 32 blk + (lane % 32)
+        const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
+        const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
+        const char *p0 = vb + v_off(row, col >> 3) + 2 * (col & 7);
+        const char *p1 = vb + v_off(row + 4, col >> 3) + 2 * (col & 7);
+        const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(p0));
+        const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(p1));
+        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[blk] = mfma32(va, pb[ks], o[blk]);
+        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+      }
+    }
+  };
+
+  // ---- pipeline: K tiles one step ahead of V tiles, two LDS buffers each ----
+  issue_k(0, kb0);
+  issue_v(0, vb0);
+  if (ntiles > 1) issue_k(1, kb1);
+  wait_dma_and_sync();
+  f32x16 sa0, sa1, sb0, sb1;  // S of the even / odd tile
+  s_only(kb0, sa0, sa1);
+
+  for (int t = 0; t < ntiles; t += 2) {
+    // even tile t: K(t+1) in kb1, V(t) in vb0 (for the last tile, kb1 is stale
+    // and the S it yields is discarded: one copy of the body per parity)
+    wait_dma_and_sync();
+    if (t + 2 < ntiles) issue_k(t + 2, kb0);
+    if (t + 1 < ntiles) issue_v(t + 1, vb1);
+    tile_step(t, sa0, sa1, kb1, sb0, sb1, vb0);
+    if (t + 1 >= ntiles) break;
+    // odd tile t+1: K(t+2) in kb0, V(t+1) in vb1
+    wait_dma_and_sync();
+    if (t + 3 < ntiles) issue_k(t + 3, kb1);
+    if (t + 2 < ntiles) issue_v(t + 2, vb0);
+    tile_step(t + 1, sb0, sb1, kb0, sa0, sa1, vb1);
+  }
+
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = 1.f / l_tot;
+  uint16_t *orow =
+      static_cast<uint16_t *>(a.out) + ((static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q) * D;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = 32 * blk + 8 * a4 + 4 * hl;
+      *reinterpret_cast<uint2 *>(orow + d) =
+          make_uint2(pack_bf16_rne(o[blk][4 * a4] * inv, o[blk][4 * a4 + 1] * inv),
+                     pack_bf16_rne(o[blk][4 * a4 + 2] * inv, o[blk][4 * a4 + 3] * inv));
+    }
+  }
+  if (hl == 0) {
+    const float L = m_run + log2f(l_tot);
+    const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
+    a.lse2[li] = L;
+    if (a.lse_nat) a.lse_nat[li] = L * 0.69314718055994530942f;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass B: 256 keys per block, 4 wavefronts x 64 keys; 128-row Q blocks
+// ---------------------------------------------------------------------------
+
+constexpr int PB_KEYS = 256;
+constexpr int PB_ROWS = 128;
+constexpr int QBLK_BYTES = PB_ROWS * ROW_BYTES;  // 32 KB
+
+__global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
+  __shared__ __attribute__((aligned(1024))) char qb0[QBLK_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qb1[QBLK_BYTES];
+  __shared__ __attribute__((aligned(512))) float lb0[PB_ROWS];
+  __shared__ __attribute__((aligned(512))) float lb1[PB_ROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hl = lane >> 5;
+  const int n_occ = a.n_occ;
+  const int n_keys = n_occ + a.T;
+  const int R = a.qg * a.T;
+  const int kblocks = (n_keys + PB_KEYS - 1) / PB_KEYS;
+  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = wi / kblocks, kbk = wi % kblocks;
+  const int g = grp % a.Hkv, b = grp / a.Hkv;
+  const int j_base = kbk * PB_KEYS;
+  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
+  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
+  const float sl2 = a.sl2;
+
+  // K^T operands of the wave's two 32-key sub-blocks
+  int key0 = j_base + wave * 64 + n, key1 = key0 + 32;
+  const int tnew0 = key0 - n_occ, tnew1 = key1 - n_occ;
+  bf16x8 kf0[8], kf1[8];
+  {
+    const char *src0 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key0 < n_keys ? key0 : 0);
+    const char *src1 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key1 < n_keys ? key1 : 0);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      kf0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src0 + 32 * st + 16 * hl));
+      kf1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src1 + 32 * st + 16 * hl));
+    }
+  }
+
+  const int row_first = (j_base >= n_occ) ? (j_base - n_occ) * a.qg : 0;
+  const int rb_begin = row_first / PB_ROWS * PB_ROWS;
+  const int nrb = (R - rb_begin + PB_ROWS - 1) / PB_ROWS;
+  const int t_last = j_base + PB_KEYS - 1 - n_occ;
+  const size_t lse_base = static_cast<size_t>(b) * a.Hq * a.T;
+
+  // DMA of a 128-row Q block (32 KB: 32 segments, 8 per wavefront) and its normalisers
+  auto issue_rows = [&](int rb, char *qdst, float *ldst) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int seg = wave * 8 + q;
+      const int rr = seg * 4 + (lane >> 4);
+      int row = rb + rr;
+      row = row < R ? row : R - 1;  // rows past the end are masked
+      const int ii = row / a.qg, hh = g * a.qg + row % a.qg;
+      const char *src = static_cast<const char *>(a.q) +
+                        ((static_cast<size_t>(b) * a.Hq + hh) * a.T + ii) * ROW_BYTES;
+      dma16(src + 16 * kq_chunk_at(rr, lane & 15), qdst + seg * 1024);
+    }
+    if (wave < 2) {
+      int row = rb + wave * 64 + lane;
+      row = row < R ? row : R - 1;
+      const int ii = row / a.qg, hh = g * a.qg + row % a.qg;
+      dma4(a.lse2 + lse_base + static_cast<size_t>(hh) * a.T + ii,
+           reinterpret_cast<char *>(ldst + wave * 64));
+    }
+  };
+
+  float acc0 = 0.f, comp0 = 0.f, acc1 = 0.f, comp1 = 0.f;
+  auto add_comp = [](float &acc, float &comp, float part) {
+    const float y = part - comp;
+    const float tt = acc + y;
+    comp = (tt - acc) - y;
+    acc = tt;
+  };
+  auto load_l = [&](const float *lb, int sub, float (&Lv)[16]) {
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const float4 L = *reinterpret_cast<const float4 *>(lb + 32 * sub + 8 * a4 + 4 * hl);
+      Lv[4 * a4] = L.x;
+      Lv[4 * a4 + 1] = L.y;
+      Lv[4 * a4 + 2] = L.z;
+      Lv[4 * a4 + 3] = L.w;
+    }
+  };
+
+  // One 128-row block: the MFMAs of sub-block k+1 run while the VALU sums
+  // the exponentials of sub-block k.  FULL: every row sees every key.
+  auto do_block = [&](auto full_tag, const char *qb, const float *lb, int rb) {
+    constexpr bool FULL = decltype(full_tag)::value;
+    f32x16 c0 = f32x16{}, c1 = f32x16{};
+    float Lc[16];
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 qa = lds16(qb + kq_off(n, 2 * st + hl));
+      c0 = mfma32(qa, kf0[st], c0);
+      c1 = mfma32(qa, kf1[st], c1);
+    }
+    load_l(lb, 0, Lc);
+#pragma unroll
+    for (int sub = 1; sub <= 4; ++sub) {
+      f32x16 n0 = f32x16{}, n1 = f32x16{};
+      float p0 = 0.f, p1 = 0.f;
+      const int rsub = rb + 32 * (sub - 1);  // rows of the block being summed
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        if (sub < 4) {
+          const bf16x8 qa = lds16(qb + kq_off(32 * sub + n, 2 * st + hl));
+          n0 = mfma32(qa, kf0[st], n0);
+          n1 = mfma32(qa, kf1[st], n1);
+        }
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const int r = 2 * st + h2;
+          float x0 = fmaf(c0[r], sl2, -Lc[r]);
+          float x1 = fmaf(c1[r], sl2, -Lc[r]);
+          if constexpr (!FULL) {
+            const int row = rsub + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const int i = row / a.qg;
+            x0 = (row < R && tnew0 <= i) ? x0 : -INFINITY;
+            x1 = (row < R && tnew1 <= i) ? x1 : -INFINITY;
+          }
+          p0 += __builtin_amdgcn_exp2f(x0);
+          p1 += __builtin_amdgcn_exp2f(x1);
+        }
+        if (FULL && sub < 4) {
+          __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 12, 0);
+        }
+      }
+      add_comp(acc0, comp0, p0);
+      add_comp(acc1, comp1, p1);
+      if (sub < 4) {
+        c0 = n0;
+        c1 = n1;
+        load_l(lb, sub, Lc);
+      }
+    }
+  };
+  auto block = [&](const char *qb, const float *lb, int rb) {
+    const bool full = (rb + PB_ROWS <= R) && (j_base + PB_KEYS <= n_occ || rb / a.qg >= t_last);
+    if (full) {
+      do_block(std::true_type{}, qb, lb, rb);
+    } else {
+      do_block(std::false_type{}, qb, lb, rb);
+    }
+  };
+
+  issue_rows(rb_begin, qb0, lb0);
+  for (int it = 0; it < nrb; it += 2) {
+    const int rb = rb_begin + it * PB_ROWS;
+    wait_dma_and_sync();  // block it in qb0; everybody done with qb1
+    if (it + 1 < nrb) issue_rows(rb + PB_ROWS, qb1, lb1);
+    block(qb0, lb0, rb);
+    if (it + 1 >= nrb) break;
+    wait_dma_and_sync();  // block it+1 in qb1; everybody done with qb0
+    if (it + 2 < nrb) issue_rows(rb + 2 * PB_ROWS, qb0, lb0);
+    block(qb1, lb1, rb + PB_ROWS);
+  }
+
+  const float mine0 = acc0 - comp0, mine1 = acc1 - comp1;
+  const float other0 = __shfl_xor(mine0, 32), other1 = __shfl_xor(mine1, 32);
+  if (hl == 0) {
+    float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
+    if (key0 < n_keys) w[key0] = mine0 + other0;
+    if (key1 < n_keys) w[key1] = mine1 + other1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
+  const int groups = a.B * a.Hkv;
+  const int R = a.qg * a.T;
+  const int nA = groups * ((R + 127) / 128);
+  {
+    KernelTimer timer(H2O_K_ATTN_A, s);
+    hipLaunchKernelGGL(attn_a_native, dim3(nA), dim3(256), 0, s, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
+  {
+    KernelTimer timer(H2O_K_ATTN_B, s);
+    hipLaunchKernelGGL(attn_b_native, dim3(nB), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h2o

@@ -12,8 +12,8 @@
 // an index-ordered compaction: a slot is taken if its key is below the
 // threshold key, or equal to it and among the first k such slots.  The replay
 // log row comes out in ascending slot order; chunk token t goes to the t-th
-// entry.  Each thread owns ITEMS consecutive slots held in registers, so no
-// thread reads a slot another thread writes.
+// entry.  Each thread owns ITEMS consecutive slots held in registers (loaded
+// through LDS so that global accesses stay coalesced).
 
 #include "device_util.hpp"
 #include "h2o_internal.hpp"
@@ -57,8 +57,12 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t &ea
   eb = pb + ib - b;
 }
 
-template <int ITEMS>
+template <int ITEMS, bool STAGE>
 __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
+  // Updated scores pass through LDS so that global traffic is coalesced while
+  // each thread still owns a contiguous index range (row stride ITEMS + 1
+  // keeps the per-thread reads conflict-free).
+  extern __shared__ float stage[];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t sh_sel, sh_k;
   __shared__ uint32_t sh_a[NWAVES], sh_b[NWAVES];
@@ -84,17 +88,29 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
     return;
   }
 
-  // evicting: n_occ == C
+  // evicting: n_occ == C.  phi += w
   const int base = tid * ITEMS;
   uint32_t key[ITEMS];
-#pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    const int j = base + k;
-    key[k] = 0xffffffffu;
-    if (j < C) {
+  if constexpr (STAGE) {  // coalesced, staged in LDS
+    for (int j = tid; j < C; j += NT) {
       const float f = phi[j] + w[j];
       phi[j] = f;
-      key[k] = ordered_key(f);
+      stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      key[k] = (base + k < C) ? ordered_key(stage[tid * (ITEMS + 1) + k]) : 0xffffffffu;
+  } else {  // caches too large to stage: each thread reads its own range
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int j = base + k;
+      key[k] = 0xffffffffu;
+      if (j < C) {
+        const float f = phi[j] + w[j];
+        phi[j] = f;
+        key[k] = ordered_key(f);
+      }
     }
   }
 
@@ -107,11 +123,12 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
     for (int k = 0; k < ITEMS; ++k) {
       const bool act = (base + k < C) && ((key[k] & pmask) == prefix);
       const uint32_t digit = (key[k] >> shift) & 255u;
+      // one LDS increment per distinct digit present in the wavefront
       uint64_t pending = __ballot(act);
       while (pending) {
         const int leader = __builtin_ctzll(pending);
-        const uint32_t ld = __shfl(digit, leader);
-        const uint64_t same = __ballot(act && digit == ld) & pending;
+        const uint32_t ld = __builtin_amdgcn_readlane(digit, leader);
+        const uint64_t same = __ballot(act && digit == ld);
         if (lane == leader) atomicAdd(&hist[ld], static_cast<uint32_t>(__popcll(same)));
         pending &= ~same;
       }
@@ -188,8 +205,15 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
 
 template <int ITEMS>
 hipError_t launch_items(const EvictArgs &a, hipStream_t s) {
+  constexpr bool STAGE = ITEMS <= 32;  // 1024 x 33 floats = 132 KB of LDS at most
+  constexpr int stage_bytes = STAGE ? static_cast<int>(sizeof(float)) * NT * (ITEMS + 1) : 0;
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void *>(&evict_kernel<ITEMS, STAGE>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, stage_bytes);
+  if (attr != hipSuccess) return attr;
+  const size_t lds = (a.n_occ == a.C) ? stage_bytes : 0;
   KernelTimer timer(H2O_K_EVICT, s);
-  hipLaunchKernelGGL(evict_kernel<ITEMS>, dim3(a.groups), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL((evict_kernel<ITEMS, STAGE>), dim3(a.groups), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 

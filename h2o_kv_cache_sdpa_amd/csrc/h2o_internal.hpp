@@ -62,6 +62,7 @@ class KernelTimer {
 
 hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
+hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s);
 hipError_t launch_evict(const EvictArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_dequant(const KvWriteArgs &a, int n_slots, float *kout, float *vout, hipStream_t s);
