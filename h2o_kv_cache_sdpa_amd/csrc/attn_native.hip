@@ -154,26 +154,36 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
 
   // DMA of one 64-row tile: 16 segments of 1 KB (4 rows), 4 per wavefront.
-  auto issue_k = [&](int tile, char *dst) {
+  // Lane offsets inside a tile are fixed; a tile lying wholly in the cache or
+  // wholly in the chunk only moves a wave-uniform base.
+  const char *kc_base = static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES;
+  const char *vc_base = static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES;
+  const char *kn_base = static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES;
+  const char *vn_base = static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES;
+  auto lane_off = [&](int q, bool is_v) -> uint32_t {
+    const int row = (wave * 4 + q) * 4 + (lane >> 4);
+    const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
+    return static_cast<uint32_t>(row * ROW_BYTES + 16 * c);
+  };
+  auto issue_tile = [&](int tile, char *dst, const char *cbase, const char *nbase, const void *cache,
+                        const void *chunk, bool is_v) {
+    const int j0 = tile * 64;
+    if (j0 + 64 <= n_occ) {
+      const char *tb = cbase + static_cast<size_t>(j0) * ROW_BYTES;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int seg = wave * 4 + q;
-      const int row = seg * 4 + (lane >> 4);
-      const int c = kq_chunk_at(row, lane & 15);
-      dma16(key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, tile * 64 + row) + 16 * c,
-            dst + seg * 1024);
+      for (int q = 0; q < 4; ++q) dma16(tb + lane_off(q, is_v), dst + (wave * 4 + q) * 1024);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int seg = wave * 4 + q;
+        const int row = seg * 4 + (lane >> 4);
+        const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
+        dma16(key_row(cache, chunk, cache_row0, new_row0, n_occ, a.T, j0 + row) + 16 * c, dst + seg * 1024);
+      }
     }
   };
-  auto issue_v = [&](int tile, char *dst) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int seg = wave * 4 + q;
-      const int row = seg * 4 + (lane >> 4);
-      const int c = v_chunk_at(row, lane & 15);
-      dma16(key_row(a.vc, a.vn, cache_row0, new_row0, n_occ, a.T, tile * 64 + row) + 16 * c,
-            dst + seg * 1024);
-    }
-  };
+  auto issue_k = [&](int tile, char *dst) { issue_tile(tile, dst, kc_base, kn_base, a.kc, a.kn, false); };
+  auto issue_v = [&](int tile, char *dst) { issue_tile(tile, dst, vc_base, vn_base, a.vc, a.vn, true); };
 
   const int prow = perm_key(n);
   const int grp16 = lane >> 4, i16 = lane & 15;
@@ -228,23 +238,21 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
     bf16x8 pb[4];
-    float ls0 = 0.f, ls1 = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
     n0 = f32x16{};
     n1 = f32x16{};
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      {
-        const bf16x8 k0 = lds16(kb_next + kq_off(prow, 2 * st + hl));
-        const bf16x8 k1 = lds16(kb_next + kq_off(32 + prow, 2 * st + hl));
-        n0 = mfma32(k0, qf[st], n0);
-        n1 = mfma32(k1, qf[st], n1);
-      }
+      n0 = mfma32(lds16(kb_next + kq_off(prow, 2 * st + hl)), qf[st], n0);
+      n1 = mfma32(lds16(kb_next + kq_off(32 + prow, 2 * st + hl)), qf[st], n1);
       const float p00 = __builtin_amdgcn_exp2f(fmaf(c0[st], sl2, neg_m));
       const float p01 = __builtin_amdgcn_exp2f(fmaf(c0[8 + st], sl2, neg_m));
       const float p10 = __builtin_amdgcn_exp2f(fmaf(c1[st], sl2, neg_m));
       const float p11 = __builtin_amdgcn_exp2f(fmaf(c1[8 + st], sl2, neg_m));
-      ls0 += p00 + p01;
-      ls1 += p10 + p11;
+      ls[0] += p00;
+      ls[1] += p01;
+      ls[2] += p10;
+      ls[3] += p11;
       pb[0][st] = static_cast<__bf16>(p00);
       pb[1][st] = static_cast<__bf16>(p01);
       pb[2][st] = static_cast<__bf16>(p10);
@@ -253,23 +261,21 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
       __builtin_amdgcn_sched_group_barrier(SG_VALU, 14, 0);
     }
-    l_run += ls0 + ls1;
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // keys 16ks + 8h + 0..3 and + 4..7 at d = 32 blk + (lane % 32)
+    auto v_operand = [&](int ks, int blk) {
+      const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
+      const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
+      const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(vb + v_off(row, col >> 3) + 2 * (col & 7)));
+      const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(vb + v_off(row + 4, col >> 3) + 2 * (col & 7)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        // keys 16ks + 8h + 0..3 and + 4..7 at d = 32 blk + (lane % 32)
-        const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
-        const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
-        const char *p0 = vb + v_off(row, col >> 3) + 2 * (col & 7);
-        const char *p1 = vb + v_off(row + 4, col >> 3) + 2 * (col & 7);
-        const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(p0));
-        const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(p1));
-        const bf16x8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[blk] = mfma32(va, pb[ks], o[blk]);
-        __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
-        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
-      }
+    for (int step = 0; step < 16; ++step) {
+      const int ks = step >> 2, blk = step & 3;
+      o[blk] = mfma32(v_operand(ks, blk), pb[ks], o[blk]);
+      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
     }
   };
 
@@ -367,8 +373,33 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   const int t_last = j_base + PB_KEYS - 1 - n_occ;
   const size_t lse_base = static_cast<size_t>(b) * a.Hq * a.T;
 
-  // DMA of a 128-row Q block (32 KB: 32 segments, 8 per wavefront) and its normalisers
+  // DMA of a 128-row Q block (32 KB: 32 segments, 8 per wavefront) and its
+  // normalisers.  When q_g divides the block height, row rb + rr is query
+  // rb/q_g + rr/q_g of head g*q_g + rr%q_g: a per-lane constant offset plus a
+  // wave-uniform base.
+  const bool rows_split = (PB_ROWS % a.qg) == 0;
+  const char *q_grp = static_cast<const char *>(a.q) +
+                      (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg) * a.T * ROW_BYTES;
+  const float *l_grp = a.lse2 + lse_base + static_cast<size_t>(g) * a.qg * a.T;
+  uint32_t qoff[8];
+  uint32_t loff = 0;
+  if (rows_split) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int rr = (wave * 8 + q) * 4 + (lane >> 4);
+      qoff[q] = ((rr % a.qg) * a.T + rr / a.qg) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15);
+    }
+    const int rl = (wave & 1) * 64 + lane;
+    loff = (rl % a.qg) * a.T + rl / a.qg;
+  }
   auto issue_rows = [&](int rb, char *qdst, float *ldst) {
+    if (rows_split && rb + PB_ROWS <= R) {
+      const size_t shift = static_cast<size_t>(rb / a.qg);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dma16(q_grp + shift * ROW_BYTES + qoff[q], qdst + (wave * 8 + q) * 1024);
+      if (wave < 2) dma4(l_grp + shift + loff, reinterpret_cast<char *>(ldst + wave * 64));
+      return;
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int seg = wave * 8 + q;
@@ -407,23 +438,32 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     }
   };
 
+  // Row r sees chunk key t iff floor(r / q_g) >= t, i.e. r >= t * q_g.
+  const int first_row0 = tnew0 > 0 ? tnew0 * a.qg : 0;
+  const int first_row1 = tnew1 > 0 ? tnew1 * a.qg : 0;
+
   // One 128-row block: the MFMAs of sub-block k+1 run while the VALU sums
   // the exponentials of sub-block k.  FULL: every row sees every key.
   auto do_block = [&](auto full_tag, const char *qb, const float *lb, int rb) {
     constexpr bool FULL = decltype(full_tag)::value;
     f32x16 c0 = f32x16{}, c1 = f32x16{};
     float Lc[16];
+    {
+      bf16x8 qa = lds16(qb + kq_off(n, hl));
 #pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 qa = lds16(qb + kq_off(n, 2 * st + hl));
-      c0 = mfma32(qa, kf0[st], c0);
-      c1 = mfma32(qa, kf1[st], c1);
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 qn = qa;
+        if (st < 7) qn = lds16(qb + kq_off(n, 2 * (st + 1) + hl));
+        c0 = mfma32(qa, kf0[st], c0);
+        c1 = mfma32(qa, kf1[st], c1);
+        qa = qn;
+      }
     }
     load_l(lb, 0, Lc);
 #pragma unroll
     for (int sub = 1; sub <= 4; ++sub) {
       f32x16 n0 = f32x16{}, n1 = f32x16{};
-      float p0 = 0.f, p1 = 0.f;
+      float p0[2] = {0.f, 0.f}, p1[2] = {0.f, 0.f};
       const int rsub = rb + 32 * (sub - 1);  // rows of the block being summed
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
@@ -439,21 +479,20 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
           float x1 = fmaf(c1[r], sl2, -Lc[r]);
           if constexpr (!FULL) {
             const int row = rsub + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const int i = row / a.qg;
-            x0 = (row < R && tnew0 <= i) ? x0 : -INFINITY;
-            x1 = (row < R && tnew1 <= i) ? x1 : -INFINITY;
+            x0 = (row < R && row >= first_row0) ? x0 : -INFINITY;
+            x1 = (row < R && row >= first_row1) ? x1 : -INFINITY;
           }
-          p0 += __builtin_amdgcn_exp2f(x0);
-          p1 += __builtin_amdgcn_exp2f(x1);
+          p0[h2] += __builtin_amdgcn_exp2f(x0);
+          p1[h2] += __builtin_amdgcn_exp2f(x1);
         }
-        if (FULL && sub < 4) {
+        if (sub < 4) {
           __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
           __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_VALU, 12, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 12 : 20, 0);
         }
       }
-      add_comp(acc0, comp0, p0);
-      add_comp(acc1, comp1, p1);
+      add_comp(acc0, comp0, p0[0] + p0[1]);
+      add_comp(acc1, comp1, p1[0] + p1[1]);
       if (sub < 4) {
         c0 = n0;
         c1 = n1;
