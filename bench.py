@@ -12,7 +12,16 @@ measured with HIP events on the launch stream over the timed region;
 `cpu_baseline` times the fp64 oracle on a bounded sample of the same step.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
-       [--no-cpu-baseline]
+       [--no-cpu-baseline] [--calibrate-copy]
+       python bench.py --traffic-from FETCH_DIR WRITE_DIR   (no GPU)
+
+HBM traffic of the dominant kernel comes from two rocprofv3 counter runs of
+this script with --calibrate-copy (one collecting FETCH_SIZE, one WRITE_SIZE).
+--calibrate-copy appends a plain elementwise copy of known size after the
+timed region; the ratio of its known bytes to what each counter reads for it
+scales the attention kernel's readings to bytes.  --traffic-from turns the
+two counter folders into profiles/attn_a_traffic.json (tagged with a digest
+of the kernel sources, so a stale record is ignored) and prints a summary.
 """
 
 from __future__ import annotations
@@ -33,6 +42,15 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector / matrix peak
 PEAK_HBM_GBS = 8000.0
 N_CHUNKS = 4                # distinct chunks rotated through the timed steps
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_a_traffic.json")
+COPY_ELEMS = 64 << 20       # fp32 elements of the calibration copy (256 MiB each way)
+COPY_REPS = 3
+
+
+def dominant_kernel(w):
+    """Name of pass A's kernel for a workload, as the profiler reports it."""
+    if w.cache_fmt == "native" and w.D == 128 and w.dtype == "bf16":
+        return "attn_a_native"
+    return "attn_a_mfma"
 
 
 def kernel_sources_digest():
@@ -40,7 +58,7 @@ def kernel_sources_digest():
     HBM-traffic measurement is only reported while it still matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "h2o_kv_cache_sdpa_amd", "csrc")
-    for name in ("attn_mfma.hip", "device_util.hpp", "h2o_internal.hpp"):
+    for name in ("attn_native.hip", "attn_mfma.hip", "device_util.hpp", "h2o_internal.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -81,6 +99,48 @@ def cpu_baseline(w, groups=2):
     }
 
 
+def _counter_rows(folder, counter):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True)):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter:
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def traffic_from(workload, fetch_dir, write_dir):
+    """Scale FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of pass A by the calibration copy."""
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    kname = dominant_kernel(w)
+    out = {"workload": w.name, "kernel": kname, "sources": kernel_sources_digest()}
+    known = COPY_ELEMS * 4
+    for counter, folder, key in (("FETCH_SIZE", fetch_dir, "read"), ("WRITE_SIZE", write_dir, "write")):
+        rows = _counter_rows(folder, counter)
+        copy = [v for _, n, v in rows if "neg_kernel" in n][-COPY_REPS:]
+        attn = [v for _, n, v in rows if kname in n]
+        if len(copy) < COPY_REPS or len(attn) < 2:
+            raise SystemExit(f"{counter}: found {len(copy)} copy and {len(attn)} {kname} dispatches in {folder}")
+        attn = attn[1:]                          # drop the first (cold) dispatch
+        factor = known / (sum(copy) / len(copy) * 1024.0)
+        out[f"{key}_kib_counter"] = sum(attn) / len(attn)
+        out[f"{key}_factor"] = factor
+        out[f"{key}_bytes"] = out[f"{key}_kib_counter"] * 1024.0 * factor
+        out[f"{key}_dispatches"] = len(attn)
+    out["bytes_per_launch"] = out["read_bytes"] + out["write_bytes"]
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+    esz = {"native": 2 * D, "int8": D + 2, "int4": D // 2 + 4}[w.cache_fmt]
+    algo = 2 * B * Hkv * C * esz + 2 * B * Hq * T * D * 2 + 2 * B * Hkv * T * D * 2 + B * Hq * T * 4
+    out["algorithmic_bytes"] = algo
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,7 +148,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.workload, *args.traffic_from)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the chunk step shards "
                           "over (batch, KV head) groups with no exchange, but no multi-GPU "
@@ -170,6 +235,12 @@ def main():
         rec = json.load(open(TRAFFIC_FILE))
         if rec.get("sources") == kernel_sources_digest() and rec.get("workload") == w.name:
             traffic = rec.get("bytes_per_launch")
+    if args.calibrate_copy:
+        src = torch.randn(COPY_ELEMS, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
     line = {
         "metric": "H2O chunk-step tokens/s (S=32K,T=2048,bf16); % of MFMA/HBM roofline",
         "value": B * T / (ms_step * 1e-3),
@@ -187,7 +258,7 @@ def main():
                    "D": D, "cache_slots": C, "chunk": T, "cache_fmt": w.cache_fmt},
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_a_mfma (output + row normalisers)",
+            "kernel": dominant_kernel(w) + " (pass A: output and row normalisers)",
             "achieved": achieved_a,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
