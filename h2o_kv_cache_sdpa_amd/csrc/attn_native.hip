@@ -6,10 +6,14 @@
 // mask with the chunk attending before it is written: cache slots visible,
 // chunk keys causal), organised for throughput:
 //
-//  * K, V and Q tiles move HBM -> LDS with global_load_lds_dwordx4 (no
-//    staging registers, no VALU).  Each lane's 16 bytes land at
-//    segment_base + 16*lane, so a tile's XOR swizzle is produced by choosing
-//    which global chunk each lane fetches.
+//  * K, V and Q tiles move HBM -> LDS with buffer_load_dwordx4 ... lds (no
+//    staging registers).  Each lane's 16 bytes land at segment_base +
+//    16*lane, so a tile's XOR swizzle is produced by choosing which global
+//    chunk each lane fetches; the per-lane offset is a loop constant and the
+//    tile position goes into the scalar offset.  The buffer form (rather than
+//    global_load_lds) keeps the LDS-read counter in order, so a read issued
+//    ahead of its use is waited for with lgkmcnt(N) instead of lgkmcnt(0).
+//  * Operands read from LDS are fetched one MFMA step ahead of their use.
 //  * V stays row-major [key][d] in LDS; the A operand of O^T = V^T P^T (keys
 //    contiguous per lane) comes from ds_read_b64_tr_b16: within a 16-lane
 //    group, lane k supplies V[kb + k/4][c0 + 4(k%4) .. +3] and lane i receives
@@ -40,7 +44,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-typedef __attribute__((address_space(1))) void gbl_void;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int D = 128;
 constexpr int ROW_BYTES = D * 2;    // 256
@@ -51,12 +55,19 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ void dma16(const void *src, char *lds_segment) {
-  __builtin_amdgcn_global_load_lds((gbl_void *)(src), (lds_void *)(lds_segment), 16, 0, 0);
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3:
+// 32-bit data format, no swizzle).  Lanes whose offset is past `bytes` read 0.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
 }
 
-__device__ __forceinline__ void dma4(const void *src, char *lds_segment) {
-  __builtin_amdgcn_global_load_lds((gbl_void *)(src), (lds_void *)(lds_segment), 4, 0, 0);
+// LDS DMA: lane l's `size` bytes from base + voff + soff land at lds_segment + size*l.
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, char *lds_segment) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds_segment), 16, voff, soff, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, char *lds_segment) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(lds_segment), 4, voff, soff, 0, 0);
 }
 
 __device__ __forceinline__ void wait_dma_and_sync() {
@@ -154,38 +165,43 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
 
   // DMA of one 64-row tile: 16 segments of 1 KB (4 rows), 4 per wavefront.
-  // Lane offsets inside a tile are fixed; a tile lying wholly in the cache or
-  // wholly in the chunk only moves a wave-uniform base.
-  const char *kc_base = static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES;
-  const char *vc_base = static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES;
-  const char *kn_base = static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES;
-  const char *vn_base = static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES;
+  // Buffer resources span this group's n_occ cache rows and T chunk rows;
+  // chunk rows past T read as zeros (and are masked).  A tile lying wholly in
+  // the cache moves only the scalar offset.
+  const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
+  const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
+  const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
+  const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
   auto lane_off = [&](int q, bool is_v) -> uint32_t {
     const int row = (wave * 4 + q) * 4 + (lane >> 4);
     const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
     return static_cast<uint32_t>(row * ROW_BYTES + 16 * c);
   };
-  auto issue_tile = [&](int tile, char *dst, const char *cbase, const char *nbase, const void *cache,
-                        const void *chunk, bool is_v) {
+  auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs, bool is_v) {
     const int j0 = tile * 64;
     if (j0 + 64 <= n_occ) {
-      const char *tb = cbase + static_cast<size_t>(j0) * ROW_BYTES;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16(tb + lane_off(q, is_v), dst + (wave * 4 + q) * 1024);
+      for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
     } else {
+      // chunk rows (and, in the one tile that straddles n_occ, cache rows)
+      const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int seg = wave * 4 + q;
-        const int row = seg * 4 + (lane >> 4);
-        const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
-        dma16(key_row(cache, chunk, cache_row0, new_row0, n_occ, a.T, j0 + row) + 16 * c, dst + seg * 1024);
+        const int row = (wave * 4 + q) * 4 + (lane >> 4);
+        const uint32_t lo = lane_off(q, is_v);
+        if (dt + row >= 0) {
+          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+        } else {
+          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+        }
       }
     }
   };
-  auto issue_k = [&](int tile, char *dst) { issue_tile(tile, dst, kc_base, kn_base, a.kc, a.kn, false); };
-  auto issue_v = [&](int tile, char *dst) { issue_tile(tile, dst, vc_base, vn_base, a.vc, a.vn, true); };
+  auto issue_k = [&](int tile, char *dst) { issue_tile(tile, dst, kc_rs, kn_rs, false); };
+  auto issue_v = [&](int tile, char *dst) { issue_tile(tile, dst, vc_rs, vn_rs, true); };
 
   const int prow = perm_key(n);
+  const uint32_t k_lane = static_cast<uint32_t>(prow * ROW_BYTES + ((hl ^ (prow & 15)) << 4));
   const int grp16 = lane >> 4, i16 = lane & 15;
   f32x16 o[4];
 #pragma unroll
@@ -241,10 +257,25 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
     n0 = f32x16{};
     n1 = f32x16{};
+    // K operand of step st at k_lane ^ (st << 5) (rows prow and 32 + prow);
+    // k_lane is made opaque per tile so that the eight addresses cost one
+    // v_xor each instead of eight registers held across the loop.
+    uint32_t ka = k_lane;
+    asm volatile("" : "+v"(ka));
+    bf16x8 kc0 = lds16(kb_next + ka), kc1 = lds16(kb_next + ka + 32 * ROW_BYTES);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      n0 = mfma32(lds16(kb_next + kq_off(prow, 2 * st + hl)), qf[st], n0);
-      n1 = mfma32(lds16(kb_next + kq_off(32 + prow, 2 * st + hl)), qf[st], n1);
+      bf16x8 kn0 = kc0, kn1 = kc1;
+      if (st < 7) {
+        const char *kp = kb_next + (ka ^ ((st + 1) << 5));
+        kn0 = lds16(kp);
+        kn1 = lds16(kp + 32 * ROW_BYTES);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      n0 = mfma32(kc0, qf[st], n0);
+      n1 = mfma32(kc1, qf[st], n1);
+      kc0 = kn0;
+      kc1 = kn1;
       const float p00 = __builtin_amdgcn_exp2f(fmaf(c0[st], sl2, neg_m));
       const float p01 = __builtin_amdgcn_exp2f(fmaf(c0[8 + st], sl2, neg_m));
       const float p10 = __builtin_amdgcn_exp2f(fmaf(c1[st], sl2, neg_m));
@@ -257,9 +288,11 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
       pb[1][st] = static_cast<__bf16>(p01);
       pb[2][st] = static_cast<__bf16>(p10);
       pb[3][st] = static_cast<__bf16>(p11);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_VALU, 14, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     // keys 16ks + 8h + 0..3 and + 4..7 at d = 32 blk + (lane % 32)
@@ -270,12 +303,16 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
       const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(vb + v_off(row + 4, col >> 3) + 2 * (col & 7)));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
+    bf16x8 vc = v_operand(0, 0);
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
       const int ks = step >> 2, blk = step & 3;
-      o[blk] = mfma32(v_operand(ks, blk), pb[ks], o[blk]);
-      __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2, 1);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 1);
+      bf16x8 vn = vc;
+      if (step < 15) vn = v_operand((step + 1) >> 2, (step + 1) & 3);
+      __builtin_amdgcn_sched_barrier(0);
+      o[blk] = mfma32(vc, pb[ks], o[blk]);
+      vc = vn;
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -378,9 +415,12 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   // rb/q_g + rr/q_g of head g*q_g + rr%q_g: a per-lane constant offset plus a
   // wave-uniform base.
   const bool rows_split = (PB_ROWS % a.qg) == 0;
-  const char *q_grp = static_cast<const char *>(a.q) +
-                      (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg) * a.T * ROW_BYTES;
-  const float *l_grp = a.lse2 + lse_base + static_cast<size_t>(g) * a.qg * a.T;
+  // The group's q_g query heads (q_g*T rows of Q) and their normalisers are
+  // contiguous: row r = i*q_g + hh lives at (hh*T + i).
+  const rsrc_t q_rs = make_rsrc(static_cast<const char *>(a.q) +
+                                    (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg) * a.T * ROW_BYTES,
+                                R * ROW_BYTES);
+  const rsrc_t l_rs = make_rsrc(a.lse2 + lse_base + static_cast<size_t>(g) * a.qg * a.T, R * 4);
   uint32_t qoff[8];
   uint32_t loff = 0;
   if (rows_split) {
@@ -390,14 +430,14 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
       qoff[q] = ((rr % a.qg) * a.T + rr / a.qg) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15);
     }
     const int rl = (wave & 1) * 64 + lane;
-    loff = (rl % a.qg) * a.T + rl / a.qg;
+    loff = ((rl % a.qg) * a.T + rl / a.qg) * 4;
   }
   auto issue_rows = [&](int rb, char *qdst, float *ldst) {
     if (rows_split && rb + PB_ROWS <= R) {
-      const size_t shift = static_cast<size_t>(rb / a.qg);
+      const uint32_t shift = static_cast<uint32_t>(rb / a.qg);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dma16(q_grp + shift * ROW_BYTES + qoff[q], qdst + (wave * 8 + q) * 1024);
-      if (wave < 2) dma4(l_grp + shift + loff, reinterpret_cast<char *>(ldst + wave * 64));
+      for (int q = 0; q < 8; ++q) dma16(q_rs, qoff[q], shift * ROW_BYTES, qdst + (wave * 8 + q) * 1024);
+      if (wave < 2) dma4(l_rs, loff, shift * 4, reinterpret_cast<char *>(ldst + wave * 64));
       return;
     }
 #pragma unroll
@@ -406,17 +446,14 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
       const int rr = seg * 4 + (lane >> 4);
       int row = rb + rr;
       row = row < R ? row : R - 1;  // rows past the end are masked
-      const int ii = row / a.qg, hh = g * a.qg + row % a.qg;
-      const char *src = static_cast<const char *>(a.q) +
-                        ((static_cast<size_t>(b) * a.Hq + hh) * a.T + ii) * ROW_BYTES;
-      dma16(src + 16 * kq_chunk_at(rr, lane & 15), qdst + seg * 1024);
+      const int ii = row / a.qg, hh = row % a.qg;
+      dma16(q_rs, (hh * a.T + ii) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, qdst + seg * 1024);
     }
     if (wave < 2) {
       int row = rb + wave * 64 + lane;
       row = row < R ? row : R - 1;
-      const int ii = row / a.qg, hh = g * a.qg + row % a.qg;
-      dma4(a.lse2 + lse_base + static_cast<size_t>(hh) * a.T + ii,
-           reinterpret_cast<char *>(ldst + wave * 64));
+      const int ii = row / a.qg, hh = row % a.qg;
+      dma4(l_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(ldst + wave * 64));
     }
   };
 
@@ -438,6 +475,7 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     }
   };
 
+  const uint32_t q_lane = static_cast<uint32_t>(n * ROW_BYTES + ((hl ^ (n & 15)) << 4));
   // Row r sees chunk key t iff floor(r / q_g) >= t, i.e. r >= t * q_g.
   const int first_row0 = tnew0 > 0 ? tnew0 * a.qg : 0;
   const int first_row1 = tnew1 > 0 ? tnew1 * a.qg : 0;
@@ -446,18 +484,22 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   // the exponentials of sub-block k.  FULL: every row sees every key.
   auto do_block = [&](auto full_tag, const char *qb, const float *lb, int rb) {
     constexpr bool FULL = decltype(full_tag)::value;
+    // Q operand of sub-block sub, step st: sub * 32 rows + (q_lane ^ (st << 5));
+    // q_lane is made opaque per block (one v_xor per read, no held addresses).
+    uint32_t qa_l = q_lane;
+    asm volatile("" : "+v"(qa_l));
+    auto qop = [&](int sub, int st) { return lds16(qb + sub * (32 * ROW_BYTES) + (qa_l ^ (st << 5))); };
     f32x16 c0 = f32x16{}, c1 = f32x16{};
     float Lc[16];
-    {
-      bf16x8 qa = lds16(qb + kq_off(n, hl));
+    bf16x8 qc = qop(0, 0);
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        bf16x8 qn = qa;
-        if (st < 7) qn = lds16(qb + kq_off(n, 2 * (st + 1) + hl));
-        c0 = mfma32(qa, kf0[st], c0);
-        c1 = mfma32(qa, kf1[st], c1);
-        qa = qn;
-      }
+    for (int st = 0; st < 8; ++st) {
+      const bf16x8 qn = st < 7 ? qop(0, st + 1) : qop(1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      c0 = mfma32(qc, kf0[st], c0);
+      c1 = mfma32(qc, kf1[st], c1);
+      qc = qn;
+      __builtin_amdgcn_sched_barrier(0);
     }
     load_l(lb, 0, Lc);
 #pragma unroll
@@ -468,9 +510,16 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         if (sub < 4) {
-          const bf16x8 qa = lds16(qb + kq_off(32 * sub + n, 2 * st + hl));
-          n0 = mfma32(qa, kf0[st], n0);
-          n1 = mfma32(qa, kf1[st], n1);
+          bf16x8 qn = qc;
+          if (st < 7) {
+            qn = qop(sub, st + 1);
+          } else if (sub < 3) {
+            qn = qop(sub + 1, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          n0 = mfma32(qc, kf0[st], n0);
+          n1 = mfma32(qc, kf1[st], n1);
+          qc = qn;
         }
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
@@ -486,9 +535,11 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
           p1[h2] += __builtin_amdgcn_exp2f(x1);
         }
         if (sub < 4) {
-          __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 12 : 20, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 6 : 10, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 6 : 10, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       add_comp(acc0, comp0, p0[0] + p0[1]);
