@@ -43,6 +43,12 @@ R7 A chunk either fits (n_occ + T <= C, fill) or meets a full cache
 R8 Scale = d_h^{-1/2} given as an fp32 value; the oracle promotes it to fp64.
 R9 The chunk attends to its own keys and values at input precision; they are
    quantised only when written into a quantised cache.
+R11 Policy variants ([LF] §3.1.1).  h2o_orig ranks slot j of KV head h by
+   the sum over batch rows of the per-row scores, so every batch row selects
+   the same slots; the per-row scores are still kept.  h2o_norm ranks slot j
+   by its score divided by its age t - t(b,h,j), with t the number of tokens
+   processed once this chunk is attended (pos + T), i.e. the number of queries
+   that have contributed to the score; the stored score stays cumulative.
 R10 Quantisers (fp32 operation sequences, IEEE round-to-nearest-even):
    int8 symmetric per slot:  a = max|x|;  s = fp16(fp32(a / 127));
         c = clamp(rne(fp32(x / fp32(s))), -127, 127);  x_hat = c * s
@@ -60,6 +66,8 @@ __all__ = [
     "attend_chunk",
     "update_scores",
     "bottom_t",
+    "selection_key",
+    "POLICIES",
     "quantize_int8",
     "quantize_int4",
     "dequantize_int8",
@@ -141,12 +149,36 @@ def update_scores(phi, w, n_occ, C, T):
     return phi
 
 
+POLICIES = ("h2o", "h2o_norm", "h2o_orig")
+
+
+def selection_key(phi_updated, token_pos, pos, T, policy="h2o"):
+    """The value the occupied slots are ranked by when the cache is full
+    ([LF] §3.1.1, reading R11), shape (B, Hkv, C).
+
+    h2o:      the cumulative score itself.
+    h2o_norm: score / (t - t(b,h,j)) with t = pos + T.
+    h2o_orig: sum over b of the scores, the same for every b.
+    """
+    phi = np.asarray(phi_updated, dtype=np.float64)
+    if policy == "h2o":
+        return phi.copy()
+    if policy == "h2o_norm":
+        age = (pos + T) - np.asarray(token_pos, dtype=np.float64)
+        return phi / age
+    if policy == "h2o_orig":
+        tot = phi.sum(axis=0, keepdims=True)
+        return np.broadcast_to(tot, phi.shape).copy()
+    raise ValueError(f"unknown policy {policy!r}")
+
+
 def bottom_t(phi_updated, n_occ, C, T):
     """Slots that receive the chunk's T tokens (readings R4, R5, R7).
 
     Fill (n_occ + T <= C): slots n_occ .. n_occ+T-1 (left to right, [LF] §3.1).
-    Evict (n_occ == C): the T smallest entries under (score, index), returned
-    in ascending index order.
+    Evict (n_occ == C): the T smallest entries under (key, index), returned in
+    ascending index order; the key is the updated score, or the policy's
+    selection_key.
     """
     B, Hkv = phi_updated.shape[:2]
     if n_occ + T <= C:
@@ -239,10 +271,13 @@ class OracleCache:
     Scores are held in fp64; token_pos starts at -1 for empty slots.
     """
 
-    def __init__(self, B, Hq, Hkv, D, C, fmt="native", scale=None):
+    def __init__(self, B, Hq, Hkv, D, C, fmt="native", scale=None, policy="h2o"):
         assert Hq % Hkv == 0
         self.B, self.Hq, self.Hkv, self.D, self.C = B, Hq, Hkv, D, C
         self.fmt = fmt
+        if policy not in POLICIES:
+            raise ValueError(f"unknown policy {policy!r}")
+        self.policy = policy
         self.scale = float(np.float32(1.0 / np.sqrt(D))) if scale is None else float(scale)
         self.k = np.zeros((B, Hkv, C, D))      # values attended (dequantised for int formats)
         self.v = np.zeros((B, Hkv, C, D))
@@ -292,8 +327,9 @@ class OracleCache:
         """Attend, accumulate scores, select, log and overwrite (readings R1-R9).
 
         q (B,Hq,T,D), k_new/v_new (B,Hkv,T,D): float64 arrays of the input values.
-        Returns dict(out, w, lse, slots, phi_updated) where phi_updated holds the
-        scores after accumulation and before the selected slots are re-seeded.
+        Returns dict(out, w, lse, slots, phi_updated, rank_key) where phi_updated
+        holds the scores after accumulation and before the selected slots are
+        re-seeded, and rank_key the values the slots were ranked by.
         """
         T = q.shape[2]
         C, n_occ = self.C, self.n_occ
@@ -301,7 +337,10 @@ class OracleCache:
             raise ValueError("chunk straddles capacity")
         out, w, lse = attend_chunk(q, self.k, self.v, n_occ, k_new, v_new, self.scale)
         phi_upd = update_scores(self.phi, w, n_occ, C, T)
-        slots = bottom_t(phi_upd, n_occ, C, T)
+        key = phi_upd
+        if n_occ == C:
+            key = selection_key(phi_upd, self.token_pos, self.pos, T, self.policy)
+        slots = bottom_t(key, n_occ, C, T)
         self.phi = phi_upd.copy()
         for b in range(self.B):
             for g in range(self.Hkv):
@@ -311,4 +350,4 @@ class OracleCache:
                 self.token_pos[b, g, r] = self.pos + np.arange(T)
         self.n_occ = min(n_occ + T, C)
         self.pos += T
-        return dict(out=out, w=w, lse=lse, slots=slots, phi_updated=phi_upd)
+        return dict(out=out, w=w, lse=lse, slots=slots, phi_updated=phi_upd, rank_key=key)

@@ -19,7 +19,12 @@ def _dot(a, b):
 
 
 class BruteCache:
-    def __init__(self, B, Hq, Hkv, D, C, scale):
+    """policy: "h2o" (rank by the score), "h2o_norm" (score divided by the
+    number of queries that have seen the slot so far) or "h2o_orig" (score
+    summed over the batch rows; every row evicts the same slots)."""
+
+    def __init__(self, B, Hq, Hkv, D, C, scale, policy="h2o"):
+        self.policy = policy
         self.B, self.Hq, self.Hkv, self.D, self.C = B, Hq, Hkv, D, C
         self.qg = Hq // Hkv
         self.scale = scale
@@ -52,24 +57,36 @@ class BruteCache:
                         w[b][g][jj] += p
                         for d in range(D):
                             out[b][h][i][d] += p * vals[jj][d]
+        for b in range(B):
+            for g in range(self.Hkv):
+                for j in range(n):
+                    self.phi[b][g][j] += w[b][g][j]
         slots = []
         for b in range(B):
             srow = []
             for g in range(self.Hkv):
-                for j in range(n):
-                    self.phi[b][g][j] += w[b][g][j]
                 if n + T <= C:
                     chosen = list(range(n, n + T))
                 else:
-                    ranked = sorted(((self.phi[b][g][j], j) for j in range(C)))
+                    def rank(j):
+                        if self.policy == "h2o_orig":
+                            return sum(self.phi[bb][g][j] for bb in range(B))
+                        if self.policy == "h2o_norm":
+                            seen = self.pos + T - self.tpos[b][g][j]  # queries that have attended slot j
+                            return self.phi[b][g][j] / seen
+                        return self.phi[b][g][j]
+                    ranked = sorted((rank(j), j) for j in range(C))
                     chosen = sorted(j for _, j in ranked[:T])
+                srow.append(chosen)
+            slots.append(srow)
+        for b in range(B):
+            for g in range(self.Hkv):
+                chosen = slots[b][g]
                 for t, j in enumerate(chosen):
                     self.k[b][g][j] = list(kn[b][g][t])
                     self.v[b][g][j] = list(vn[b][g][t])
                     self.phi[b][g][j] = w[b][g][n + t]
                     self.tpos[b][g][j] = self.pos + t
-                srow.append(chosen)
-            slots.append(srow)
         self.n_occ = min(n + T, C)
         self.pos += T
         return out, w, slots

@@ -68,12 +68,13 @@ def test_worked_example_golden():
 # brute force on a tiny stream with evictions
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("policy", O.POLICIES)
 @pytest.mark.parametrize("seed", [0, 1])
-def test_bruteforce_tiny_stream(seed):
+def test_bruteforce_tiny_stream(seed, policy):
     B, Hq, Hkv, D, C, T = 2, 4, 2, 4, 8, 2
     scale = float(np.float32(1 / math.sqrt(D)))
-    oc = O.OracleCache(B, Hq, Hkv, D, C, scale=scale)
-    bc = BruteCache(B, Hq, Hkv, D, C, scale)
+    oc = O.OracleCache(B, Hq, Hkv, D, C, scale=scale, policy=policy)
+    bc = BruteCache(B, Hq, Hkv, D, C, scale, policy=policy)
     for step in range(8):  # 4 fill + 4 evicting steps
         ch = W.random_chunk([100 + seed, step], B, Hq, Hkv, T, D, "f32", hh_frac=0.5)
         q, kn, vn = ch["q"].f64, ch["k"].f64, ch["v"].f64
@@ -358,3 +359,62 @@ def test_quantisers_fp32_rows_by_fractions(fmt):
             for v, c in zip(row, codes[r].tolist()):
                 d = _f32(float(Fraction(v) - Fraction(z)))
                 assert c == max(0, min(15, _rne(_f32(float(Fraction(d) / Fraction(s))))))
+
+
+# ---------------------------------------------------------------------------
+# policy variants (h2o_norm, h2o_orig)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
+def test_policy_selection_golden(policy):
+    """Hand-worked selections (tests/golden/policy_selection_examples.json)."""
+    ex = json.load(open(os.path.join(GOLDEN, "policy_selection_examples.json")))[policy]
+    phi = np.array(ex["phi_updated"], dtype=np.float64)
+    tp = np.array(ex["token_pos"], dtype=np.int64)
+    C, T, pos = ex["C"], ex["T"], ex["pos"]
+    key = O.selection_key(phi, tp, pos, T, policy)
+    assert O.bottom_t(key, C, C, T).tolist() == ex["slots"]
+    plain = O.selection_key(phi, tp, pos, T, "h2o")
+    assert O.bottom_t(plain, C, C, T).tolist() == ex["slots_plain_h2o"]
+
+
+def test_orig_with_one_batch_row_is_h2o():
+    """With B = 1 the batch sum is the score itself: identical streams."""
+    B, Hq, Hkv, D, C, T = 1, 4, 2, 8, 16, 4
+    a = O.OracleCache(B, Hq, Hkv, D, C, policy="h2o")
+    b = O.OracleCache(B, Hq, Hkv, D, C, policy="h2o_orig")
+    for step in range(10):
+        ch = W.random_chunk([7, step], B, Hq, Hkv, T, D, "f32", hh_frac=0.25)
+        ra = a.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        rb = b.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        assert (ra["slots"] == rb["slots"]).all()
+    np.testing.assert_array_equal(a.phi, b.phi)
+
+
+def test_orig_rows_select_identical_slots_and_keep_own_scores():
+    B, Hq, Hkv, D, C, T = 3, 4, 2, 8, 16, 4
+    oc = O.OracleCache(B, Hq, Hkv, D, C, policy="h2o_orig")
+    for step in range(10):
+        ch = W.random_chunk([8, step], B, Hq, Hkv, T, D, "f32", hh_frac=0.25)
+        r = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        assert (r["slots"] == r["slots"][:1]).all()
+    # every row's slots hold the same token positions (rows evolve in lockstep)
+    assert (oc.token_pos == oc.token_pos[:1]).all()
+    # but the per-row scores differ
+    assert not np.allclose(oc.phi[0], oc.phi[1])
+
+
+def test_norm_divides_by_queries_seen():
+    """A slot's normalised key times the number of queries that have attended
+    it gives back its cumulative score (every key is a per-query average)."""
+    B, Hq, Hkv, D, C, T = 1, 2, 1, 8, 12, 3
+    oc = O.OracleCache(B, Hq, Hkv, D, C, policy="h2o_norm")
+    for step in range(8):
+        ch = W.random_chunk([9, step], B, Hq, Hkv, T, D, "f32")
+        tp_before = oc.token_pos.copy()
+        r = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        if step >= C // T:
+            seen = oc.pos - tp_before  # queries at positions tp .. pos-1
+            np.testing.assert_allclose(r["rank_key"] * seen, r["phi_updated"], rtol=1e-13)
+            # each query spreads q_g = Hq/Hkv units of weight, so the average is at most q_g
+            assert (r["rank_key"] <= Hq // Hkv + 1e-12).all()
