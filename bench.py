@@ -147,6 +147,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
+    ap.add_argument("--policy", default="h2o", choices=["h2o", "h2o_norm", "h2o_orig"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -175,7 +176,7 @@ def main():
     B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
 
     # ---- resident inputs: a full cache and a rotation of chunks ----
-    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=dev)
+    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=dev, policy=args.policy)
     seed = [w.cfg_id, 777]
     if w.cache_fmt == "native":
         k, v, scores, tp, _ = W.random_cache(seed, B, Hkv, C, D, C, w.dtype, hh_frac=0.02)
@@ -255,7 +256,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: evicting chunk step", "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "D": D, "cache_slots": C, "chunk": T, "cache_fmt": w.cache_fmt},
+                   "D": D, "cache_slots": C, "chunk": T, "cache_fmt": w.cache_fmt, "policy": args.policy},
         "roofline": {
             "bound": "mfma",
             "kernel": dominant_kernel(w) + " (pass A: output and row normalisers)",

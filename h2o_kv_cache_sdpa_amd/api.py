@@ -108,9 +108,12 @@ def status_str(status):
     return lib().h2o_status_str(int(status)).decode()
 
 
+POLICIES = {"h2o": 0, "h2o_norm": 1, "h2o_orig": 2}
+
+
 def make_dims(B, Hq, Hkv, D, C, T, dtype="bf16", cache_fmt="native", scale=0.0, policy=0):
     return H2ODims(B, Hq, Hkv, D, C, T, DTYPES.get(dtype, dtype), FORMATS.get(cache_fmt, cache_fmt),
-                   policy, float(scale))
+                   POLICIES.get(policy, policy), float(scale))
 
 
 def workspace_bytes(dims):

@@ -16,10 +16,10 @@ _TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 class H2OCache:
     def __init__(self, B, Hq, Hkv, D, C, T, dtype="bf16", cache_fmt="native", scale=0.0,
-                 device="cuda", track_positions=True):
+                 device="cuda", track_positions=True, policy="h2o"):
         self.B, self.Hq, self.Hkv, self.D, self.C, self.T = B, Hq, Hkv, D, C, T
-        self.dtype, self.cache_fmt = dtype, cache_fmt
-        self.dims = api.make_dims(B, Hq, Hkv, D, C, T, dtype, cache_fmt, scale)
+        self.dtype, self.cache_fmt, self.policy = dtype, cache_fmt, policy
+        self.dims = api.make_dims(B, Hq, Hkv, D, C, T, dtype, cache_fmt, scale, policy)
         self.device = torch.device(device)
         z = dict(device=self.device)
         self.k_scale = self.v_scale = self.k_zero = self.v_zero = None

@@ -1,10 +1,16 @@
 // Score accumulate + slot selection + replay log + seeding, one workgroup of
-// 1024 threads per (b, KV head).
+// 1024 threads per (b, KV head) -- per KV head for h2o_orig.
 //
 // H2O score = cumulative sum of attention weights; the lowest-scoring slots are
 // overwritten (aimodeling article on KeysAndValues; "Learning how to Forget",
 // §3.1.1).  While the cache has room it fills left to right (§3.1).  Every
-// decision goes to the replay log (§3.2).
+// decision goes to the replay log (§3.2).  Ranking key per policy (§3.1.1):
+//   h2o       the updated score;
+//   h2o_norm  the updated score / (t - t(b,h,j)), t = pos + T (the number of
+//             queries that have attended the slot), in IEEE fp32;
+//   h2o_orig  the updated scores summed over b (fp32, b ascending); every
+//             batch row then takes the same slots.
+// The stored scores stay cumulative and per (b, h, slot) under all three.
 //
 // Selection of the T smallest keys under (score, slot index) is an MSB-first
 // radix select over the order-preserving uint32 image of the fp32 scores
@@ -57,7 +63,7 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t &ea
   eb = pb + ib - b;
 }
 
-template <int ITEMS, bool STAGE>
+template <int ITEMS, bool STAGE, int POL>
 __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
   // Updated scores pass through LDS so that global traffic is coalesced while
   // each thread still owns a contiguous index range (row stride ITEMS + 1
@@ -69,15 +75,38 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int grp = blockIdx.x;
   const int C = a.C, T = a.T, n_occ = a.n_occ;
   const int n_keys = n_occ + T;
+  // h2o_orig: this workgroup serves KV head blockIdx.x of every batch row
+  const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+  auto grp_of = [&](int bb) { return (POL == H2O_POLICY_ORIG) ? bb * a.Hkv + blockIdx.x : blockIdx.x; };
+  const int grp = grp_of(0);
   float *phi = a.scores + static_cast<size_t>(grp) * C;
   const float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
   int32_t *log = a.slot_log + static_cast<size_t>(grp) * T;
   int32_t *tp = a.token_pos ? a.token_pos + static_cast<size_t>(grp) * C : nullptr;
+  // Updated score of slot j in every batch row served; returns the ranking value.
+  auto update = [&](int j) -> float {
+    if constexpr (POL == H2O_POLICY_ORIG) {
+      float tot = 0.f;
+      for (int bb = 0; bb < nb; ++bb) {
+        const size_t g = static_cast<size_t>(grp_of(bb));
+        const float f = a.scores[g * C + j] + a.wsum[g * n_keys + j];
+        a.scores[g * C + j] = f;
+        tot = (bb == 0) ? f : tot + f;
+      }
+      return tot;
+    } else {
+      const float f = phi[j] + w[j];
+      phi[j] = f;
+      if constexpr (POL == H2O_POLICY_NORM) {
+        return f / static_cast<float>(a.pos + T - tp[j]);
+      }
+      return f;
+    }
+  };
 
-  if (n_occ + T <= C) {  // filling: left to right
+  if (POL != H2O_POLICY_ORIG && n_occ + T <= C) {  // filling: left to right
     for (int j = tid; j < n_occ; j += NT) phi[j] = phi[j] + w[j];
     for (int t = tid; t < T; t += NT) {
       const int slot = n_occ + t;
@@ -92,11 +121,7 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
   const int base = tid * ITEMS;
   uint32_t key[ITEMS];
   if constexpr (STAGE) {  // coalesced, staged in LDS
-    for (int j = tid; j < C; j += NT) {
-      const float f = phi[j] + w[j];
-      phi[j] = f;
-      stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = f;
-    }
+    for (int j = tid; j < C; j += NT) stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = update(j);
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k)
@@ -106,11 +131,7 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
     for (int k = 0; k < ITEMS; ++k) {
       const int j = base + k;
       key[k] = 0xffffffffu;
-      if (j < C) {
-        const float f = phi[j] + w[j];
-        phi[j] = f;
-        key[k] = ordered_key(f);
-      }
+      if (j < C) key[k] = ordered_key(update(j));
     }
   }
 
@@ -196,25 +217,38 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
       ++eq_before;
     }
     if (out >= 0) {
-      log[out] = j;
-      phi[j] = w[C + out];
-      if (tp) tp[j] = static_cast<int32_t>(a.pos + out);
+      for (int bb = 0; bb < nb; ++bb) {
+        const size_t g = static_cast<size_t>(grp_of(bb));
+        a.slot_log[g * T + out] = j;
+        a.scores[g * C + j] = a.wsum[g * n_keys + C + out];
+        if (a.token_pos) a.token_pos[g * C + j] = static_cast<int32_t>(a.pos + out);
+      }
     }
   }
 }
 
-template <int ITEMS>
-hipError_t launch_items(const EvictArgs &a, hipStream_t s) {
+template <int ITEMS, int POL>
+hipError_t launch_pol(const EvictArgs &a, hipStream_t s) {
   constexpr bool STAGE = ITEMS <= 32;  // 1024 x 33 floats = 132 KB of LDS at most
   constexpr int stage_bytes = STAGE ? static_cast<int>(sizeof(float)) * NT * (ITEMS + 1) : 0;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void *>(&evict_kernel<ITEMS, STAGE>),
+      reinterpret_cast<const void *>(&evict_kernel<ITEMS, STAGE, POL>),
       hipFuncAttributeMaxDynamicSharedMemorySize, stage_bytes);
   if (attr != hipSuccess) return attr;
-  const size_t lds = (a.n_occ == a.C) ? stage_bytes : 0;
+  const bool evicting = a.n_occ == a.C;
+  const size_t lds = evicting ? stage_bytes : 0;
+  const int grid = (POL == H2O_POLICY_ORIG) ? a.Hkv : a.groups;
   KernelTimer timer(H2O_K_EVICT, s);
-  hipLaunchKernelGGL((evict_kernel<ITEMS, STAGE>), dim3(a.groups), dim3(NT), lds, s, a);
+  hipLaunchKernelGGL((evict_kernel<ITEMS, STAGE, POL>), dim3(grid), dim3(NT), lds, s, a);
   return hipGetLastError();
+}
+
+template <int ITEMS>
+hipError_t launch_items(const EvictArgs &a, hipStream_t s) {
+  // Filling is the same under every policy.
+  if (a.n_occ + a.T <= a.C || a.policy == H2O_POLICY_H2O) return launch_pol<ITEMS, H2O_POLICY_H2O>(a, s);
+  if (a.policy == H2O_POLICY_NORM) return launch_pol<ITEMS, H2O_POLICY_NORM>(a, s);
+  return launch_pol<ITEMS, H2O_POLICY_ORIG>(a, s);
 }
 
 }  // namespace

@@ -29,7 +29,7 @@ int check_dims(const h2o_dims *d) {
   if (d->dtype != H2O_F32 && d->dtype != H2O_BF16) return H2O_EINVAL;
   if (d->cache_fmt < H2O_CACHE_NATIVE || d->cache_fmt > H2O_CACHE_INT4) return H2O_EINVAL;
   if (!(std::isfinite(d->scale) && d->scale >= 0.f)) return H2O_EINVAL;
-  if (d->policy != H2O_POLICY_H2O) return H2O_EUNSUPPORTED;
+  if (d->policy < H2O_POLICY_H2O || d->policy > H2O_POLICY_ORIG) return H2O_EUNSUPPORTED;
   if (d->D != 64 && d->D != 128) return H2O_EUNSUPPORTED;
   // index arithmetic inside the kernels uses 32-bit row counts
   const int64_t rows = static_cast<int64_t>(d->Hq / d->Hkv) * d->T;
@@ -94,6 +94,7 @@ int check_evict(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, int64_
   if (!cache || !cache->scores || !wsum || !slot_log) return H2O_EINVAL;
   if (n_occ < 0 || n_occ > d->C || pos < 0) return H2O_EINVAL;
   if (cache->token_pos && pos + d->T > INT32_MAX) return H2O_EINVAL;
+  if (d->policy == H2O_POLICY_NORM && !cache->token_pos) return H2O_EINVAL;  // ages need positions
   if (!(n_occ + static_cast<int64_t>(d->T) <= d->C || n_occ == d->C)) return H2O_EUNSUPPORTED;
   if (n_occ == d->C && d->T > d->C) return H2O_EUNSUPPORTED;  // cannot evict more than C slots
   if (d->C > 65536) return H2O_EUNSUPPORTED;
@@ -177,6 +178,9 @@ h2o::EvictArgs evict_args(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, in
   e.wsum = wsum;
   e.slot_log = slot_log;
   e.groups = d->B * d->Hkv;
+  e.B = d->B;
+  e.Hkv = d->Hkv;
+  e.policy = d->policy;
   e.C = d->C;
   e.T = d->T;
   e.n_occ = n_occ;

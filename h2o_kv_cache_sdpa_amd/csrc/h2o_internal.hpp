@@ -29,10 +29,11 @@ struct AttnArgs {
 
 struct EvictArgs {
   float *scores;        // (B,Hkv,C)
-  int32_t *token_pos;   // (B,Hkv,C) or null
+  int32_t *token_pos;   // (B,Hkv,C); may be null for the h2o and h2o_orig policies
   const float *wsum;    // (B,Hkv,n_occ+T)
   int32_t *slot_log;    // (B,Hkv,T)
   int groups, C, T, n_occ;
+  int B, Hkv, policy;   // groups = B * Hkv; policy: enum h2o_policy
   long long pos;
 };
 

@@ -66,9 +66,16 @@ enum h2o_cache_fmt {
                            k_scale, v_scale, k_zero, v_zero: fp16 (B,Hkv,C) */
 };
 
-/* Score used to choose the slots to overwrite once the cache is full. */
+/* Score used to choose the slots to overwrite once the cache is full
+ * ("Learning how to Forget", §3.1.1).  The stored scores are the cumulative
+ * summed weights per (b, KV head, slot) under every policy; the policy only
+ * changes the value the slots are ranked by. */
 enum h2o_policy {
-  H2O_POLICY_H2O = 0 /* cumulative summed attention weights per (b, KV head, slot) */
+  H2O_POLICY_H2O = 0,  /* the cumulative score */
+  H2O_POLICY_NORM = 1, /* score / (pos + T - token_pos[slot]): the score averaged over the
+                          queries that have attended the slot; needs token_pos */
+  H2O_POLICY_ORIG = 2  /* score summed over the batch rows (fp32, b ascending); every batch
+                          row selects the same slots */
 };
 
 /* Problem sizes.  B batch, Hq query heads, Hkv KV heads (Hq % Hkv == 0),
@@ -130,11 +137,13 @@ int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ,
  * §3.1: left-to-right fill, B*Hkv*T slots per chunk; §3.2: replay log).
  *   scores[j] += wsum[j] for j < n_occ.
  *   If n_occ + T <= C: slot_log[b,g,t] = n_occ + t.
- *   If n_occ == C:     slot_log[b,g,:] = the T slots with the smallest updated
- *                      score under (score, slot index), in ascending slot order.
+ *   If n_occ == C:     slot_log[b,g,:] = the T slots with the smallest ranking
+ *                      value (enum h2o_policy) under (value, slot index), in
+ *                      ascending slot order.
  *   Then for each t: scores[slot_log[t]] = wsum[n_occ+t] and, if token_pos is
  *   not NULL, token_pos[slot_log[t]] = pos + t.  K/V buffers are not touched.
- *   n_occ < C < n_occ + T, or T > C when n_occ == C, returns H2O_EUNSUPPORTED.
+ *   n_occ < C < n_occ + T, or T > C when n_occ == C, returns H2O_EUNSUPPORTED;
+ *   H2O_POLICY_NORM without token_pos returns H2O_EINVAL.
  *   C must be <= 65536.
  *   slot_log: int32 (B,Hkv,T). */
 int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,

@@ -106,6 +106,9 @@ def test_evict_validation():
     assert ev(d, 0, pos=2**31 - 10) == api.H2O_EINVAL  # token_pos would overflow int32
     big = api.make_dims(1, 8, 2, 128, 70000, 64)
     assert ev(big, 70000) == api.H2O_EUNSUPPORTED
+    norm = api.make_dims(1, 8, 2, 128, 256, 64, policy="h2o_norm")
+    assert ev(norm, 256, cache=_cache(token_pos=None)) == api.H2O_EINVAL  # ages need positions
+    assert ev(api.make_dims(1, 8, 2, 128, 256, 64, policy=3), 256) == api.H2O_EUNSUPPORTED
 
 
 def test_write_validation():

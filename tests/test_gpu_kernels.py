@@ -139,9 +139,9 @@ def test_sdpa_zero_queries_closed_form():
 # eviction
 # ---------------------------------------------------------------------------
 
-def _run_evict(scores, w, n_occ, T, pos=1000, token_pos=True):
+def _run_evict(scores, w, n_occ, T, pos=1000, token_pos=True, policy="h2o"):
     B, H, C = scores.shape
-    dims = api.make_dims(B, 8 * H, H, 128, C, T)
+    dims = api.make_dims(B, 8 * H, H, 128, C, T, policy=policy)
     sc = torch.from_numpy(scores.copy()).to(DEV)
     tp = torch.from_numpy(np.arange(B * H * C, dtype=np.int32).reshape(B, H, C) % 977).to(DEV) if token_pos else None
     wd = torch.from_numpy(w).to(DEV)
@@ -197,6 +197,45 @@ def test_evict_parity(case):
             kept[b, g, slots[b, g]] = False
     kept[..., n_occ:] = False
     check_rel(sc[kept], phi_upd[kept], T, 1, "scores")
+
+
+POLICY_CASES = [
+    # B, H, C, T, n_occ
+    (1, 2, 1000, 100, 1000),
+    (4, 8, 32768, 1024, 32768),  # the int4 batch workload's shape
+    (3, 2, 4096, 512, 4096),
+    (2, 2, 512, 64, 128),        # filling: the same under every policy
+    (2, 1, 300, 300, 300),       # T == C
+]
+
+
+@pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
+@pytest.mark.parametrize("case", POLICY_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_evict_policy_parity(case, policy):
+    B, H, C, T, n_occ = case
+    print(f"evict {policy} case {case}", flush=True)
+    rng = np.random.default_rng([42, B, H, C, T])
+    scores = np.zeros((B, H, C), np.float32)
+    scores[..., :n_occ] = rng.uniform(0, 50, (B, H, n_occ)).astype(np.float32)
+    w = rng.exponential(0.3, (B, H, n_occ + T)).astype(np.float32)
+    pos = 5000
+    tp0 = np.arange(B * H * C, dtype=np.int32).reshape(B, H, C) % 977
+    sc, tp, slots = _run_evict(scores, w, n_occ, T, pos, policy=policy)
+    phi_upd = O.update_scores(scores.astype(np.float64), w.astype(np.float64), n_occ, C, T)
+    key = O.selection_key(phi_upd, tp0, pos, T, policy) if n_occ == C else phi_upd
+    ref = O.bottom_t(key, n_occ, C, T)
+    check_selection(slots, ref, key, n_occ, C, T)
+    if policy == "h2o_orig":
+        assert (slots == slots[:1]).all(), "batch rows selected different slots"
+    expect = scores.copy()
+    expect[..., :n_occ] = scores[..., :n_occ] + w[..., :n_occ]
+    tp_exp = tp0.copy()
+    for b in range(B):
+        for g in range(H):
+            expect[b, g, slots[b, g]] = w[b, g, n_occ:]
+            tp_exp[b, g, slots[b, g]] = pos + np.arange(T)
+    np.testing.assert_array_equal(sc, expect)
+    np.testing.assert_array_equal(tp, tp_exp)
 
 
 def test_evict_ties_resolve_to_lower_index():

@@ -67,9 +67,10 @@ def _check_state(gc: H2OCache, oc: O.OracleCache, T, qg):
     check_rel(gc.scores.cpu().numpy()[:, :, :n], oc.phi[:, :, :n], T, qg, "scores")
 
 
-def _run_stream(w: W.Workload, steps=None):
-    gc = H2OCache(w.B, w.Hq, w.Hkv, w.D, w.C, w.T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=DEV)
-    oc = O.OracleCache(w.B, w.Hq, w.Hkv, w.D, w.C, fmt=w.cache_fmt)
+def _run_stream(w: W.Workload, steps=None, policy="h2o"):
+    gc = H2OCache(w.B, w.Hq, w.Hkv, w.D, w.C, w.T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=DEV,
+                  policy=policy)
+    oc = O.OracleCache(w.B, w.Hq, w.Hkv, w.D, w.C, fmt=w.cache_fmt, policy=policy)
     if w.start_full:
         k, v, scores, tp, n = W.prefilled_cache(w)
         oc.k[:], oc.v[:] = k.f64, v.f64
@@ -87,7 +88,7 @@ def _run_stream(w: W.Workload, steps=None):
         torch.cuda.synchronize()
         err = check_out(out, ref["out"], w.dtype, f"step {step} out")
         werr = check_rel(wsum.cpu().numpy(), ref["w"], w.T, w.qg, f"step {step} wsum")
-        differ = check_selection(slots.cpu().numpy(), ref["slots"], ref["phi_updated"], n_occ, w.C, w.T)
+        differ = check_selection(slots.cpu().numpy(), ref["slots"], ref["rank_key"], n_occ, w.C, w.T)
         print(f"{w.name} step {step} n_occ {n_occ}: out err {err:.2e} wsum rel {werr:.2e} "
               f"in-band differ {differ}", flush=True)
         if differ:
@@ -116,6 +117,18 @@ def test_stream_cfg4_int8_reduced():
 
 def test_stream_cfg5_int4_reduced():
     _run_stream(W.WORKLOADS[5].scaled(C=1024, T=32, n_fill=32, n_evict=10))
+
+
+@pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
+def test_stream_policies_bf16_batch(policy):
+    """The long bf16 stream's structure with B = 2 under the other two
+    ranking policies ([LF] §3.1.1)."""
+    _run_stream(W.WORKLOADS[3].scaled(B=2, C=1024, T=64, n_fill=16, n_evict=10), policy=policy)
+
+
+@pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
+def test_stream_policies_int4_batch(policy):
+    _run_stream(W.WORKLOADS[5].scaled(C=512, T=32, n_fill=16, n_evict=8), policy=policy)
 
 
 # ---------------------------------------------------------------------------
