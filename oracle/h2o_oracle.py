@@ -351,3 +351,26 @@ class OracleCache:
         self.n_occ = min(n_occ + T, C)
         self.pos += T
         return dict(out=out, w=w, lse=lse, slots=slots, phi_updated=phi_upd, rank_key=key)
+
+    def replay_step(self, q, k_new, v_new, slots):
+        """Replay a logged decision ([LF] §3.2: replay caches act like normal
+        caches but take their eviction decisions from the log): attend as in
+        step(), write the chunk into the logged slots (quantising for 8/4-bit
+        caches) and set their token positions.  No score is computed or kept.
+
+        slots: integer array (B, Hkv, T), one replay-log row per (b, g).
+        Returns out.
+        """
+        T = q.shape[2]
+        C, n_occ = self.C, self.n_occ
+        if not (n_occ + T <= C or n_occ == C):
+            raise ValueError("chunk straddles capacity")
+        out, _, _ = attend_chunk(q, self.k, self.v, n_occ, k_new, v_new, self.scale)
+        for b in range(self.B):
+            for g in range(self.Hkv):
+                r = np.asarray(slots[b, g], dtype=np.int64)
+                self._write_rows(b, g, r, k_new[b, g], v_new[b, g])
+                self.token_pos[b, g, r] = self.pos + np.arange(T)
+        self.n_occ = min(n_occ + T, C)
+        self.pos += T
+        return out

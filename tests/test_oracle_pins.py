@@ -418,3 +418,45 @@ def test_norm_divides_by_queries_seen():
             np.testing.assert_allclose(r["rank_key"] * seen, r["phi_updated"], rtol=1e-13)
             # each query spreads q_g = Hq/Hkv units of weight, so the average is at most q_g
             assert (r["rank_key"] <= Hq // Hkv + 1e-12).all()
+
+
+# ---------------------------------------------------------------------------
+# replay of a logged decision
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["native", "int4"])
+def test_replay_reproduces_recorded_stream(fmt):
+    """Replaying the log of a recorded stream on a fresh cache gives the same
+    outputs and the same cache contents and positions ([LF] §3.2); scores are
+    not kept by the replay."""
+    B, Hq, Hkv, D, C, T = 2, 4, 2, 8, 16, 4
+    rec = O.OracleCache(B, Hq, Hkv, D, C, fmt=fmt)
+    rep = O.OracleCache(B, Hq, Hkv, D, C, fmt=fmt)
+    for step in range(10):
+        ch = W.random_chunk([11, step], B, Hq, Hkv, T, D, "f32", hh_frac=0.25)
+        q, kn, vn = ch["q"].f64, ch["k"].f64, ch["v"].f64
+        r = rec.step(q, kn, vn)
+        out = rep.replay_step(q, kn, vn, r["slots"])
+        np.testing.assert_array_equal(out, r["out"])
+        np.testing.assert_array_equal(rep.k, rec.k)
+        np.testing.assert_array_equal(rep.v, rec.v)
+        np.testing.assert_array_equal(rep.token_pos, rec.token_pos)
+    assert (rep.phi == 0).all()
+    assert rep.n_occ == rec.n_occ and rep.pos == rec.pos
+
+
+def test_replay_of_another_log_changes_only_the_named_slots():
+    B, Hq, Hkv, D, C, T = 1, 2, 1, 4, 8, 2
+    oc = O.OracleCache(B, Hq, Hkv, D, C)
+    for step in range(4):  # fill
+        ch = W.random_chunk([12, step], B, Hq, Hkv, T, D, "f32")
+        oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+    k0, tp0 = oc.k.copy(), oc.token_pos.copy()
+    ch = W.random_chunk([12, 9], B, Hq, Hkv, T, D, "f32")
+    oc.replay_step(ch["q"].f64, ch["k"].f64, ch["v"].f64, np.array([[[6, 1]]]))
+    changed = np.flatnonzero((oc.k[0, 0] != k0[0, 0]).any(axis=-1))
+    assert changed.tolist() == [1, 6]
+    np.testing.assert_array_equal(oc.k[0, 0, 6], ch["k"].f64[0, 0, 0])  # token 0 -> slot 6
+    np.testing.assert_array_equal(oc.k[0, 0, 1], ch["k"].f64[0, 0, 1])
+    assert oc.token_pos[0, 0, 6] == 8 and oc.token_pos[0, 0, 1] == 9
+    assert (np.delete(oc.token_pos[0, 0], [1, 6]) == np.delete(tp0[0, 0], [1, 6])).all()
