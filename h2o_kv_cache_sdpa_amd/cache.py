@@ -73,3 +73,14 @@ class H2OCache:
         self.n_occ = min(self.n_occ + self.T, self.C)
         self.pos += self.T
         return out, wsum, slot_log
+
+    def replay_step(self, q, k_new, v_new, slot_log, out=None, stream=None):
+        """Attend and overwrite the slots of a logged decision (no scoring);
+        returns out."""
+        if out is None:
+            out = self.new_outputs()[0]
+        api.h2o_replay_step(self.dims, self.bufs(), self.n_occ, self.pos, q, k_new, v_new, out,
+                            slot_log, self.ws, stream)
+        self.n_occ = min(self.n_occ + self.T, self.C)
+        self.pos += self.T
+        return out

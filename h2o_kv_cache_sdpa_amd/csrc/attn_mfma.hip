@@ -649,7 +649,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(ka, dim3(nA), dim3(256), lds_a, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.wsum) return e;
   const int nB = groups * ((a.n_occ + a.T + B_KEYS - 1) / B_KEYS);
   {
     KernelTimer timer(H2O_K_ATTN_B, s);

@@ -592,7 +592,7 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(attn_a_native, dim3(nA), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.wsum) return e;
   const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
   {
     KernelTimer timer(H2O_K_ATTN_B, s);

@@ -200,7 +200,7 @@ hipError_t launch_simple_t(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL((attn_a_simple<DT, FMT, D>), ga, dim3(ROWS_A), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || !a.wsum) return e;
   const int n_keys = a.n_occ + a.T;
   dim3 gb((n_keys + KEYS_B - 1) / KEYS_B, groups);
   {

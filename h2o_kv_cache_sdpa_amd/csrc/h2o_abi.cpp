@@ -71,13 +71,13 @@ int from_hip(hipError_t e) {
 
 int check_sdpa(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
                const void *k_new, const void *v_new, const void *out, const float *wsum,
-               const float *lse, const void *ws, size_t ws_bytes) {
+               const float *lse, const void *ws, size_t ws_bytes, bool need_wsum = true) {
   int st = check_dims(d);
   if (st != H2O_OK) return st;
   if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
-  if (!q || !k_new || !v_new || !out || !wsum) return H2O_EINVAL;
+  if (!q || !k_new || !v_new || !out || (need_wsum && !wsum)) return H2O_EINVAL;
   if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out) ||
-      !aligned16(wsum) || (lse && !aligned16(lse)))
+      (wsum && !aligned16(wsum)) || (lse && !aligned16(lse)))
     return H2O_EINVAL;
   if (n_occ > 0) {
     st = check_cache_buffers(d, cache);
@@ -167,6 +167,8 @@ h2o::KvWriteArgs write_args(const h2o_dims *d, h2o_cache *cache, const void *k_n
   w.D = d->D;
   w.dtype = d->dtype;
   w.cache_fmt = d->cache_fmt;
+  w.token_pos = nullptr;
+  w.pos = 0;
   return w;
 }
 
@@ -283,6 +285,24 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
   st = from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, w, slot_log), s));
   if (st != H2O_OK) return st;
   return from_hip(h2o::launch_kv_write(write_args(d, cache, k_new, v_new, slot_log), s));
+}
+
+int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,
+                    const void *k_new, const void *v_new, void *out, const int32_t *slot_log, void *ws,
+                    size_t ws_bytes, void *stream) {
+  int st = check_sdpa(d, cache, n_occ, q, k_new, v_new, out, nullptr, nullptr, ws, ws_bytes, false);
+  if (st != H2O_OK) return st;
+  if (!(n_occ + static_cast<int64_t>(d->T) <= d->C || n_occ == d->C)) return H2O_EUNSUPPORTED;
+  if (pos < 0 || (cache && cache->token_pos && pos + d->T > INT32_MAX)) return H2O_EINVAL;
+  st = check_write(d, cache, k_new, v_new, slot_log);
+  if (st != H2O_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = launch_sdpa(attn_args(d, cache, n_occ, q, k_new, v_new, out, nullptr, nullptr, ws), s);
+  if (st != H2O_OK) return st;
+  h2o::KvWriteArgs w = write_args(d, cache, k_new, v_new, slot_log);
+  w.token_pos = cache->token_pos;
+  w.pos = pos;
+  return from_hip(h2o::launch_kv_write(w, s));
 }
 
 }  // extern "C"

@@ -19,7 +19,7 @@ struct AttnArgs {
   const void *kc, *vc;
   const uint16_t *ks, *vs, *kz, *vz;  // fp16 scale / zero bit patterns (B,Hkv,C)
   void *out;
-  float *wsum;
+  float *wsum;     // null: output only (pass B is skipped)
   float *lse2;     // workspace: m + log2(l) with logits measured in units of log2
   float *lse_nat;  // optional natural-log copy for the caller (may be null)
   int B, Hq, Hkv, D, C, T, qg, n_occ;
@@ -42,6 +42,8 @@ struct KvWriteArgs {
   uint16_t *ks, *vs, *kz, *vz;
   const void *kn, *vn;
   const int32_t *slot_log;
+  int32_t *token_pos;  // when set, token_pos[slot_log[t]] = pos + t (replay)
+  long long pos;
   int groups, C, T, D;
   int dtype, cache_fmt;
 };

@@ -29,6 +29,8 @@ __global__ __launch_bounds__(256) void scatter_native(KvWriteArgs a, int row_byt
   const int grp = static_cast<int>(r / a.T);
   const int slot = a.slot_log[r];
   if (slot < 0 || slot >= a.C) return;  // caller-supplied log: never write outside the cache
+  if (a.token_pos && chunk == 0 && isv == 0)
+    a.token_pos[static_cast<size_t>(grp) * a.C + slot] = static_cast<int32_t>(a.pos + static_cast<int>(r % a.T));
   const char *src = static_cast<const char *>(isv ? a.vn : a.kn) + r * row_bytes + chunk * 16;
   char *dst = static_cast<char *>(isv ? a.vc : a.kc) +
               (static_cast<size_t>(grp) * a.C + slot) * row_bytes + chunk * 16;
@@ -60,6 +62,7 @@ __global__ __launch_bounds__(256) void quant_pack(KvWriteArgs a) {
   const int slot = a.slot_log[rr];
   if (slot < 0 || slot >= a.C) return;  // wave-uniform: one row per wavefront
   const size_t dst_row = static_cast<size_t>(grp) * a.C + slot;
+  if (a.token_pos && !isv && lane == 0) a.token_pos[dst_row] = static_cast<int32_t>(a.pos + static_cast<int>(rr % a.T));
   const void *src = isv ? a.vn : a.kn;
   const bool has = 2 * lane < a.D;
   const float x0 = has ? load_elem<DT>(src, rr * a.D + 2 * lane) : 0.f;

@@ -183,6 +183,22 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
                    void *out, float *wsum, int32_t *slot_log,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* Replay step ("Learning how to Forget", §3.2: replay caches act like normal
+ * KV caches except that eviction decisions are replayed from the log): the
+ * attention of h2o_sdpa_scoresum without the summed weights (no scoring, no
+ * selection), then the chunk's keys and values are written (quantised for
+ * INT8/INT4) into the slots of a logged decision, and token_pos (if not NULL)
+ * is set to pos + t for slot_log[b,g,t].  Scores are left untouched.
+ *   slot_log  int32 (B,Hkv,T): a row of the replay log, e.g. as written by
+ *             h2o_evict_topk / h2o_chunk_step for the same step; entries
+ *             outside [0, C) are skipped.
+ *   out       (B,Hq,T,D) dtype.  ws: at least h2o_workspace_bytes(d) bytes.
+ *   n_occ, pos and the return codes are as for h2o_chunk_step; after the call
+ *   the caller's occupancy is min(n_occ + T, C) and its position pos + T. */
+int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                    const void *q, const void *k_new, const void *v_new, void *out,
+                    const int32_t *slot_log, void *ws, size_t ws_bytes, void *stream);
+
 /* Kernel timing, for measurement.  While enabled, every kernel the library
  * launches is bracketed by two hipEvents recorded on the caller's stream (the
  * events come from a pool the library owns; no device memory is allocated).

@@ -131,6 +131,36 @@ def test_stream_policies_int4_batch(policy):
     _run_stream(W.WORKLOADS[5].scaled(C=512, T=32, n_fill=16, n_evict=8), policy=policy)
 
 
+def _replay_stream(w: W.Workload, steps):
+    """Record the oracle's replay log on a stream, then replay it on the GPU
+    (h2o_replay_step) beside the oracle's replay: outputs to tolerance, cache
+    contents and positions bit for bit, scores untouched."""
+    rec = O.OracleCache(w.B, w.Hq, w.Hkv, w.D, w.C, fmt=w.cache_fmt)
+    oc = O.OracleCache(w.B, w.Hq, w.Hkv, w.D, w.C, fmt=w.cache_fmt)
+    gc = H2OCache(w.B, w.Hq, w.Hkv, w.D, w.C, w.T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=DEV)
+    gc.scores.fill_(7.0)
+    for step in range(steps):
+        ch = W.chunk(w, step)
+        q, kn, vn = ch["q"].f64, ch["k"].f64, ch["v"].f64
+        log = rec.step(q, kn, vn)["slots"]
+        ref = oc.replay_step(q, kn, vn, log)
+        out = gc.replay_step(to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"]),
+                             torch.from_numpy(log.astype(np.int32)).to(DEV))
+        torch.cuda.synchronize()
+        err = check_out(out, ref, w.dtype, f"replay step {step} out")
+        print(f"{w.name} replay step {step}: out err {err:.2e}", flush=True)
+        oc.phi[:] = 7.0  # the replay keeps no scores; compare the rest of the state
+        _check_state(gc, oc, w.T, w.qg)
+    assert (gc.scores == 7.0).all()
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4, 5])
+def test_replay_stream(cfg):
+    sizes = {1: {}, 3: dict(C=512, T=64), 4: dict(C=512, T=64), 5: dict(C=256, T=32)}[cfg]
+    w = W.WORKLOADS[cfg].scaled(**sizes)
+    _replay_stream(w, steps=min(w.steps, (w.C // w.T) + 6))
+
+
 # ---------------------------------------------------------------------------
 # one evicting step at full size, checked on whole KV groups
 # ---------------------------------------------------------------------------
