@@ -29,7 +29,7 @@ EXPORTS = (
     "kv_dequant_unpack", "h2o_chunk_step", "h2o_replay_step", "h2o_profile_enable", "h2o_profile_read",
     "h2o_profile_reset",
 )
-KERNEL_KINDS = ("attn_a", "attn_b", "evict", "kv_write")
+KERNEL_KINDS = ("attn_a", "attn_b", "evict", "kv_write", "attn_combine")
 
 
 class H2ODims(ctypes.Structure):

@@ -30,6 +30,7 @@
 // compile time (loops are unrolled by the buffer parity), so the compiler can
 // tell an in-flight DMA target from the buffer being read.
 
+#include <algorithm>
 #include <type_traits>
 
 #include "device_util.hpp"
@@ -131,7 +132,9 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   const int n = lane & 31, hl = lane >> 5;
   const int R = a.qg * a.T;
   const int tiles_per_grp = (R + 127) / 128;
-  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = wi_all % a.nsplit;  // key split of this block (0 when unsplit)
+  const int wi = wi_all / a.nsplit;
   const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
   const int row0 = rt * 128;
@@ -160,7 +163,11 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
 
   const int last_row = min(R, row0 + 128) - 1;
   const int key_end = n_occ + last_row / a.qg + 1;
-  const int ntiles = (key_end + 63) / 64;
+  // key tiles t_lo .. t_lo + ntiles - 1 of the block's range (all of it when unsplit)
+  const int ntiles_all = (key_end + 63) / 64;
+  const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
+  const int t_lo = split * per_split;
+  const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;  // <= 0: empty split
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
 
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
     return static_cast<uint32_t>(row * ROW_BYTES + 16 * c);
   };
   auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs, bool is_v) {
-    const int j0 = tile * 64;
+    const int j0 = (t_lo + tile) * 64;
     if (j0 + 64 <= n_occ) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
@@ -226,7 +233,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   // interleaved with the exponentials of tile t, and O^T += V(t)^T P(t)^T.
   auto tile_step = [&](int t, f32x16 c0, f32x16 c1, const char *kb_next, f32x16 &n0, f32x16 &n1,
                        const char *vb) {
-    const int j0 = t * 64;
+    const int j0 = (t_lo + t) * 64;
     if (wave_ragged || j0 + 63 - n_occ > wave_i_min) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -317,12 +324,14 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   };
 
   // ---- pipeline: K tiles one step ahead of V tiles, two LDS buffers each ----
-  issue_k(0, kb0);
-  issue_v(0, vb0);
-  if (ntiles > 1) issue_k(1, kb1);
-  wait_dma_and_sync();
+  if (ntiles > 0) {
+    issue_k(0, kb0);
+    issue_v(0, vb0);
+    if (ntiles > 1) issue_k(1, kb1);
+    wait_dma_and_sync();
+  }
   f32x16 sa0, sa1, sb0, sb1;  // S of the even / odd tile
-  s_only(kb0, sa0, sa1);
+  if (ntiles > 0) s_only(kb0, sa0, sa1);
 
   for (int t = 0; t < ntiles; t += 2) {
     // even tile t: K(t+1) in kb1, V(t) in vb0 (for the last tile, kb1 is stale
@@ -341,9 +350,24 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!row_ok) return;
+  const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
+  if (a.nsplit > 1) {  // unnormalised partial output and (m, l) of this key split
+    const size_t pr = static_cast<size_t>(split) * a.B * a.Hq * a.T + li;
+    float *po = a.part + pr * D;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * blk + 8 * a4 + 4 * hl;
+        *reinterpret_cast<float4 *>(po + d) =
+            make_float4(o[blk][4 * a4], o[blk][4 * a4 + 1], o[blk][4 * a4 + 2], o[blk][4 * a4 + 3]);
+      }
+    }
+    if (hl == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * pr) = make_float2(m_run, l_tot);
+    return;
+  }
   const float inv = 1.f / l_tot;
-  uint16_t *orow =
-      static_cast<uint16_t *>(a.out) + ((static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q) * D;
+  uint16_t *orow = static_cast<uint16_t *>(a.out) + li * D;
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
 #pragma unroll
@@ -356,9 +380,44 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   }
   if (hl == 0) {
     const float L = m_run + log2f(l_tot);
-    const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
     a.lse2[li] = L;
     if (a.lse_nat) a.lse_nat[li] = L * 0.69314718055994530942f;
+  }
+}
+
+// Merge of the key splits of pass A: per row, M = max_s m_s,
+// l = sum_s l_s 2^(m_s - M), out = sum_s 2^(m_s - M) O_s / l, L = M + log2 l
+// (the same rescaling the online softmax applies between tiles), in fixed
+// split order.  Eight rows per block, 32 lanes x 4 components per row.
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+  const size_t row = static_cast<size_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int c = threadIdx.x & 31;
+  if (row >= rows) return;
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, a.part_ml[2 * (sp * rows + row)]);
+  float l = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sp = 0; sp < a.nsplit; ++sp) {
+    const size_t pr = sp * rows + row;
+    const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
+    if (ms == -INFINITY) continue;  // no visible key in this split
+    const float wgt = __builtin_amdgcn_exp2f(ms - M);
+    l = fmaf(ls, wgt, l);
+    const float4 o = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c);
+    acc.x = fmaf(o.x, wgt, acc.x);
+    acc.y = fmaf(o.y, wgt, acc.y);
+    acc.z = fmaf(o.z, wgt, acc.z);
+    acc.w = fmaf(o.w, wgt, acc.w);
+  }
+  const float inv = 1.f / l;
+  uint16_t *orow = static_cast<uint16_t *>(a.out) + row * D;
+  *reinterpret_cast<uint2 *>(orow + 4 * c) =
+      make_uint2(pack_bf16_rne(acc.x * inv, acc.y * inv), pack_bf16_rne(acc.z * inv, acc.w * inv));
+  if (c == 0) {
+    const float L = M + log2f(l);
+    a.lse2[row] = L;
+    if (a.lse_nat) a.lse_nat[row] = L * 0.69314718055994530942f;
   }
 }
 
@@ -583,16 +642,41 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
 
 }  // namespace
 
+int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int cache_fmt) {
+  if (dtype != DT_BF16 || cache_fmt != FMT_NATIVE || D != 128) return 1;
+  // 2 blocks of pass A per CU on 256 CUs; split the keys of each row block
+  // until the grid fills them, keeping at least 4 key tiles per split.
+  constexpr int kSlots = 512;
+  const long long blocks = static_cast<long long>(B) * Hkv * (((Hq / Hkv) * T + 127) / 128);
+  const int tiles = (n_occ + T + 63) / 64;
+  int ns = static_cast<int>((kSlots + blocks - 1) / blocks);
+  ns = std::min(ns, std::max(1, tiles / 4));
+  return std::max(1, std::min(ns, 64));
+}
+
+size_t attn_split_floats(int B, int Hq, int D, int T, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return static_cast<size_t>(nsplit) * B * Hq * T * (D + 2);
+}
+
 hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
   const int R = a.qg * a.T;
-  const int nA = groups * ((R + 127) / 128);
+  const int nA = groups * ((R + 127) / 128) * a.nsplit;
   {
     KernelTimer timer(H2O_K_ATTN_A, s);
     hipLaunchKernelGGL(attn_a_native, dim3(nA), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.wsum) return e;
+  if (e != hipSuccess) return e;
+  if (a.nsplit > 1) {
+    const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+    KernelTimer timer(H2O_K_ATTN_COMBINE, s);
+    hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!a.wsum) return hipSuccess;
   const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
   {
     KernelTimer timer(H2O_K_ATTN_B, s);

@@ -45,6 +45,12 @@ size_t lse_bytes(const h2o_dims *d) {
   return align_up(2 * sizeof(float) * static_cast<size_t>(d->B) * d->Hq * d->T);
 }
 
+// Partial outputs of a key-split pass A (zero when the step is not split).
+size_t split_bytes(const h2o_dims *d, int n_occ) {
+  const int ns = h2o::attn_splits(d->B, d->Hq, d->Hkv, d->D, d->T, n_occ, d->dtype, d->cache_fmt);
+  return align_up(sizeof(float) * h2o::attn_split_floats(d->B, d->Hq, d->D, d->T, ns));
+}
+
 size_t wsum_bytes(const h2o_dims *d, int n_occ) {
   return align_up(sizeof(float) * static_cast<size_t>(d->B) * d->Hkv * (n_occ + d->T));
 }
@@ -83,7 +89,7 @@ int check_sdpa(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const v
     st = check_cache_buffers(d, cache);
     if (st != H2O_OK) return st;
   }
-  if (!ws || !aligned16(ws) || ws_bytes < lse_bytes(d)) return H2O_EWORKSPACE;
+  if (!ws || !aligned16(ws) || ws_bytes < lse_bytes(d) + split_bytes(d, n_occ)) return H2O_EWORKSPACE;
   return H2O_OK;
 }
 
@@ -129,6 +135,9 @@ h2o::AttnArgs attn_args(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ
   a.wsum = wsum;
   a.lse2 = static_cast<float *>(ws);
   a.lse_nat = lse;
+  a.nsplit = h2o::attn_splits(d->B, d->Hq, d->Hkv, d->D, d->T, n_occ, d->dtype, d->cache_fmt);
+  a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d));
+  a.part_ml = a.part + static_cast<size_t>(a.nsplit) * d->B * d->Hq * d->T * d->D;
   a.B = d->B;
   a.Hq = d->Hq;
   a.Hkv = d->Hkv;
@@ -211,7 +220,7 @@ int h2o_last_hip_error(void) { return g_last_hip_error; }
 
 size_t h2o_workspace_bytes(const h2o_dims *d) {
   if (check_dims(d) != H2O_OK) return 0;
-  return lse_bytes(d) + wsum_bytes(d, d->C);
+  return lse_bytes(d) + split_bytes(d, d->C) + wsum_bytes(d, d->C);
 }
 
 int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
@@ -269,9 +278,10 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
   int st = check_dims(d);
   if (st != H2O_OK) return st;
   if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
-  const size_t need = lse_bytes(d) + (wsum ? 0 : wsum_bytes(d, n_occ));
+  const size_t need = lse_bytes(d) + split_bytes(d, n_occ) + (wsum ? 0 : wsum_bytes(d, n_occ));
   if (!ws || !aligned16(ws) || ws_bytes < need) return H2O_EWORKSPACE;
-  float *w = wsum ? wsum : reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d));
+  float *w = wsum ? wsum
+                  : reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d) + split_bytes(d, n_occ));
   st = check_sdpa(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws, ws_bytes);
   if (st != H2O_OK) return st;
   st = check_evict(d, cache, n_occ, pos, w, slot_log);

@@ -22,6 +22,11 @@ struct AttnArgs {
   float *wsum;     // null: output only (pass B is skipped)
   float *lse2;     // workspace: m + log2(l) with logits measured in units of log2
   float *lse_nat;  // optional natural-log copy for the caller (may be null)
+  // Key-split pass A (nsplit > 1): split s of row r leaves its unnormalised
+  // output in part[(s*B*Hq*T + r)*D ..] and (m, l) in part_ml[2*(s*B*Hq*T + r)];
+  // a combine kernel merges them into out and lse2.
+  float *part, *part_ml;
+  int nsplit;
   int B, Hq, Hkv, D, C, T, qg, n_occ;
   int dtype, cache_fmt;
   float sl2;  // softmax scale * log2(e)
@@ -66,6 +71,10 @@ class KernelTimer {
 hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s);
+// Key splits pass A uses for these sizes (1 unless the row blocks alone
+// cannot fill the chip); the workspace must hold attn_split_floats() floats.
+int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int cache_fmt);
+size_t attn_split_floats(int B, int Hq, int D, int T, int nsplit);
 hipError_t launch_evict(const EvictArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_dequant(const KvWriteArgs &a, int n_slots, float *kout, float *vout, hipStream_t s);

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define H2O_ABI_VERSION 1
+#define H2O_ABI_VERSION 2
 
 /* Status codes. */
 enum h2o_status {
@@ -210,7 +210,8 @@ enum h2o_kernel_kind {
   H2O_K_ATTN_B = 1,   /* summed weights */
   H2O_K_EVICT = 2,    /* score update, selection, replay log */
   H2O_K_KV_WRITE = 3, /* slot overwrite / quantise */
-  H2O_K_COUNT = 4
+  H2O_K_ATTN_COMBINE = 4, /* merge of key-split partial outputs (small chunks) */
+  H2O_K_COUNT = 5
 };
 int h2o_profile_enable(int on);
 int h2o_profile_read(double *total_ms, int64_t *launches, int n);

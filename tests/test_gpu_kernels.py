@@ -62,6 +62,10 @@ SDPA_CASES = [
     ("bf16", "native", 1, 8, 8, 128, 1000, 77, 1000),
     ("bf16", "native", 1, 16, 2, 128, 700, 50, 700),
     ("bf16", "native", 1, 8, 2, 64, 333, 129, 201),
+    ("bf16", "native", 1, 8, 2, 128, 4096, 64, 4096),   # pass A split over 16 key ranges
+    ("bf16", "native", 2, 8, 2, 128, 2048, 16, 2000),   # split, ragged occupancy
+    ("bf16", "native", 1, 32, 8, 128, 8192, 1, 8192),   # one query per head (decode)
+    ("bf16", "native", 1, 8, 2, 128, 700, 3, 0),        # tiny chunk, empty cache
     ("bf16", "int8", 1, 8, 2, 128, 512, 100, 300),
     ("bf16", "int8", 1, 8, 2, 64, 300, 40, 300),
     ("bf16", "int4", 2, 8, 2, 128, 512, 96, 512),
