@@ -141,6 +141,102 @@ def traffic_from(workload, fetch_dir, write_dir):
     print(json.dumps(out, indent=1))
 
 
+def step_bytes(w, n_occ):
+    """Algorithmic HBM bytes of one chunk step: the cache read once plus Q, the
+    chunk's K/V, O, the summed weights, the scores (read and written) and the
+    row normalisers; token positions and the replay log row."""
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+    row = {"native": 2 * D, "int8": D + 2, "int4": D // 2 + 4}[w.cache_fmt]
+    esz = 2 if w.dtype == "bf16" else 4
+    cache = 2 * B * Hkv * n_occ * row
+    qo = 2 * B * Hq * T * D * esz
+    chunk = 2 * B * Hkv * T * D * esz
+    small = B * Hkv * ((n_occ + T) * 4 + 2 * C * 4 + C * 4 + T * 4) + B * Hq * T * 4
+    return cache + qo + chunk + small
+
+
+def _resident_setup(w, policy, dev):
+    """A full cache of workload w with seeded contents and a rotation of
+    chunks, all resident on the device."""
+    import numpy as np
+    import torch
+
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    from h2o_kv_cache_sdpa_amd.cache import H2OCache
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=dev, policy=policy)
+    seed = [w.cfg_id, 777]
+    if w.cache_fmt == "native":
+        k, v, scores, tp, _ = W.random_cache(seed, B, Hkv, C, D, C, w.dtype, hh_frac=0.02)
+        for name, st in (("k", k), ("v", v)):
+            getattr(gc, name).copy_(torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16))
+                                    .view(torch.bfloat16))
+    else:
+        arr = W.random_quant_cache(seed, B, Hkv, C, D, C, w.cache_fmt)
+        scores, tp = arr["scores"], arr["token_pos"]
+        for key, val in arr.items():
+            if key.endswith(("_codes", "_scale", "_zero")):
+                name = key.replace("_codes", "")
+                getattr(gc, name).copy_(torch.from_numpy(val))
+    gc.scores.copy_(torch.from_numpy(scores))
+    gc.token_pos.copy_(torch.from_numpy(tp))
+    gc.n_occ, gc.pos = C, C
+    chunks = []
+    to_dev = lambda st: torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+    for s in range(N_CHUNKS):
+        ch = W.chunk(w, w.n_fill + s)
+        chunks.append((to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"])))
+    return gc, chunks
+
+
+def sweep_small_t(args):
+    """HBM-bound regime: chunk lengths 1..128 on the 32K-slot cache."""
+    import torch
+
+    from h2o_kv_cache_sdpa_amd import api
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    dev = torch.device("cuda:0")
+    base = W.WORKLOADS[3]
+    for fmt in ("native", "int8", "int4"):
+        for T in (1, 16, 64, 128):
+            w = base.scaled(T=T, cache_fmt=fmt, name=f"small_t_{fmt}_32k_t{T}")
+            gc, chunks = _resident_setup(w, "h2o", dev)
+            out, wsum, slot_log = gc.new_outputs(w.C)
+            bufs = gc.bufs()
+            stream = torch.cuda.current_stream()
+            reps = 200
+
+            def step(i):
+                q, kn, vn = chunks[i % N_CHUNKS]
+                api.h2o_chunk_step(gc.dims, bufs, w.C, gc.pos, q, kn, vn, out, wsum, slot_log, gc.ws, stream)
+                gc.pos += T
+
+            for i in range(10):
+                step(i)
+            torch.cuda.synchronize()
+            api.profile_reset()
+            api.profile_enable(True)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                step(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            api.profile_enable(False)
+            prof = api.profile_read()
+            ms = e0.elapsed_time(e1) / reps
+            nbytes = step_bytes(w, w.C)
+            print(json.dumps({
+                "sweep": "small_t", "workload": w.name, "cache_fmt": fmt, "chunk": T, "cache_slots": w.C,
+                "ms_per_step": ms, "tokens_per_s": w.B * T / (ms * 1e-3),
+                "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()},
+            }), flush=True)
+            del gc, chunks, out, wsum, slot_log
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,9 +247,15 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--sweep-small-t", action="store_true",
+                    help="chunk lengths 1, 16, 64, 128 on the 32K-slot cache in bf16, int8 and int4; "
+                         "one JSON line each (HBM-bound regime)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.workload, *args.traffic_from)
+        return
+    if args.sweep_small_t:
+        sweep_small_t(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the chunk step shards "
@@ -176,28 +278,7 @@ def main():
     B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
 
     # ---- resident inputs: a full cache and a rotation of chunks ----
-    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=dev, policy=args.policy)
-    seed = [w.cfg_id, 777]
-    if w.cache_fmt == "native":
-        k, v, scores, tp, _ = W.random_cache(seed, B, Hkv, C, D, C, w.dtype, hh_frac=0.02)
-        for name, st in (("k", k), ("v", v)):
-            getattr(gc, name).copy_(torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16))
-                                    .view(torch.bfloat16))
-    else:
-        arr = W.random_quant_cache(seed, B, Hkv, C, D, C, w.cache_fmt)
-        scores, tp = arr["scores"], arr["token_pos"]
-        for key, val in arr.items():
-            if key.endswith(("_codes", "_scale", "_zero")):
-                name = key.replace("_codes", "")
-                getattr(gc, name).copy_(torch.from_numpy(val))
-    gc.scores.copy_(torch.from_numpy(scores))
-    gc.token_pos.copy_(torch.from_numpy(tp))
-    gc.n_occ, gc.pos = C, C
-    chunks = []
-    for s in range(N_CHUNKS):
-        ch = W.chunk(w, w.n_fill + s)
-        to_dev = lambda st: torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).view(torch.bfloat16).to(dev)
-        chunks.append((to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"])))
+    gc, chunks = _resident_setup(w, args.policy, dev)
     out, wsum, slot_log = gc.new_outputs(C)
     bufs = gc.bufs()
     stream = torch.cuda.current_stream()

@@ -133,7 +133,9 @@ __global__ __launch_bounds__(256, 2) void attn_a_mfma(AttnArgs a) {
   const int n = lane & 31, hl = lane >> 5;
   const int R = a.qg * a.T;
   const int tiles_per_grp = (R + A_ROWS - 1) / A_ROWS;
-  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = wi_all % a.nsplit;  // key split of this block (0 when unsplit)
+  const int wi = wi_all / a.nsplit;
   const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
   const int row0 = rt * A_ROWS;
@@ -164,7 +166,11 @@ __global__ __launch_bounds__(256, 2) void attn_a_mfma(AttnArgs a) {
 
   const int last_row = min(R, row0 + A_ROWS) - 1;
   const int key_end = n_occ + last_row / a.qg + 1;  // keys any row of the block can see
-  const int ntiles = (key_end + A_KT - 1) / A_KT;
+  // key tiles t_lo .. t_lo + ntiles - 1 (all of them when unsplit)
+  const int ntiles_all = (key_end + A_KT - 1) / A_KT;
+  const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
+  const int t_lo = split * per_split;
+  const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;  // <= 0: empty split
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
 
@@ -308,12 +314,14 @@ __global__ __launch_bounds__(256, 2) void attn_a_mfma(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f, u_run = 0.f;
   const int prow = perm_key(n);
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  if (ntiles > 0) {
+    load_tile(t_lo * A_KT);
+    store_tile(0);
+    __syncthreads();
+  }
 
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * A_KT;
+    const int j0 = (t_lo + t) * A_KT;
     if (t + 1 < ntiles) load_tile(j0 + A_KT);
     const char *kb = smem + (t & 1) * P::BUF;
     const char *vb = kb + P::KS_BYTES;
@@ -429,9 +437,29 @@ __global__ __launch_bounds__(256, 2) void attn_a_mfma(AttnArgs a) {
   float u_tot = 0.f;
   if constexpr (FMT == FMT_INT4) u_tot = u_run + __shfl_xor(u_run, 32);
   if (!row_ok) return;
+  const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
+  if (a.nsplit > 1) {  // unnormalised partial output and (m, l) of this key split
+    const size_t pr = static_cast<size_t>(split) * a.B * a.Hq * a.T + li;
+    float *po = a.part + pr * D;
+#pragma unroll
+    for (int blk = 0; blk < P::NBLK; ++blk) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d = 32 * blk + 8 * a4 + 4 * hl;
+        *reinterpret_cast<float4 *>(po + d) = make_float4(o[blk][4 * a4] + u_tot, o[blk][4 * a4 + 1] + u_tot,
+                                                          o[blk][4 * a4 + 2] + u_tot, o[blk][4 * a4 + 3] + u_tot);
+      }
+    }
+    if (hl == 0) {
+      *reinterpret_cast<float2 *>(a.part_ml + 2 * pr) = make_float2(m_run, l_tot);
+      if constexpr (FMT == FMT_INT4) {
+        if (split == 0) a.lse2[static_cast<size_t>(a.B) * a.Hq * a.T + li] = qsum;
+      }
+    }
+    return;
+  }
   const float inv = 1.f / l_tot;
-  uint16_t *orow =
-      static_cast<uint16_t *>(a.out) + ((static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q) * D;
+  uint16_t *orow = static_cast<uint16_t *>(a.out) + li * D;
 #pragma unroll
   for (int blk = 0; blk < P::NBLK; ++blk) {
 #pragma unroll
@@ -445,7 +473,6 @@ __global__ __launch_bounds__(256, 2) void attn_a_mfma(AttnArgs a) {
   }
   if (hl == 0) {
     const float L = m_run + log2f(l_tot);
-    const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
     a.lse2[li] = L;
     if (a.lse_nat) a.lse_nat[li] = L * 0.69314718055994530942f;
     if constexpr (FMT == FMT_INT4) a.lse2[static_cast<size_t>(a.B) * a.Hq * a.T + li] = qsum;
@@ -633,7 +660,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   constexpr int lds_b = PassB<D>::LDS;
   const int groups = a.B * a.Hkv;
   const int R = a.qg * a.T;
-  const int nA = groups * ((R + A_ROWS - 1) / A_ROWS);
+  const int nA = groups * ((R + A_ROWS - 1) / A_ROWS) * a.nsplit;
   static const hipError_t attr = [] {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&attn_a_mfma<FMT, D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds_a);
@@ -649,7 +676,12 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(ka, dim3(nA), dim3(256), lds_a, s, a);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.wsum) return e;
+  if (e != hipSuccess) return e;
+  if (a.nsplit > 1) {
+    e = launch_attn_combine(a, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!a.wsum) return hipSuccess;
   const int nB = groups * ((a.n_occ + a.T + B_KEYS - 1) / B_KEYS);
   {
     KernelTimer timer(H2O_K_ATTN_B, s);

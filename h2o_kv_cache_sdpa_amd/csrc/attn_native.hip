@@ -387,28 +387,54 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
 
 // Merge of the key splits of pass A: per row, M = max_s m_s,
 // l = sum_s l_s 2^(m_s - M), out = sum_s 2^(m_s - M) O_s / l, L = M + log2 l
-// (the same rescaling the online softmax applies between tiles), in fixed
-// split order.  Eight rows per block, 32 lanes x 4 components per row.
+// (the same rescaling the online softmax applies between tiles).  A row is
+// served by sg = min(nsplit, 8) groups of 32 lanes (4 components each); group
+// k takes splits k, k + sg, ...; the groups' sums are added in group order, so
+// the result does not depend on timing.  256 threads = 8 / sg rows.
 __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  __shared__ float red_m[8], red_l[8];
+  __shared__ float4 red_o[8][32];
   const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
-  const size_t row = static_cast<size_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
-  const int c = threadIdx.x & 31;
-  if (row >= rows) return;
+  const int ns = a.nsplit;
+  const int sg = ns < 8 ? ns : 8;
+  const int slot = threadIdx.x >> 5, c = threadIdx.x & 31;
+  const int rloc = slot / sg, sl = slot % sg;
+  const size_t row = static_cast<size_t>(blockIdx.x) * (8 / sg) + rloc;
+  const bool ok = rloc < 8 / sg && row < rows;
   float M = -INFINITY;
-  for (int sp = 0; sp < a.nsplit; ++sp) M = fmaxf(M, a.part_ml[2 * (sp * rows + row)]);
+  if (ok)
+    for (int sp = sl; sp < ns; sp += sg) M = fmaxf(M, a.part_ml[2 * (sp * rows + row)]);
+  if (c == 0) red_m[slot] = M;
+  __syncthreads();
+  if (ok)
+    for (int k = 0; k < sg; ++k) M = fmaxf(M, red_m[rloc * sg + k]);
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int sp = 0; sp < a.nsplit; ++sp) {
-    const size_t pr = sp * rows + row;
-    const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
-    if (ms == -INFINITY) continue;  // no visible key in this split
-    const float wgt = __builtin_amdgcn_exp2f(ms - M);
-    l = fmaf(ls, wgt, l);
-    const float4 o = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c);
-    acc.x = fmaf(o.x, wgt, acc.x);
-    acc.y = fmaf(o.y, wgt, acc.y);
-    acc.z = fmaf(o.z, wgt, acc.z);
-    acc.w = fmaf(o.w, wgt, acc.w);
+  if (ok) {
+    for (int sp = sl; sp < ns; sp += sg) {
+      const size_t pr = sp * rows + row;
+      const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
+      if (ms == -INFINITY) continue;  // no visible key in this split
+      const float wgt = __builtin_amdgcn_exp2f(ms - M);
+      l = fmaf(ls, wgt, l);
+      const float4 o = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c);
+      acc.x = fmaf(o.x, wgt, acc.x);
+      acc.y = fmaf(o.y, wgt, acc.y);
+      acc.z = fmaf(o.z, wgt, acc.z);
+      acc.w = fmaf(o.w, wgt, acc.w);
+    }
+  }
+  red_o[slot][c] = acc;
+  if (c == 0) red_l[slot] = l;
+  __syncthreads();
+  if (!ok || sl != 0) return;
+  for (int k = 1; k < sg; ++k) {
+    const float4 o = red_o[slot + k][c];
+    acc.x += o.x;
+    acc.y += o.y;
+    acc.z += o.z;
+    acc.w += o.w;
+    l += red_l[slot + k];
   }
   const float inv = 1.f / l;
   uint16_t *orow = static_cast<uint16_t *>(a.out) + row * D;
@@ -642,8 +668,17 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
 
 }  // namespace
 
+hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s) {
+  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+  const int rpb = 8 / (a.nsplit < 8 ? a.nsplit : 8);  // rows per block
+  KernelTimer timer(H2O_K_ATTN_COMBINE, s);
+  hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((rows + rpb - 1) / rpb)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int cache_fmt) {
-  if (dtype != DT_BF16 || cache_fmt != FMT_NATIVE || D != 128) return 1;
+  (void)cache_fmt;
+  if (dtype != DT_BF16 || D != 128) return 1;
   // 2 blocks of pass A per CU on 256 CUs; split the keys of each row block
   // until the grid fills them, keeping at least 4 key tiles per split.
   constexpr int kSlots = 512;
@@ -670,10 +705,7 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nsplit > 1) {
-    const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
-    KernelTimer timer(H2O_K_ATTN_COMBINE, s);
-    hipLaunchKernelGGL(attn_combine, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, s, a);
-    e = hipGetLastError();
+    e = launch_attn_combine(a, s);
     if (e != hipSuccess) return e;
   }
   if (!a.wsum) return hipSuccess;

@@ -74,6 +74,8 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s);
 // Key splits pass A uses for these sizes (1 unless the row blocks alone
 // cannot fill the chip); the workspace must hold attn_split_floats() floats.
 int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int cache_fmt);
+// Merge of the key-split partials of pass A into out and lse2 (D = 128).
+hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s);
 size_t attn_split_floats(int B, int Hq, int D, int T, int nsplit);
 hipError_t launch_evict(const EvictArgs &a, hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);

@@ -66,6 +66,9 @@ SDPA_CASES = [
     ("bf16", "native", 2, 8, 2, 128, 2048, 16, 2000),   # split, ragged occupancy
     ("bf16", "native", 1, 32, 8, 128, 8192, 1, 8192),   # one query per head (decode)
     ("bf16", "native", 1, 8, 2, 128, 700, 3, 0),        # tiny chunk, empty cache
+    ("bf16", "int8", 1, 8, 2, 128, 4096, 16, 4096),     # quantised pass A split 16 ways
+    ("bf16", "int4", 1, 32, 8, 128, 4096, 1, 4096),     # quantised decode, split
+    ("bf16", "int4", 2, 8, 2, 128, 3000, 40, 2960),     # split, ragged
     ("bf16", "int8", 1, 8, 2, 128, 512, 100, 300),
     ("bf16", "int8", 1, 8, 2, 64, 300, 40, 300),
     ("bf16", "int4", 2, 8, 2, 128, 512, 96, 512),
