@@ -107,7 +107,11 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
   };
 
   if (POL != H2O_POLICY_ORIG && n_occ + T <= C) {  // filling: left to right
-    for (int j = tid; j < n_occ; j += NT) phi[j] = phi[j] + w[j];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int j = tid + k * NT;
+      if (j < n_occ) phi[j] = phi[j] + w[j];
+    }
     for (int t = tid; t < T; t += NT) {
       const int slot = n_occ + t;
       log[t] = slot;
@@ -121,7 +125,18 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
   const int base = tid * ITEMS;
   uint32_t key[ITEMS];
   if constexpr (STAGE) {  // coalesced, staged in LDS
-    for (int j = tid; j < C; j += NT) stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = update(j);
+    // fixed trip count so that all loads of a thread are in flight together
+    float f[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int j = tid + k * NT;
+      f[k] = (j < C) ? update(j) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int j = tid + k * NT;
+      if (j < C) stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = f[k];
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k)
@@ -135,24 +150,63 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
     }
   }
 
+  // Keys relative to the block minimum, so that the first 8-bit digit is
+  // taken from the top of the occupied range (the raw top byte -- sign and
+  // exponent -- takes few values, and counting them serialises on a few bins).
+  {
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      if (base + k < C) {
+        kmin = min(kmin, key[k]);
+        kmax = max(kmax, key[k]);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      kmin = min(kmin, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmin), o)));
+      kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
+    }
+    if (lane == 0) {
+      sh_a[tid >> 6] = kmin;
+      sh_b[tid >> 6] = kmax;
+    }
+    __syncthreads();
+    kmin = sh_a[0];
+    kmax = sh_b[0];
+    for (int wv = 1; wv < NWAVES; ++wv) {
+      kmin = min(kmin, sh_a[wv]);
+      kmax = max(kmax, sh_b[wv]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) key[k] -= kmin;  // padding keys wrap to large values, never active
+    const uint32_t range = kmax - kmin;
+    sh_k = range ? 32 - __builtin_clz(range) : 0;  // significant bits of the range
+  }
+  __syncthreads();
+  const int nbits = static_cast<int>(sh_k);
+  __syncthreads();
+  const int npass = (nbits + 7) / 8;
+
   uint32_t prefix = 0, pmask = 0, need = static_cast<uint32_t>(T);
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  for (int pass = 0; pass < npass; ++pass) {
+    // digit p covers bits [shift, shift + width) counted from the top of the range
+    int shift = nbits - 8 * (pass + 1), width = 8;
+    if (shift < 0) {
+      width += shift;
+      shift = 0;
+    }
+    const uint32_t dmask = (1u << width) - 1u;
     for (int e = tid; e < 256; e += NT) hist[e] = 0;
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
       const bool act = (base + k < C) && ((key[k] & pmask) == prefix);
-      const uint32_t digit = (key[k] >> shift) & 255u;
-      // one LDS increment per distinct digit present in the wavefront
-      uint64_t pending = __ballot(act);
-      while (pending) {
-        const int leader = __builtin_ctzll(pending);
-        const uint32_t ld = __builtin_amdgcn_readlane(digit, leader);
-        const uint64_t same = __ballot(act && digit == ld);
-        if (lane == leader) atomicAdd(&hist[ld], static_cast<uint32_t>(__popcll(same)));
-        pending &= ~same;
-      }
+      const uint32_t digit = (key[k] >> shift) & dmask;
+      // one LDS atomic per key; lanes hitting the same bin are serialised by
+      // the LDS, which costs less than aggregating per distinct digit
+      if (act) atomicAdd(&hist[digit], 1u);
     }
     __syncthreads();
     if (tid < 64) {
@@ -187,7 +241,7 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
     }
     __syncthreads();
     prefix |= sh_sel << shift;
-    pmask |= 255u << shift;
+    pmask |= dmask << shift;
     need = sh_k;
     __syncthreads();
   }
