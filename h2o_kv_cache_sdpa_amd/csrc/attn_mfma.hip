@@ -671,11 +671,16 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   if (attr != hipSuccess) return attr;
   auto ka = attn_a_mfma<FMT, D>;
   auto kb = attn_b_mfma<FMT, D>;
-  {
-    KernelTimer timer(H2O_K_ATTN_A, s);
-    hipLaunchKernelGGL(ka, dim3(nA), dim3(256), lds_a, s, a);
+  hipError_t e;
+  if (FMT != FMT_NATIVE && D == 128) {
+    e = launch_attn_a_quant_d128(a, s);  // DMA-staged codes, widened in LDS
+  } else {
+    {
+      KernelTimer timer(H2O_K_ATTN_A, s);
+      hipLaunchKernelGGL(ka, dim3(nA), dim3(256), lds_a, s, a);
+    }
+    e = hipGetLastError();
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.nsplit > 1) {
     e = launch_attn_combine(a, s);

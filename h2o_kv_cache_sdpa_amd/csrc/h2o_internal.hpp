@@ -71,6 +71,8 @@ class KernelTimer {
 hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s);
+// Pass A alone for int8 / int4 caches, bf16, D = 128.
+hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s);
 // Key splits pass A uses for these sizes (1 unless the row blocks alone
 // cannot fill the chip); the workspace must hold attn_split_floats() floats.
 int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int cache_fmt);
