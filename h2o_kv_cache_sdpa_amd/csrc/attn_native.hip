@@ -389,11 +389,45 @@ constexpr int PB_KEYS = 256;
 constexpr int PB_ROWS = 128;
 constexpr int QBLK_BYTES = PB_ROWS * ROW_BYTES;  // 32 KB
 
+// 8 codes of one key row (int8: 8 bytes, int4: 4 bytes with element 2k in the
+// low nibble of byte k) -> 8 bf16; integers are exact in bf16.
+template <int FMT>
+__device__ __forceinline__ bf16x8 widen8(const char *codes) {
+  uint32_t r[4];
+  if constexpr (FMT == FMT_INT8) {
+    const uint2 c = *reinterpret_cast<const uint2 *>(codes);
+    const uint32_t w[2] = {c.x, c.y};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int32_t x = static_cast<int32_t>(w[h]);
+      const float f0 = static_cast<float>((x << 24) >> 24), f1 = static_cast<float>((x << 16) >> 24);
+      const float f2 = static_cast<float>((x << 8) >> 24), f3 = static_cast<float>(x >> 24);
+      r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+      r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+    }
+  } else {
+    const uint32_t w = *reinterpret_cast<const uint32_t *>(codes);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t byte = (w >> (8 * q)) & 0xffu;
+      const float lo = static_cast<float>(byte & 15u), hi = static_cast<float>(byte >> 4);
+      r[q] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    }
+  }
+  return __builtin_bit_cast(bf16x8, make_uint4(r[0], r[1], r[2], r[3]));
+}
+
+// FMT: cache format.  For 8/4-bit caches the K operands are the widened codes
+// and the per-key factors enter the exponent: x = s_j*sl2*acc (+ z_j*sl2*sum(q_i)) - L_i.
+template <int FMT>
 __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char qb0[QBLK_BYTES];
   __shared__ __attribute__((aligned(1024))) char qb1[QBLK_BYTES];
   __shared__ __attribute__((aligned(512))) float lb0[PB_ROWS];
   __shared__ __attribute__((aligned(512))) float lb1[PB_ROWS];
+  // int4: per-row sum(q) beside the normalisers
+  __shared__ __attribute__((aligned(512))) float sb0[FMT == FMT_INT4 ? PB_ROWS : 1];
+  __shared__ __attribute__((aligned(512))) float sb1[FMT == FMT_INT4 ? PB_ROWS : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hl = lane >> 5;
@@ -413,7 +447,9 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   int key0 = j_base + wave * 64 + n, key1 = key0 + 32;
   const int tnew0 = key0 - n_occ, tnew1 = key1 - n_occ;
   bf16x8 kf0[8], kf1[8];
-  {
+  // per-key factors of the exponent: sl2 * s_k, sl2 * z_k (chunk keys: sl2, 0)
+  float ksl0 = sl2, ksl1 = sl2, kzl0 = 0.f, kzl1 = 0.f;
+  if constexpr (FMT == FMT_NATIVE) {
     const char *src0 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key0 < n_keys ? key0 : 0);
     const char *src1 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key1 < n_keys ? key1 : 0);
 #pragma unroll
@@ -421,6 +457,25 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
       kf0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src0 + 32 * st + 16 * hl));
       kf1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src1 + 32 * st + 16 * hl));
     }
+  } else {
+    constexpr int CROW = (FMT == FMT_INT8) ? D : D / 2;  // code bytes per key
+    auto load_key = [&](int key, bf16x8 (&kf)[8], float &ksl, float &kzl) {
+      const int kk = key < n_keys ? key : 0;
+      if (kk < n_occ) {
+        const char *src = static_cast<const char *>(a.kc) + (cache_row0 + kk) * CROW;
+#pragma unroll
+        for (int st = 0; st < 8; ++st) kf[st] = widen8<FMT>(src + (16 * st + 8 * hl) * CROW / D);
+        ksl = f16_to_f32(a.ks[cache_row0 + kk]) * sl2;
+        if constexpr (FMT == FMT_INT4) kzl = f16_to_f32(a.kz[cache_row0 + kk]) * sl2;
+      } else {
+        const char *src = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, kk);
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+          kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src + 32 * st + 16 * hl));
+      }
+    };
+    load_key(key0, kf0, ksl0, kzl0);
+    load_key(key1, kf1, ksl1, kzl1);
   }
 
   const int row_first = (j_base >= n_occ) ? (j_base - n_occ) * a.qg : 0;
@@ -440,6 +495,9 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
                                     (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg) * a.T * ROW_BYTES,
                                 R * ROW_BYTES);
   const rsrc_t l_rs = make_rsrc(a.lse2 + lse_base + static_cast<size_t>(g) * a.qg * a.T, R * 4);
+  const rsrc_t s_rs = make_rsrc(a.lse2 + static_cast<size_t>(a.B) * a.Hq * a.T + lse_base +
+                                    static_cast<size_t>(g) * a.qg * a.T,
+                                R * 4);
   uint32_t qoff[8];
   uint32_t loff = 0;
   if (rows_split) {
@@ -451,12 +509,17 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     const int rl = (wave & 1) * 64 + lane;
     loff = ((rl % a.qg) * a.T + rl / a.qg) * 4;
   }
-  auto issue_rows = [&](int rb, char *qdst, float *ldst) {
+  // L rows by waves 0-1; for int4 the sum(q) rows by waves 2-3
+  auto issue_rows = [&](int rb, char *qdst, float *ldst, float *sdst) {
     if (rows_split && rb + PB_ROWS <= R) {
       const uint32_t shift = static_cast<uint32_t>(rb / a.qg);
 #pragma unroll
       for (int q = 0; q < 8; ++q) dma16(q_rs, qoff[q], shift * ROW_BYTES, qdst + (wave * 8 + q) * 1024);
-      if (wave < 2) dma4(l_rs, loff, shift * 4, reinterpret_cast<char *>(ldst + wave * 64));
+      if (wave < 2) {
+        dma4(l_rs, loff, shift * 4, reinterpret_cast<char *>(ldst + wave * 64));
+      } else if (FMT == FMT_INT4) {
+        dma4(s_rs, loff, shift * 4, reinterpret_cast<char *>(sdst + (wave - 2) * 64));
+      }
       return;
     }
 #pragma unroll
@@ -468,11 +531,15 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
       const int ii = row / a.qg, hh = row % a.qg;
       dma16(q_rs, (hh * a.T + ii) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, qdst + seg * 1024);
     }
-    if (wave < 2) {
-      int row = rb + wave * 64 + lane;
+    {
+      int row = rb + (wave & 1) * 64 + lane;
       row = row < R ? row : R - 1;
       const int ii = row / a.qg, hh = row % a.qg;
-      dma4(l_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(ldst + wave * 64));
+      if (wave < 2) {
+        dma4(l_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(ldst + wave * 64));
+      } else if (FMT == FMT_INT4) {
+        dma4(s_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(sdst + (wave - 2) * 64));
+      }
     }
   };
 
@@ -501,7 +568,7 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
 
   // One 128-row block: the MFMAs of sub-block k+1 run while the VALU sums
   // the exponentials of sub-block k.  FULL: every row sees every key.
-  auto do_block = [&](auto full_tag, const char *qb, const float *lb, int rb) {
+  auto do_block = [&](auto full_tag, const char *qb, const float *lb, const float *sb, int rb) {
     constexpr bool FULL = decltype(full_tag)::value;
     // Q operand of sub-block sub, step st: sub * 32 rows + (q_lane ^ (st << 5));
     // q_lane is made opaque per block (one v_xor per read, no held addresses).
@@ -509,7 +576,7 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     asm volatile("" : "+v"(qa_l));
     auto qop = [&](int sub, int st) { return lds16(qb + sub * (32 * ROW_BYTES) + (qa_l ^ (st << 5))); };
     f32x16 c0 = f32x16{}, c1 = f32x16{};
-    float Lc[16];
+    float Lc[16], Sc[16];
     bf16x8 qc = qop(0, 0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
@@ -521,6 +588,7 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
     load_l(lb, 0, Lc);
+    if constexpr (FMT == FMT_INT4) load_l(sb, 0, Sc);
 #pragma unroll
     for (int sub = 1; sub <= 4; ++sub) {
       f32x16 n0 = f32x16{}, n1 = f32x16{};
@@ -543,8 +611,17 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int r = 2 * st + h2;
-          float x0 = fmaf(c0[r], sl2, -Lc[r]);
-          float x1 = fmaf(c1[r], sl2, -Lc[r]);
+          float x0, x1;
+          if constexpr (FMT == FMT_NATIVE) {
+            x0 = fmaf(c0[r], sl2, -Lc[r]);
+            x1 = fmaf(c1[r], sl2, -Lc[r]);
+          } else if constexpr (FMT == FMT_INT8) {
+            x0 = fmaf(c0[r], ksl0, -Lc[r]);
+            x1 = fmaf(c1[r], ksl1, -Lc[r]);
+          } else {
+            x0 = fmaf(c0[r], ksl0, fmaf(kzl0, Sc[r], -Lc[r]));
+            x1 = fmaf(c1[r], ksl1, fmaf(kzl1, Sc[r], -Lc[r]));
+          }
           if constexpr (!FULL) {
             const int row = rsub + 8 * (r >> 2) + 4 * hl + (r & 3);
             x0 = (row < R && row >= first_row0) ? x0 : -INFINITY;
@@ -567,28 +644,29 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
         c0 = n0;
         c1 = n1;
         load_l(lb, sub, Lc);
+        if constexpr (FMT == FMT_INT4) load_l(sb, sub, Sc);
       }
     }
   };
-  auto block = [&](const char *qb, const float *lb, int rb) {
+  auto block = [&](const char *qb, const float *lb, const float *sb, int rb) {
     const bool full = (rb + PB_ROWS <= R) && (j_base + PB_KEYS <= n_occ || rb / a.qg >= t_last);
     if (full) {
-      do_block(std::true_type{}, qb, lb, rb);
+      do_block(std::true_type{}, qb, lb, sb, rb);
     } else {
-      do_block(std::false_type{}, qb, lb, rb);
+      do_block(std::false_type{}, qb, lb, sb, rb);
     }
   };
 
-  issue_rows(rb_begin, qb0, lb0);
+  issue_rows(rb_begin, qb0, lb0, sb0);
   for (int it = 0; it < nrb; it += 2) {
     const int rb = rb_begin + it * PB_ROWS;
     wait_dma_and_sync();  // block it in qb0; everybody done with qb1
-    if (it + 1 < nrb) issue_rows(rb + PB_ROWS, qb1, lb1);
-    block(qb0, lb0, rb);
+    if (it + 1 < nrb) issue_rows(rb + PB_ROWS, qb1, lb1, sb1);
+    block(qb0, lb0, sb0, rb);
     if (it + 1 >= nrb) break;
     wait_dma_and_sync();  // block it+1 in qb1; everybody done with qb0
-    if (it + 2 < nrb) issue_rows(rb + 2 * PB_ROWS, qb0, lb0);
-    block(qb1, lb1, rb + PB_ROWS);
+    if (it + 2 < nrb) issue_rows(rb + 2 * PB_ROWS, qb0, lb0, sb0);
+    block(qb1, lb1, sb1, rb + PB_ROWS);
   }
 
   const float mine0 = acc0 - comp0, mine1 = acc1 - comp1;
@@ -643,10 +721,17 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (!a.wsum) return hipSuccess;
+  return launch_attn_b_native(a, s);
+}
+
+hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s) {
+  const int groups = a.B * a.Hkv;
   const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
-  {
-    KernelTimer timer(H2O_K_ATTN_B, s);
-    hipLaunchKernelGGL(attn_b_native, dim3(nB), dim3(256), 0, s, a);
+  KernelTimer timer(H2O_K_ATTN_B, s);
+  switch (a.cache_fmt) {
+    case FMT_INT8: hipLaunchKernelGGL(attn_b_native<FMT_INT8>, dim3(nB), dim3(256), 0, s, a); break;
+    case FMT_INT4: hipLaunchKernelGGL(attn_b_native<FMT_INT4>, dim3(nB), dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(attn_b_native<FMT_NATIVE>, dim3(nB), dim3(256), 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -73,11 +73,14 @@ __device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4]) {
     const uint32_t w[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      // even elements are the low nibbles, odd ones the high nibbles; with the
+      // nibbles spread into bytes each converts with one v_cvt_f32_ubyteN
+      const uint32_t ev = w[i] & 0x0f0f0f0fu, od = (w[i] >> 4) & 0x0f0f0f0fu;
       uint32_t r[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t byte = (w[i] >> (8 * q)) & 0xffu;  // element 2k in the low nibble
-        const float lo = static_cast<float>(byte & 15u), hi = static_cast<float>(byte >> 4);
+        const float lo = static_cast<float>((ev >> (8 * q)) & 0xffu);
+        const float hi = static_cast<float>((od >> (8 * q)) & 0xffu);
         r[q] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
       }
       out[i] = make_uint4(r[0], r[1], r[2], r[3]);

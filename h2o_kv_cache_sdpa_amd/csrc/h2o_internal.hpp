@@ -71,6 +71,8 @@ class KernelTimer {
 hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s);
+// Pass B (summed weights) for bf16 queries, D = 128, any cache format.
+hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s);
 // Pass A alone for int8 / int4 caches, bf16, D = 128.
 hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s);
 // Key splits pass A uses for these sizes (1 unless the row blocks alone
