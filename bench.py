@@ -197,8 +197,8 @@ def sweep_small_t(args):
     from h2o_kv_cache_sdpa_amd import workloads as W
     dev = torch.device("cuda:0")
     base = W.WORKLOADS[3]
-    for fmt in ("native", "int8", "int4"):
-        for T in (1, 16, 64, 128):
+    for fmt in args.sweep_fmts.split(","):
+        for T in (int(t) for t in args.sweep_ts.split(",")):
             w = base.scaled(T=T, cache_fmt=fmt, name=f"small_t_{fmt}_32k_t{T}")
             gc, chunks = _resident_setup(w, "h2o", dev)
             out, wsum, slot_log = gc.new_outputs(w.C)
@@ -214,23 +214,31 @@ def sweep_small_t(args):
             for i in range(10):
                 step(i)
             torch.cuda.synchronize()
-            api.profile_reset()
-            api.profile_enable(True)
+            # step time without per-kernel events
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
+            t0 = time.perf_counter()
             for i in range(reps):
                 step(i)
+            host_ms = (time.perf_counter() - t0) * 1e3 / reps
             e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            # per-kernel breakdown in a second, event-bracketed run
+            api.profile_reset()
+            api.profile_enable(True)
+            for i in range(reps):
+                step(i)
             torch.cuda.synchronize()
             api.profile_enable(False)
             prof = api.profile_read()
-            ms = e0.elapsed_time(e1) / reps
             nbytes = step_bytes(w, w.C)
             print(json.dumps({
                 "sweep": "small_t", "workload": w.name, "cache_fmt": fmt, "chunk": T, "cache_slots": w.C,
                 "ms_per_step": ms, "tokens_per_s": w.B * T / (ms * 1e-3),
                 "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
                 "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                "host_enqueue_ms": host_ms,
                 "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()},
             }), flush=True)
             del gc, chunks, out, wsum, slot_log
@@ -250,6 +258,8 @@ def main():
     ap.add_argument("--sweep-small-t", action="store_true",
                     help="chunk lengths 1, 16, 64, 128 on the 32K-slot cache in bf16, int8 and int4; "
                          "one JSON line each (HBM-bound regime)")
+    ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
+    ap.add_argument("--sweep-ts", default="1,16,64,128", help="chunk lengths of --sweep-small-t")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.workload, *args.traffic_from)

@@ -687,7 +687,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (!a.wsum) return hipSuccess;
-  if (D == 128) return launch_attn_b_native(a, s);  // every cache format
+  if (D == 128) return a.lg ? launch_attn_b_logits(a, s) : launch_attn_b_native(a, s);  // every cache format
   const int nB = groups * ((a.n_occ + a.T + B_KEYS - 1) / B_KEYS);
   {
     KernelTimer timer(H2O_K_ATTN_B, s);

@@ -56,6 +56,8 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
 // Pass A: 128 packed query rows per block, 4 wavefronts x 32 rows
 // ---------------------------------------------------------------------------
 
+// LG: also store the raw logits of every tile (short chunks; a.lg).
+template <bool LG>
 __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
@@ -168,6 +170,9 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   auto tile_step = [&](int t, f32x16 c0, f32x16 c1, const char *kb_next, f32x16 &n0, f32x16 &n1,
                        const char *vb) {
     const int j0 = (t_lo + t) * 64;
+    if constexpr (LG) {
+      if (row_ok) store_logits(a.lg + (static_cast<size_t>(grp) * R + my_row) * a.lg_stride + j0 + 8 * hl, c0, c1);
+    }
     if (wave_ragged || j0 + 63 - n_occ > wave_i_min) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -335,28 +340,43 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
   const int rloc = slot / sg, sl = slot % sg;
   const size_t row = static_cast<size_t>(blockIdx.x) * (8 / sg) + rloc;
   const bool ok = rloc < 8 / sg && row < rows;
+  // nsplit <= 64 = 8 lane groups x MAXI: every load of a lane group is issued
+  // before the first one is used
+  constexpr int MAXI = 8;
+  float ms[MAXI], ls[MAXI];
+  float4 po[MAXI];
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    const int sp = sl + i * sg;
+    ms[i] = -INFINITY;
+    ls[i] = 0.f;
+    po[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ok && sp < ns) {
+      const size_t pr = sp * rows + row;
+      const float2 v = *reinterpret_cast<const float2 *>(a.part_ml + 2 * pr);
+      ms[i] = v.x;
+      ls[i] = v.y;
+      po[i] = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c);
+    }
+  }
   float M = -INFINITY;
-  if (ok)
-    for (int sp = sl; sp < ns; sp += sg) M = fmaxf(M, a.part_ml[2 * (sp * rows + row)]);
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) M = fmaxf(M, ms[i]);
   if (c == 0) red_m[slot] = M;
   __syncthreads();
   if (ok)
     for (int k = 0; k < sg; ++k) M = fmaxf(M, red_m[rloc * sg + k]);
   float l = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (ok) {
-    for (int sp = sl; sp < ns; sp += sg) {
-      const size_t pr = sp * rows + row;
-      const float ms = a.part_ml[2 * pr], ls = a.part_ml[2 * pr + 1];
-      if (ms == -INFINITY) continue;  // no visible key in this split
-      const float wgt = __builtin_amdgcn_exp2f(ms - M);
-      l = fmaf(ls, wgt, l);
-      const float4 o = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c);
-      acc.x = fmaf(o.x, wgt, acc.x);
-      acc.y = fmaf(o.y, wgt, acc.y);
-      acc.z = fmaf(o.z, wgt, acc.z);
-      acc.w = fmaf(o.w, wgt, acc.w);
-    }
+#pragma unroll
+  for (int i = 0; i < MAXI; ++i) {
+    if (ms[i] == -INFINITY) continue;  // no visible key in this split (or no split)
+    const float wgt = __builtin_amdgcn_exp2f(ms[i] - M);
+    l = fmaf(ls[i], wgt, l);
+    acc.x = fmaf(po[i].x, wgt, acc.x);
+    acc.y = fmaf(po[i].y, wgt, acc.y);
+    acc.z = fmaf(po[i].z, wgt, acc.z);
+    acc.w = fmaf(po[i].w, wgt, acc.w);
   }
   red_o[slot][c] = acc;
   if (c == 0) red_l[slot] = l;
@@ -379,6 +399,45 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
     a.lse2[row] = L;
     if (a.lse_nat) a.lse_nat[row] = L * 0.69314718055994530942f;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Summed weights of short chunks from the logits pass A stored: one thread per
+// key, rows of the KV group in order, Kahan-compensated like pass B.  Key j is
+// visible to row r (chunk position r / qg) when it is a cache slot or a chunk
+// key at a position <= r / qg.
+// ---------------------------------------------------------------------------
+// xs: factor that brings a stored logit to log2 units (sl2 for native caches,
+// whose pass A stores q.k; 1 for 8/4-bit caches, whose factors include sl2).
+__global__ __launch_bounds__(256) void attn_b_logits(AttnArgs a, float xs) {
+  __shared__ float Ls[LOGIT_ROWS_MAX];
+  const int grp = blockIdx.y, g = grp % a.Hkv, b = grp / a.Hkv;
+  const int R = a.qg * a.T;
+  if (threadIdx.x < R) {
+    const int r = threadIdx.x, i = r / a.qg, hh = r % a.qg;
+    Ls[r] = a.lse2[(static_cast<size_t>(b) * a.Hq + g * a.qg + hh) * a.T + i];
+  }
+  __syncthreads();
+  const int n_keys = a.n_occ + a.T;
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j >= n_keys) return;
+  const float *src = a.lg + static_cast<size_t>(grp) * R * a.lg_stride + j;
+  const int t = j - a.n_occ;  // chunk position of the key, < 0 for cache slots
+  float x[LOGIT_ROWS_MAX];
+#pragma unroll
+  for (int r = 0; r < LOGIT_ROWS_MAX; ++r) x[r] = r < R ? src[static_cast<size_t>(r) * a.lg_stride] : 0.f;
+  float acc = 0.f, comp = 0.f;
+#pragma unroll
+  for (int r = 0; r < LOGIT_ROWS_MAX; ++r) {
+    if (r < R && t * a.qg <= r - r % a.qg) {  // t <= r / qg
+      const float p = __builtin_amdgcn_exp2f(fmaf(x[r], xs, -Ls[r]));
+      const float y = p - comp;
+      const float s2 = acc + y;
+      comp = (s2 - acc) - y;
+      acc = s2;
+    }
+  }
+  a.wsum[static_cast<size_t>(grp) * n_keys + j] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -712,7 +771,11 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
   const int nA = groups * ((R + 127) / 128) * a.nsplit;
   {
     KernelTimer timer(H2O_K_ATTN_A, s);
-    hipLaunchKernelGGL(attn_a_native, dim3(nA), dim3(256), 0, s, a);
+    if (a.lg) {
+      hipLaunchKernelGGL(attn_a_native<true>, dim3(nA), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(attn_a_native<false>, dim3(nA), dim3(256), 0, s, a);
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -721,7 +784,16 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
     if (e != hipSuccess) return e;
   }
   if (!a.wsum) return hipSuccess;
+  if (a.lg) return launch_attn_b_logits(a, s);
   return launch_attn_b_native(a, s);
+}
+
+hipError_t launch_attn_b_logits(const AttnArgs &a, hipStream_t s) {
+  const int n_keys = a.n_occ + a.T;
+  KernelTimer timer(H2O_K_ATTN_B, s);
+  const float xs = a.cache_fmt == FMT_NATIVE ? a.sl2 : 1.f;
+  hipLaunchKernelGGL(attn_b_logits, dim3((n_keys + 255) / 256, a.B * a.Hkv), dim3(256), 0, s, a, xs);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s) {

@@ -88,7 +88,8 @@ __device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4]) {
   }
 }
 
-template <int FMT>
+// LG: also store every tile's logits (in log2 units) for short chunks (a.lg).
+template <int FMT, bool LG>
 __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
   using Q = QTile<FMT>;
   __shared__ __attribute__((aligned(1024))) char kb[TILE_BYTES];  // bf16 K tile (K/Q swizzle)
@@ -293,6 +294,9 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
         }
       }
     }
+    if constexpr (LG) {
+      if (row_ok) store_logits(a.lg + (static_cast<size_t>(grp) * R + my_row) * a.lg_stride + j0 + 8 * hl, c0, c1);
+    }
     if (wave_ragged || j0 + 63 - n_occ > wave_i_min) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -429,9 +433,17 @@ hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s) {
   const int nA = groups * ((R + 127) / 128) * a.nsplit;
   KernelTimer timer(H2O_K_ATTN_A, s);
   if (a.cache_fmt == FMT_INT8) {
-    hipLaunchKernelGGL(attn_a_quant<FMT_INT8>, dim3(nA), dim3(256), 0, s, a);
+    if (a.lg) {
+      hipLaunchKernelGGL((attn_a_quant<FMT_INT8, true>), dim3(nA), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_a_quant<FMT_INT8, false>), dim3(nA), dim3(256), 0, s, a);
+    }
   } else {
-    hipLaunchKernelGGL(attn_a_quant<FMT_INT4>, dim3(nA), dim3(256), 0, s, a);
+    if (a.lg) {
+      hipLaunchKernelGGL((attn_a_quant<FMT_INT4, true>), dim3(nA), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_a_quant<FMT_INT4, false>), dim3(nA), dim3(256), 0, s, a);
+    }
   }
   return hipGetLastError();
 }

@@ -1,5 +1,4 @@
-// Score accumulate + slot selection + replay log + seeding, one workgroup of
-// 1024 threads per (b, KV head) -- per KV head for h2o_orig.
+// Score accumulate + slot selection + replay log + seeding.
 //
 // H2O score = cumulative sum of attention weights; the lowest-scoring slots are
 // overwritten (aimodeling article on KeysAndValues; "Learning how to Forget",
@@ -13,13 +12,21 @@
 // The stored scores stay cumulative and per (b, h, slot) under all three.
 //
 // Selection of the T smallest keys under (score, slot index) is an MSB-first
-// radix select over the order-preserving uint32 image of the fp32 scores
-// (4 passes of 8 bits, LDS histograms with wave-aggregated increments), then
-// an index-ordered compaction: a slot is taken if its key is below the
-// threshold key, or equal to it and among the first k such slots.  The replay
-// log row comes out in ascending slot order; chunk token t goes to the t-th
-// entry.  Each thread owns ITEMS consecutive slots held in registers (loaded
-// through LDS so that global accesses stay coalesced).
+// radix select over the order-preserving uint32 image of the fp32 ranking
+// values (up to 4 passes of 8 bits over the occupied key range, LDS
+// histograms), then an index-ordered compaction: a slot is taken if its key is
+// below the threshold key, or equal to it and among the first k such slots.
+// The replay log row comes out in ascending slot order; chunk token t goes to
+// the t-th entry.
+//
+// Two launch shapes:
+//  * one 1024-thread workgroup per (b, KV head) -- per KV head for h2o_orig --
+//    that updates, selects and writes (filling, long chunks, no workspace);
+//  * for short chunks a candidate pass over slices of SLICE slots (many
+//    workgroups per head: update, rank, and keep each slice's T smallest in
+//    slot order), then one workgroup per head that selects the T smallest of
+//    the candidates.  A slot among the T smallest of its head is among the T
+//    smallest of its slice, so both shapes select the same slots.
 
 #include "device_util.hpp"
 #include "h2o_internal.hpp"
@@ -27,8 +34,9 @@
 namespace h2o {
 namespace {
 
-constexpr int NT = 1024;
-constexpr int NWAVES = NT / 64;
+constexpr int NT = 1024;     // threads of the per-head workgroups
+constexpr int SLICE = 1024;  // slots per candidate workgroup
+constexpr int NT_C = 256;    // threads of the candidate workgroups (4 slots each)
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -36,9 +44,16 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+struct SelShared {
+  uint32_t hist[256];
+  uint32_t sel, k;
+  uint32_t a[16], b[16];
+};
+
 // Block-wide exclusive scan of two counters; returns the prefixes for this thread.
+template <int NTH>
 __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t &ea, uint32_t &eb,
-                                            uint32_t *sh_a, uint32_t *sh_b) {
+                                            SelShared &sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t ia = a, ib = b;
 #pragma unroll
@@ -50,114 +65,35 @@ __device__ __forceinline__ void block_scan2(uint32_t a, uint32_t b, uint32_t &ea
     }
   }
   if (lane == 63) {
-    sh_a[wave] = ia;
-    sh_b[wave] = ib;
+    sh.a[wave] = ia;
+    sh.b[wave] = ib;
   }
   __syncthreads();
   uint32_t pa = 0, pb = 0;
   for (int w = 0; w < wave; ++w) {
-    pa += sh_a[w];
-    pb += sh_b[w];
+    pa += sh.a[w];
+    pb += sh.b[w];
   }
   ea = pa + ia - a;
   eb = pb + ib - b;
+  __syncthreads();  // sh.a / sh.b are free again
 }
 
-template <int ITEMS, bool STAGE, int POL>
-__global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
-  // Updated scores pass through LDS so that global traffic is coalesced while
-  // each thread still owns a contiguous index range (row stride ITEMS + 1
-  // keeps the per-thread reads conflict-free).
-  extern __shared__ float stage[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_sel, sh_k;
-  __shared__ uint32_t sh_a[NWAVES], sh_b[NWAVES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int C = a.C, T = a.T, n_occ = a.n_occ;
-  const int n_keys = n_occ + T;
-  // h2o_orig: this workgroup serves KV head blockIdx.x of every batch row
-  const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
-  auto grp_of = [&](int bb) { return (POL == H2O_POLICY_ORIG) ? bb * a.Hkv + blockIdx.x : blockIdx.x; };
-  const int grp = grp_of(0);
-  float *phi = a.scores + static_cast<size_t>(grp) * C;
-  const float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
-  int32_t *log = a.slot_log + static_cast<size_t>(grp) * T;
-  int32_t *tp = a.token_pos ? a.token_pos + static_cast<size_t>(grp) * C : nullptr;
-  // Updated score of slot j in every batch row served; returns the ranking value.
-  auto update = [&](int j) -> float {
-    if constexpr (POL == H2O_POLICY_ORIG) {
-      float tot = 0.f;
-      for (int bb = 0; bb < nb; ++bb) {
-        const size_t g = static_cast<size_t>(grp_of(bb));
-        const float f = a.scores[g * C + j] + a.wsum[g * n_keys + j];
-        a.scores[g * C + j] = f;
-        tot = (bb == 0) ? f : tot + f;
-      }
-      return tot;
-    } else {
-      const float f = phi[j] + w[j];
-      phi[j] = f;
-      if constexpr (POL == H2O_POLICY_NORM) {
-        return f / static_cast<float>(a.pos + T - tp[j]);
-      }
-      return f;
-    }
-  };
-
-  if (POL != H2O_POLICY_ORIG && n_occ + T <= C) {  // filling: left to right
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      const int j = tid + k * NT;
-      if (j < n_occ) phi[j] = phi[j] + w[j];
-    }
-    for (int t = tid; t < T; t += NT) {
-      const int slot = n_occ + t;
-      log[t] = slot;
-      phi[slot] = w[n_occ + t];
-      if (tp) tp[slot] = static_cast<int32_t>(a.pos + t);
-    }
-    return;
-  }
-
-  // evicting: n_occ == C.  phi += w
-  const int base = tid * ITEMS;
-  uint32_t key[ITEMS];
-  if constexpr (STAGE) {  // coalesced, staged in LDS
-    // fixed trip count so that all loads of a thread are in flight together
-    float f[ITEMS];
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      const int j = tid + k * NT;
-      f[k] = (j < C) ? update(j) : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      const int j = tid + k * NT;
-      if (j < C) stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = f[k];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k)
-      key[k] = (base + k < C) ? ordered_key(stage[tid * (ITEMS + 1) + k]) : 0xffffffffu;
-  } else {  // caches too large to stage: each thread reads its own range
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      const int j = base + k;
-      key[k] = 0xffffffffu;
-      if (j < C) key[k] = ordered_key(update(j));
-    }
-  }
-
-  // Keys relative to the block minimum, so that the first 8-bit digit is
-  // taken from the top of the occupied range (the raw top byte -- sign and
-  // exponent -- takes few values, and counting them serialises on a few bins).
+// Threshold of the `need` smallest of the block's keys; key[k] is valid for
+// k < nvalid.  Keys are rewritten relative to the block minimum, so that the
+// first digit is taken from the top of the occupied range (the raw top byte --
+// sign and exponent -- takes few values).  theta is the (relative) key of the
+// need-th smallest; take_eq says how many keys equal to theta are taken.
+template <int NTH, int ITEMS>
+__device__ __forceinline__ void select_smallest(uint32_t (&key)[ITEMS], int nvalid, uint32_t need,
+                                                SelShared &sh, uint32_t &theta, uint32_t &take_eq) {
+  constexpr int NW = NTH / 64;
+  const int tid = threadIdx.x, lane = tid & 63;
   {
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      if (base + k < C) {
+      if (k < nvalid) {
         kmin = min(kmin, key[k]);
         kmax = max(kmax, key[k]);
       }
@@ -168,28 +104,28 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
       kmax = max(kmax, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmax), o)));
     }
     if (lane == 0) {
-      sh_a[tid >> 6] = kmin;
-      sh_b[tid >> 6] = kmax;
+      sh.a[tid >> 6] = kmin;
+      sh.b[tid >> 6] = kmax;
     }
     __syncthreads();
-    kmin = sh_a[0];
-    kmax = sh_b[0];
-    for (int wv = 1; wv < NWAVES; ++wv) {
-      kmin = min(kmin, sh_a[wv]);
-      kmax = max(kmax, sh_b[wv]);
+    kmin = sh.a[0];
+    kmax = sh.b[0];
+    for (int wv = 1; wv < NW; ++wv) {
+      kmin = min(kmin, sh.a[wv]);
+      kmax = max(kmax, sh.b[wv]);
     }
-    __syncthreads();
 #pragma unroll
-    for (int k = 0; k < ITEMS; ++k) key[k] -= kmin;  // padding keys wrap to large values, never active
+    for (int k = 0; k < ITEMS; ++k) key[k] -= kmin;  // invalid keys are never counted
     const uint32_t range = kmax - kmin;
-    sh_k = range ? 32 - __builtin_clz(range) : 0;  // significant bits of the range
+    __syncthreads();
+    if (tid == 0) sh.k = range ? 32 - __builtin_clz(range) : 0;  // significant bits of the range
   }
   __syncthreads();
-  const int nbits = static_cast<int>(sh_k);
+  const int nbits = static_cast<int>(sh.k);
   __syncthreads();
   const int npass = (nbits + 7) / 8;
 
-  uint32_t prefix = 0, pmask = 0, need = static_cast<uint32_t>(T);
+  uint32_t prefix = 0, pmask = 0;
   for (int pass = 0; pass < npass; ++pass) {
     // digit p covers bits [shift, shift + width) counted from the top of the range
     int shift = nbits - 8 * (pass + 1), width = 8;
@@ -198,20 +134,16 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
       shift = 0;
     }
     const uint32_t dmask = (1u << width) - 1u;
-    for (int e = tid; e < 256; e += NT) hist[e] = 0;
+    for (int e = tid; e < 256; e += NTH) sh.hist[e] = 0;
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      const bool act = (base + k < C) && ((key[k] & pmask) == prefix);
-      const uint32_t digit = (key[k] >> shift) & dmask;
-      // one LDS atomic per key; lanes hitting the same bin are serialised by
-      // the LDS, which costs less than aggregating per distinct digit
-      if (act) atomicAdd(&hist[digit], 1u);
+    for (int k = 0; k < ITEMS; ++k) {  // one LDS atomic per key
+      if (k < nvalid && (key[k] & pmask) == prefix) atomicAdd(&sh.hist[(key[k] >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (tid < 64) {
-      const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1];
-      const uint32_t c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+      const uint32_t c0 = sh.hist[4 * tid], c1 = sh.hist[4 * tid + 1];
+      const uint32_t c2 = sh.hist[4 * tid + 2], c3 = sh.hist[4 * tid + 3];
       const uint32_t s = c0 + c1 + c2 + c3;
       uint32_t inc = s;
 #pragma unroll
@@ -235,49 +167,278 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
             }
           }
         }
-        sh_sel = d;
-        sh_k = need - c;
+        sh.sel = d;
+        sh.k = need - c;
       }
     }
     __syncthreads();
-    prefix |= sh_sel << shift;
+    prefix |= sh.sel << shift;
     pmask |= dmask << shift;
-    need = sh_k;
+    need = sh.k;
     __syncthreads();
   }
-  const uint32_t theta = prefix;  // key of the T-th smallest slot
-  const uint32_t take_eq = need;  // how many slots with key == theta are taken
+  theta = prefix;
+  take_eq = need;
+}
+
+// Position in the selection (-1: not taken) of a thread's next valid key, in
+// index order; less_before / eq_before come from block_scan2 and advance.
+__device__ __forceinline__ int rank_in_selection(uint32_t key, uint32_t theta, uint32_t take_eq,
+                                                 uint32_t &less_before, uint32_t &eq_before) {
+  int out = -1;
+  if (key < theta) {
+    out = static_cast<int>(less_before + min(eq_before, take_eq));
+    ++less_before;
+  } else if (key == theta) {
+    if (eq_before < take_eq) out = static_cast<int>(less_before + eq_before);
+    ++eq_before;
+  }
+  return out;
+}
+
+// Updated scores of slots j0 + k * stride below lim (k < ITEMS) in every batch
+// row served; rank[k] gets the ranking value.  Loads go out UB items at a time
+// ahead of their stores: a store may alias a later load as far as the compiler
+// knows, so interleaving them one by one would serialise ITEMS memory round trips.
+template <int POL, int ITEMS>
+__device__ __forceinline__ void update_scores(const EvictArgs &a, int head, int j0, int stride, int lim,
+                                              float (&rank)[ITEMS]) {
+  constexpr int UB = ITEMS < 8 ? ITEMS : 8;
+  const int C = a.C, n_keys = a.n_occ + a.T;
+  const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+  for (int bb = 0; bb < nb; ++bb) {
+    const size_t g = (POL == H2O_POLICY_ORIG) ? static_cast<size_t>(bb) * a.Hkv + head : head;
+    float *ph = a.scores + g * C;
+    const float *wv = a.wsum + g * n_keys;
+    const int32_t *tp = a.token_pos ? a.token_pos + g * C : nullptr;
+#pragma unroll
+    for (int k0 = 0; k0 < ITEMS; k0 += UB) {
+      float f[UB], d[UB];
+      int32_t t0[UB] = {};
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int j = j0 + (k0 + u) * stride;
+        f[u] = j < lim ? ph[j] : 0.f;
+        d[u] = j < lim ? wv[j] : 0.f;
+        if constexpr (POL == H2O_POLICY_NORM) t0[u] = j < lim ? tp[j] : 0;
+      }
+#pragma unroll
+      for (int u = 0; u < UB; ++u) {
+        const int k = k0 + u;
+        const int j = j0 + k * stride;
+        f[u] += d[u];
+        if (j < lim) ph[j] = f[u];
+        if constexpr (POL == H2O_POLICY_ORIG) {
+          rank[k] = (bb == 0) ? f[u] : rank[k] + f[u];
+        } else if constexpr (POL == H2O_POLICY_NORM) {
+          rank[k] = f[u] / static_cast<float>(a.pos + a.T - t0[u]);
+        } else {
+          rank[k] = f[u];
+        }
+      }
+    }
+  }
+}
+
+// Replay-log entry `out` of every batch row served becomes slot j: log entry,
+// score seeded with the chunk token's own sum (seed0 for the first row),
+// token position.
+template <int POL>
+__device__ __forceinline__ void take_slot(const EvictArgs &a, int head, int j, int out, float seed0) {
+  const int C = a.C, T = a.T, n_keys = a.n_occ + T;
+  const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+  for (int bb = 0; bb < nb; ++bb) {
+    const size_t g = (POL == H2O_POLICY_ORIG) ? static_cast<size_t>(bb) * a.Hkv + head : head;
+    const float seed = (bb == 0) ? seed0 : a.wsum[g * n_keys + C + out];
+    a.slot_log[g * T + out] = j;
+    a.scores[g * C + j] = seed;
+    if (a.token_pos) a.token_pos[g * C + j] = static_cast<int32_t>(a.pos + out);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One workgroup per head: update, select, write.
+// ---------------------------------------------------------------------------
+template <int ITEMS, bool STAGE, int POL>
+__global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
+  // Updated scores pass through LDS so that global traffic is coalesced while
+  // each thread still owns a contiguous index range (row stride ITEMS + 1
+  // keeps the per-thread reads conflict-free).
+  extern __shared__ float stage[];
+  __shared__ SelShared sh;
+
+  const int tid = threadIdx.x;
+  const int C = a.C, T = a.T, n_occ = a.n_occ;
+  const int n_keys = n_occ + T;
+  const int head = blockIdx.x;  // (b, KV head); the KV head for h2o_orig
+  const size_t grp0 = head;     // first batch row's group
+
+  if (POL != H2O_POLICY_ORIG && n_occ + T <= C) {  // filling: left to right
+    {
+      float unused[ITEMS];
+      update_scores<POL, ITEMS>(a, head, tid, NT, n_occ, unused);
+    }
+    const float *w = a.wsum + grp0 * n_keys;
+    for (int t = tid; t < T; t += NT) {
+      const int slot = n_occ + t;
+      a.slot_log[grp0 * T + t] = slot;
+      a.scores[grp0 * C + slot] = w[n_occ + t];
+      if (a.token_pos) a.token_pos[grp0 * C + slot] = static_cast<int32_t>(a.pos + t);
+    }
+    return;
+  }
+
+  // evicting: n_occ == C
+  const int base = tid * ITEMS;
+  uint32_t key[ITEMS];
+  if constexpr (STAGE) {  // coalesced, staged in LDS
+    float f[ITEMS];
+    update_scores<POL, ITEMS>(a, head, tid, NT, C, f);
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int j = tid + k * NT;
+      if (j < C) stage[(j / ITEMS) * (ITEMS + 1) + j % ITEMS] = f[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      key[k] = (base + k < C) ? ordered_key(stage[tid * (ITEMS + 1) + k]) : 0xffffffffu;
+  } else {  // caches too large to stage: each thread reads its own range
+    float f[ITEMS];
+    update_scores<POL, ITEMS>(a, head, base, 1, C, f);
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) key[k] = base + k < C ? ordered_key(f[k]) : 0xffffffffu;
+  }
+  const int nvalid = C - base;  // items k < nvalid are slots
+
+  uint32_t theta, take_eq;
+  select_smallest<NT, ITEMS>(key, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
 
   uint32_t nl = 0, ne = 0;
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
-    if (base + k < C) {
+    if (k < nvalid) {
       nl += key[k] < theta;
       ne += key[k] == theta;
     }
   }
   uint32_t less_before, eq_before;
-  block_scan2(nl, ne, less_before, eq_before, sh_a, sh_b);
+  block_scan2<NT>(nl, ne, less_before, eq_before, sh);
+  // UB slots at a time: positions, then the batch's seeds, then its stores
+  // (see update_scores)
+  constexpr int UB = ITEMS < 8 ? ITEMS : 8;
+  const float *w0 = a.wsum + grp0 * n_keys;
+#pragma unroll
+  for (int k0 = 0; k0 < ITEMS; k0 += UB) {
+    int out[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      out[u] = k0 + u < nvalid ? rank_in_selection(key[k0 + u], theta, take_eq, less_before, eq_before) : -1;
+    float seed[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) seed[u] = out[u] >= 0 ? w0[C + out[u]] : 0.f;
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      if (out[u] >= 0) take_slot<POL>(a, head, base + k0 + u, out[u], seed[u]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Short chunks, pass 1: per slice of SLICE slots, update, rank, and keep the T
+// smallest (every slot of a slice that holds at most T) as (key, slot) pairs
+// in slot order at cand[(head * nslice + slice) * T ..].
+// ---------------------------------------------------------------------------
+template <int POL>
+__global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
+  constexpr int ITEMS = SLICE / NT_C;
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int C = a.C, T = a.T;
+  const int slice = blockIdx.x, head = blockIdx.y, nslice = gridDim.x;
+  const int s0 = slice * SLICE;
+  const int len = min(SLICE, C - s0);
+  const int base = s0 + tid * ITEMS;
+  const int nvalid = s0 + len - base;
+  float f[ITEMS];
+  update_scores<POL, ITEMS>(a, head, base, 1, s0 + len, f);
+  uint32_t key[ITEMS], rel[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) rel[k] = key[k] = ordered_key(f[k]);
+  uint2 *dst = cand + (static_cast<size_t>(head) * nslice + slice) * T;
+
+  if (len <= T) {  // the whole slice (only the last one can be this short)
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      if (k < nvalid) dst[base + k - s0] = make_uint2(key[k], static_cast<uint32_t>(base + k));
+    return;
+  }
+  uint32_t theta, take_eq;
+  select_smallest<NT_C, ITEMS>(rel, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
+  uint32_t nl = 0, ne = 0;
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
-    const int j = base + k;
-    if (j >= C) break;
-    int out = -1;
-    if (key[k] < theta) {
-      out = static_cast<int>(less_before + min(eq_before, take_eq));
-      ++less_before;
-    } else if (key[k] == theta) {
-      if (eq_before < take_eq) out = static_cast<int>(less_before + eq_before);
-      ++eq_before;
+    if (k < nvalid) {
+      nl += rel[k] < theta;
+      ne += rel[k] == theta;
     }
-    if (out >= 0) {
-      for (int bb = 0; bb < nb; ++bb) {
-        const size_t g = static_cast<size_t>(grp_of(bb));
-        a.slot_log[g * T + out] = j;
-        a.scores[g * C + j] = a.wsum[g * n_keys + C + out];
-        if (a.token_pos) a.token_pos[g * C + j] = static_cast<int32_t>(a.pos + out);
-      }
+  }
+  uint32_t less_before, eq_before;
+  block_scan2<NT_C>(nl, ne, less_before, eq_before, sh);
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    if (k >= nvalid) continue;
+    const int out = rank_in_selection(rel[k], theta, take_eq, less_before, eq_before);
+    if (out >= 0) dst[out] = make_uint2(key[k], static_cast<uint32_t>(base + k));
+  }
+}
+
+// Short chunks, pass 2: the T smallest candidates of each head.  The lists
+// of the slices follow one another in slot order, so list order breaks ties
+// as slot order does.  ncand: list length per head (the last slice may fill
+// fewer than T entries: nreal counts the filled ones, which come first).
+template <int ITEMS, int POL>
+__global__ __launch_bounds__(NT) void evict_pick(EvictArgs a, const uint2 *cand, int ncand, int nreal) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int C = a.C, T = a.T, n_keys = a.n_occ + T;
+  const int head = blockIdx.x;
+  const uint2 *src = cand + static_cast<size_t>(head) * ncand;
+  const int base = tid * ITEMS;
+  const int nvalid = nreal - base;
+  uint32_t key[ITEMS];
+  int slot[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    const uint2 c = k < nvalid ? src[base + k] : make_uint2(0xffffffffu, 0u);
+    key[k] = c.x;
+    slot[k] = static_cast<int>(c.y);
+  }
+  uint32_t theta, take_eq;
+  select_smallest<NT, ITEMS>(key, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
+  uint32_t nl = 0, ne = 0;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    if (k < nvalid) {
+      nl += key[k] < theta;
+      ne += key[k] == theta;
     }
+  }
+  uint32_t less_before, eq_before;
+  block_scan2<NT>(nl, ne, less_before, eq_before, sh);
+  const float *w0 = a.wsum + static_cast<size_t>(head) * n_keys;
+  constexpr int UB = ITEMS < 8 ? ITEMS : 8;  // as in evict_kernel
+#pragma unroll
+  for (int k0 = 0; k0 < ITEMS; k0 += UB) {
+    int out[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      out[u] = k0 + u < nvalid ? rank_in_selection(key[k0 + u], theta, take_eq, less_before, eq_before) : -1;
+    float seed[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) seed[u] = out[u] >= 0 ? w0[C + out[u]] : 0.f;
+#pragma unroll
+    for (int u = 0; u < UB; ++u)
+      if (out[u] >= 0) take_slot<POL>(a, head, slot[k0 + u], out[u], seed[u]);
   }
 }
 
@@ -305,9 +466,52 @@ hipError_t launch_items(const EvictArgs &a, hipStream_t s) {
   return launch_pol<ITEMS, H2O_POLICY_ORIG>(a, s);
 }
 
+int n_slices(int C) { return (C + SLICE - 1) / SLICE; }
+
+// Candidate lists of at most half the slots: the two-pass shape pays off.
+bool two_pass_fits(int C, int T) { return 2LL * n_slices(C) * T <= C; }
+
+template <int POL>
+hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, hipStream_t s) {
+  const int heads = (POL == H2O_POLICY_ORIG) ? a.Hkv : a.groups;
+  const int ns = n_slices(a.C);
+  const int ncand = ns * a.T;
+  const int last = a.C - (ns - 1) * SLICE;  // slots of the last slice
+  const int nreal = (ns - 1) * a.T + (last < a.T ? last : a.T);
+  const int per = (nreal + NT - 1) / NT;
+  KernelTimer timer(H2O_K_EVICT, s);
+  hipLaunchKernelGGL(evict_cand<POL>, dim3(ns, heads), dim3(NT_C), 0, s, a, cand);
+  if (per <= 1) {
+    hipLaunchKernelGGL((evict_pick<1, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  } else if (per <= 2) {
+    hipLaunchKernelGGL((evict_pick<2, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  } else if (per <= 4) {
+    hipLaunchKernelGGL((evict_pick<4, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  } else if (per <= 8) {
+    hipLaunchKernelGGL((evict_pick<8, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  } else if (per <= 16) {
+    hipLaunchKernelGGL((evict_pick<16, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  } else {
+    hipLaunchKernelGGL((evict_pick<32, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_evict(const EvictArgs &a, hipStream_t s) {
+size_t evict_workspace_bytes(int groups, int C, int T) {
+  if (!two_pass_fits(C, T)) return 0;
+  return sizeof(uint2) * static_cast<size_t>(groups) * n_slices(C) * T;
+}
+
+hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
+  const size_t need = evict_workspace_bytes(a.groups, a.C, a.T);
+  if (a.n_occ == a.C && need && ws && ws_bytes >= need) {
+    uint2 *cand = static_cast<uint2 *>(ws);
+    if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, s);
+    if (a.policy == H2O_POLICY_ORIG) return launch_two_pass<H2O_POLICY_ORIG>(a, cand, s);
+    return launch_two_pass<H2O_POLICY_H2O>(a, cand, s);
+  }
   const int per = (a.C + NT - 1) / NT;
   if (per <= 1) return launch_items<1>(a, s);
   if (per <= 2) return launch_items<2>(a, s);

@@ -51,6 +51,28 @@ size_t split_bytes(const h2o_dims *d, int n_occ) {
   return align_up(sizeof(float) * h2o::attn_split_floats(d->B, d->Hq, d->D, d->T, ns));
 }
 
+// Short chunks keep pass A's logits for the summed weights (bf16, D = 128,
+// at most LOGIT_ROWS_MAX query rows per KV group); rows padded to 64 keys.
+bool use_logits(const h2o_dims *d) {
+  return d->dtype == H2O_BF16 && d->D == 128 && (d->Hq / d->Hkv) * d->T <= h2o::LOGIT_ROWS_MAX;
+}
+int logit_stride(const h2o_dims *d, int n_occ) { return (n_occ + d->T + 63) / 64 * 64; }
+size_t logit_bytes(const h2o_dims *d, int n_occ) {
+  if (!use_logits(d)) return 0;
+  return align_up(sizeof(float) * static_cast<size_t>(d->B) * d->Hq * d->T * logit_stride(d, n_occ));
+}
+
+// Everything the attention passes keep in the workspace, in this order.
+size_t attn_ws_bytes(const h2o_dims *d, int n_occ) {
+  return lse_bytes(d) + split_bytes(d, n_occ) + logit_bytes(d, n_occ);
+}
+
+// Candidate lists of the short-chunk slot selection (zero when not used).
+size_t evict_bytes(const h2o_dims *d) {
+  const int heads = d->B * d->Hkv;
+  return align_up(h2o::evict_workspace_bytes(heads, d->C, d->T));
+}
+
 size_t wsum_bytes(const h2o_dims *d, int n_occ) {
   return align_up(sizeof(float) * static_cast<size_t>(d->B) * d->Hkv * (n_occ + d->T));
 }
@@ -89,7 +111,7 @@ int check_sdpa(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const v
     st = check_cache_buffers(d, cache);
     if (st != H2O_OK) return st;
   }
-  if (!ws || !aligned16(ws) || ws_bytes < lse_bytes(d) + split_bytes(d, n_occ)) return H2O_EWORKSPACE;
+  if (!ws || !aligned16(ws) || ws_bytes < attn_ws_bytes(d, n_occ)) return H2O_EWORKSPACE;
   return H2O_OK;
 }
 
@@ -138,6 +160,10 @@ h2o::AttnArgs attn_args(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ
   a.nsplit = h2o::attn_splits(d->B, d->Hq, d->Hkv, d->D, d->T, n_occ, d->dtype, d->cache_fmt);
   a.part = reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d));
   a.part_ml = a.part + static_cast<size_t>(a.nsplit) * d->B * d->Hq * d->T * d->D;
+  if (wsum && use_logits(d)) {
+    a.lg = reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d) + split_bytes(d, n_occ));
+    a.lg_stride = logit_stride(d, n_occ);
+  }
   a.B = d->B;
   a.Hq = d->Hq;
   a.Hkv = d->Hkv;
@@ -220,7 +246,7 @@ int h2o_last_hip_error(void) { return g_last_hip_error; }
 
 size_t h2o_workspace_bytes(const h2o_dims *d) {
   if (check_dims(d) != H2O_OK) return 0;
-  return lse_bytes(d) + split_bytes(d, d->C) + wsum_bytes(d, d->C);
+  return attn_ws_bytes(d, d->C) + wsum_bytes(d, d->C) + evict_bytes(d);
 }
 
 int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
@@ -235,12 +261,11 @@ int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, 
 int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
                    const float *wsum, int32_t *slot_log, void *ws, size_t ws_bytes,
                    void *stream) {
-  (void)ws;
-  (void)ws_bytes;
   const int st = check_evict(d, cache, n_occ, pos, wsum, slot_log);
   if (st != H2O_OK) return st;
-  return from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, wsum, slot_log),
-                                    static_cast<hipStream_t>(stream)));
+  if (ws && !aligned16(ws)) return H2O_EWORKSPACE;
+  return from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, wsum, slot_log), ws,
+                                    ws ? ws_bytes : 0, static_cast<hipStream_t>(stream)));
 }
 
 int kv_scatter(const h2o_dims *d, h2o_cache *cache, const void *k_new, const void *v_new,
@@ -278,10 +303,9 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
   int st = check_dims(d);
   if (st != H2O_OK) return st;
   if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
-  const size_t need = lse_bytes(d) + split_bytes(d, n_occ) + (wsum ? 0 : wsum_bytes(d, n_occ));
+  const size_t need = attn_ws_bytes(d, n_occ) + (wsum ? 0 : wsum_bytes(d, n_occ));
   if (!ws || !aligned16(ws) || ws_bytes < need) return H2O_EWORKSPACE;
-  float *w = wsum ? wsum
-                  : reinterpret_cast<float *>(static_cast<char *>(ws) + lse_bytes(d) + split_bytes(d, n_occ));
+  float *w = wsum ? wsum : reinterpret_cast<float *>(static_cast<char *>(ws) + attn_ws_bytes(d, n_occ));
   st = check_sdpa(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws, ws_bytes);
   if (st != H2O_OK) return st;
   st = check_evict(d, cache, n_occ, pos, w, slot_log);
@@ -292,7 +316,10 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = launch_sdpa(attn_args(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws), s);
   if (st != H2O_OK) return st;
-  st = from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, w, slot_log), s));
+  // the rest of the workspace, if any, holds the selection's candidate lists
+  const size_t used = need;
+  st = from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, w, slot_log),
+                                  static_cast<char *>(ws) + used, ws_bytes - used, s));
   if (st != H2O_OK) return st;
   return from_hip(h2o::launch_kv_write(write_args(d, cache, k_new, v_new, slot_log), s));
 }

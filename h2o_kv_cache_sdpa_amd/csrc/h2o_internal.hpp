@@ -27,6 +27,12 @@ struct AttnArgs {
   // a combine kernel merges them into out and lse2.
   float *part, *part_ml;
   int nsplit;
+  // Short chunks (bf16, D = 128, qg*T <= LOGIT_ROWS_MAX): pass A also stores
+  // each row's logits q.k (after the cache's scale / zero) at
+  // lg[(grp*qg*T + r)*lg_stride + j], and the summed weights come from them
+  // instead of a second pass over K.  Null otherwise.
+  float *lg;
+  int lg_stride;
   int B, Hq, Hkv, D, C, T, qg, n_occ;
   int dtype, cache_fmt;
   float sl2;  // softmax scale * log2(e)
@@ -71,8 +77,11 @@ class KernelTimer {
 hipError_t launch_attn_simple(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s);
+constexpr int LOGIT_ROWS_MAX = 16;
 // Pass B (summed weights) for bf16 queries, D = 128, any cache format.
 hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s);
+// Summed weights from the logits pass A stored (a.lg).
+hipError_t launch_attn_b_logits(const AttnArgs &a, hipStream_t s);
 // Pass A alone for int8 / int4 caches, bf16, D = 128.
 hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s);
 // Key splits pass A uses for these sizes (1 unless the row blocks alone
@@ -81,7 +90,10 @@ int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int 
 // Merge of the key-split partials of pass A into out and lse2 (D = 128).
 hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s);
 size_t attn_split_floats(int B, int Hq, int D, int T, int nsplit);
-hipError_t launch_evict(const EvictArgs &a, hipStream_t s);
+// ws / ws_bytes: optional candidate buffer of evict_workspace_bytes() bytes;
+// with it, short chunks select over many workgroups per head.
+hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+size_t evict_workspace_bytes(int groups, int C, int T);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_dequant(const KvWriteArgs &a, int n_slots, float *kout, float *vout, hipStream_t s);
 

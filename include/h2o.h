@@ -145,7 +145,11 @@ int h2o_sdpa_scoresum(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ,
  *   n_occ < C < n_occ + T, or T > C when n_occ == C, returns H2O_EUNSUPPORTED;
  *   H2O_POLICY_NORM without token_pos returns H2O_EINVAL.
  *   C must be <= 65536.
- *   slot_log: int32 (B,Hkv,T). */
+ *   slot_log: int32 (B,Hkv,T).
+ *   ws: optional scratch (may be NULL; otherwise 16-byte aligned).  With at
+ *   least h2o_workspace_bytes(d) bytes, short chunks (T up to about
+ *   C / (2 * ceil(C / 1024))) select over many workgroups per head; the
+ *   selected slots are the same either way. */
 int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
                    const float *wsum, int32_t *slot_log,
                    void *ws, size_t ws_bytes, void *stream);

@@ -66,6 +66,12 @@ SDPA_CASES = [
     ("bf16", "native", 2, 8, 2, 128, 2048, 16, 2000),   # split, ragged occupancy
     ("bf16", "native", 1, 32, 8, 128, 8192, 1, 8192),   # one query per head (decode)
     ("bf16", "native", 1, 8, 2, 128, 700, 3, 0),        # tiny chunk, empty cache
+    # at most 16 query rows per KV group: sums from pass A's stored logits
+    ("bf16", "native", 1, 16, 4, 128, 5000, 4, 4321),   # 16 rows, ragged occupancy
+    ("bf16", "int8", 2, 16, 4, 128, 3000, 4, 2990),
+    ("bf16", "int8", 1, 32, 8, 128, 8192, 1, 8192),     # int8 decode
+    ("bf16", "int4", 1, 8, 2, 128, 900, 2, 64),
+    ("bf16", "native", 1, 4, 1, 128, 64, 1, 0),         # one key in all
     ("bf16", "int8", 1, 8, 2, 128, 4096, 16, 4096),     # quantised pass A split 16 ways
     ("bf16", "int4", 1, 32, 8, 128, 4096, 1, 4096),     # quantised decode, split
     ("bf16", "int4", 2, 8, 2, 128, 3000, 40, 2960),     # split, ragged
@@ -146,7 +152,9 @@ def test_sdpa_zero_queries_closed_form():
 # eviction
 # ---------------------------------------------------------------------------
 
-def _run_evict(scores, w, n_occ, T, pos=1000, token_pos=True, policy="h2o"):
+def _run_evict(scores, w, n_occ, T, pos=1000, token_pos=True, policy="h2o", two_pass=False):
+    """two_pass: hand the call a workspace, which lets short chunks select over
+    per-slice candidate lists (same result by construction)."""
     B, H, C = scores.shape
     dims = api.make_dims(B, 8 * H, H, 128, C, T, policy=policy)
     sc = torch.from_numpy(scores.copy()).to(DEV)
@@ -155,7 +163,8 @@ def _run_evict(scores, w, n_occ, T, pos=1000, token_pos=True, policy="h2o"):
     slots = torch.empty(B, H, T, dtype=torch.int32, device=DEV)
     k = torch.empty(16, dtype=torch.uint8, device=DEV)
     bufs = api.cache_struct(k, k, sc, tp)
-    api.h2o_evict_topk(dims, bufs, n_occ, pos, wd, slots)
+    ws = torch.empty(api.workspace_bytes(dims), dtype=torch.uint8, device=DEV) if two_pass else None
+    api.h2o_evict_topk(dims, bufs, n_occ, pos, wd, slots, ws)
     torch.cuda.synchronize()
     return sc.cpu().numpy(), (tp.cpu().numpy() if token_pos else None), slots.cpu().numpy()
 
@@ -171,19 +180,24 @@ EVICT_CASES = [
     (1, 1, 65536, 64, 65536),  # largest supported cache
     (1, 1, 300, 300, 300),     # T == C
     (4, 8, 2048, 1, 2048),     # single-token chunk
+    (1, 8, 32768, 1, 32768),   # decode on the 32K-slot cache
+    (1, 8, 32768, 16, 32768),
+    (2, 3, 16384, 128, 16384),
+    (1, 2, 3082, 64, 3082),    # last 1024-slot slice shorter than the chunk
 ]
 
 
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "ws"])
 @pytest.mark.parametrize("case", EVICT_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_evict_parity(case):
+def test_evict_parity(case, two_pass):
     B, H, C, T, n_occ = case
-    print(f"evict case {case}", flush=True)
+    print(f"evict case {case} two_pass={two_pass}", flush=True)
     rng = np.random.default_rng([40, B, H, C, T])
     scores = np.zeros((B, H, C), np.float32)
     scores[..., :n_occ] = rng.uniform(0, 50, (B, H, n_occ)).astype(np.float32)
     w = rng.exponential(0.3, (B, H, n_occ + T)).astype(np.float32)
     pos = 5000
-    sc, tp, slots = _run_evict(scores, w, n_occ, T, pos)
+    sc, tp, slots = _run_evict(scores, w, n_occ, T, pos, two_pass=two_pass)
     phi_upd = O.update_scores(scores.astype(np.float64), w.astype(np.float64), n_occ, C, T)
     ref = O.bottom_t(phi_upd, n_occ, C, T)
     check_selection(slots, ref, phi_upd, n_occ, C, T)
@@ -213,21 +227,23 @@ POLICY_CASES = [
     (3, 2, 4096, 512, 4096),
     (2, 2, 512, 64, 128),        # filling: the same under every policy
     (2, 1, 300, 300, 300),       # T == C
+    (2, 2, 8192, 16, 8192),      # short chunk
 ]
 
 
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "ws"])
 @pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
 @pytest.mark.parametrize("case", POLICY_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_evict_policy_parity(case, policy):
+def test_evict_policy_parity(case, policy, two_pass):
     B, H, C, T, n_occ = case
-    print(f"evict {policy} case {case}", flush=True)
+    print(f"evict {policy} case {case} two_pass={two_pass}", flush=True)
     rng = np.random.default_rng([42, B, H, C, T])
     scores = np.zeros((B, H, C), np.float32)
     scores[..., :n_occ] = rng.uniform(0, 50, (B, H, n_occ)).astype(np.float32)
     w = rng.exponential(0.3, (B, H, n_occ + T)).astype(np.float32)
     pos = 5000
     tp0 = np.arange(B * H * C, dtype=np.int32).reshape(B, H, C) % 977
-    sc, tp, slots = _run_evict(scores, w, n_occ, T, pos, policy=policy)
+    sc, tp, slots = _run_evict(scores, w, n_occ, T, pos, policy=policy, two_pass=two_pass)
     phi_upd = O.update_scores(scores.astype(np.float64), w.astype(np.float64), n_occ, C, T)
     key = O.selection_key(phi_upd, tp0, pos, T, policy) if n_occ == C else phi_upd
     ref = O.bottom_t(key, n_occ, C, T)
@@ -245,17 +261,24 @@ def test_evict_policy_parity(case, policy):
     np.testing.assert_array_equal(tp, tp_exp)
 
 
-def test_evict_ties_resolve_to_lower_index():
+@pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "ws"])
+@pytest.mark.parametrize("T", [512, 1])
+def test_evict_ties_resolve_to_lower_index(T, two_pass):
     rng = np.random.default_rng(41)
-    B, H, C, T = 2, 4, 4096, 512
+    B, H, C = 2, 4, 4096
     scores = (rng.integers(0, 9, (B, H, C)) * 0.25).astype(np.float32)  # many exact ties
     w = np.zeros((B, H, C + T), np.float32)
-    _, _, slots = _run_evict(scores, w, C, T)
+    _, _, slots = _run_evict(scores, w, C, T, two_pass=two_pass)
     ref = O.bottom_t(scores.astype(np.float64), C, C, T)
     np.testing.assert_array_equal(slots, ref)
     scores[:] = 3.0  # all tied: lowest indices
-    _, _, slots = _run_evict(scores, w, C, T, token_pos=False)
+    _, _, slots = _run_evict(scores, w, C, T, token_pos=False, two_pass=two_pass)
     assert (slots == np.arange(T)).all()
+    # ties that straddle slices: the tied minimum sits in the last slices only
+    scores[:] = 3.0
+    scores[..., 3000:] = 1.0
+    _, _, slots = _run_evict(scores, w, C, T, token_pos=False, two_pass=two_pass)
+    assert (slots == 3000 + np.arange(T)).all()
 
 
 def test_evict_signed_zero_and_negative_scores():
