@@ -58,7 +58,8 @@ def kernel_sources_digest():
     HBM-traffic measurement is only reported while it still matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "h2o_kv_cache_sdpa_amd", "csrc")
-    for name in ("attn_native.hip", "attn_mfma.hip", "device_util.hpp", "h2o_internal.hpp"):
+    for name in ("attn_native.hip", "attn_mfma.hip", "attn_quant.hip", "tile_util.hpp", "device_util.hpp",
+                 "h2o_internal.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -256,10 +257,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--sweep-small-t", action="store_true",
-                    help="chunk lengths 1, 16, 64, 128 on the 32K-slot cache in bf16, int8 and int4; "
+                    help="chunk lengths 1, 4, 16, 64, 128 on the 32K-slot cache in bf16, int8 and int4; "
                          "one JSON line each (HBM-bound regime)")
     ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
-    ap.add_argument("--sweep-ts", default="1,16,64,128", help="chunk lengths of --sweep-small-t")
+    ap.add_argument("--sweep-ts", default="1,4,16,64,128", help="chunk lengths of --sweep-small-t")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.workload, *args.traffic_from)

@@ -48,6 +48,7 @@ struct SelShared {
   uint32_t hist[256];
   uint32_t sel, k;
   uint32_t a[16], b[16];
+  uint64_t m64[16];
 };
 
 // Block-wide exclusive scan of two counters; returns the prefixes for this thread.
@@ -179,6 +180,27 @@ __device__ __forceinline__ void select_smallest(uint32_t (&key)[ITEMS], int nval
   }
   theta = prefix;
   take_eq = need;
+}
+
+// Block-wide minimum of (key << 32 | slot): for T = 1 the selection is the
+// smallest key, ties to the lowest slot.  Every thread gets the result.
+template <int NTH>
+__device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t *sh64) {
+  constexpr int NW = NTH / 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const uint64_t u = static_cast<uint64_t>(__shfl_xor(static_cast<unsigned long long>(v), o));
+    v = u < v ? u : v;
+  }
+  if constexpr (NW == 1) {
+    return v;
+  } else {
+    if ((threadIdx.x & 63) == 0) sh64[threadIdx.x >> 6] = v;
+    __syncthreads();
+    v = sh64[0];
+    for (int w = 1; w < NW; ++w) v = sh64[w] < v ? sh64[w] : v;
+    return v;
+  }
 }
 
 // Position in the selection (-1: not taken) of a thread's next valid key, in
@@ -366,6 +388,17 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
   for (int k = 0; k < ITEMS; ++k) rel[k] = key[k] = ordered_key(f[k]);
   uint2 *dst = cand + (static_cast<size_t>(head) * nslice + slice) * T;
 
+  if (T == 1) {  // the slice's smallest (key, slot)
+    uint64_t v = ~0ull;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const uint64_t u = (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(base + k);
+      if (k < nvalid && u < v) v = u;
+    }
+    v = block_min_u64<NT_C>(v, sh.m64);
+    if (tid == 0) dst[0] = make_uint2(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v));
+    return;
+  }
   if (len <= T) {  // the whole slice (only the last one can be this short)
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k)
@@ -396,8 +429,8 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
 // of the slices follow one another in slot order, so list order breaks ties
 // as slot order does.  ncand: list length per head (the last slice may fill
 // fewer than T entries: nreal counts the filled ones, which come first).
-template <int ITEMS, int POL>
-__global__ __launch_bounds__(NT) void evict_pick(EvictArgs a, const uint2 *cand, int ncand, int nreal) {
+template <int NTH, int ITEMS, int POL>
+__global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand, int ncand, int nreal) {
   __shared__ SelShared sh;
   const int tid = threadIdx.x;
   const int C = a.C, T = a.T, n_keys = a.n_occ + T;
@@ -413,8 +446,19 @@ __global__ __launch_bounds__(NT) void evict_pick(EvictArgs a, const uint2 *cand,
     key[k] = c.x;
     slot[k] = static_cast<int>(c.y);
   }
+  if (T == 1) {
+    uint64_t v = ~0ull;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const uint64_t u = (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(slot[k]);
+      if (k < nvalid && u < v) v = u;
+    }
+    v = block_min_u64<NTH>(v, sh.m64);
+    if (tid == 0) take_slot<POL>(a, head, static_cast<int>(static_cast<uint32_t>(v)), 0, a.wsum[static_cast<size_t>(head) * n_keys + C]);
+    return;
+  }
   uint32_t theta, take_eq;
-  select_smallest<NT, ITEMS>(key, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
+  select_smallest<NTH, ITEMS>(key, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
   uint32_t nl = 0, ne = 0;
 #pragma unroll
   for (int k = 0; k < ITEMS; ++k) {
@@ -424,7 +468,7 @@ __global__ __launch_bounds__(NT) void evict_pick(EvictArgs a, const uint2 *cand,
     }
   }
   uint32_t less_before, eq_before;
-  block_scan2<NT>(nl, ne, less_before, eq_before, sh);
+  block_scan2<NTH>(nl, ne, less_before, eq_before, sh);
   const float *w0 = a.wsum + static_cast<size_t>(head) * n_keys;
   constexpr int UB = ITEMS < 8 ? ITEMS : 8;  // as in evict_kernel
 #pragma unroll
@@ -478,21 +522,21 @@ hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, hipStream_t s) {
   const int ncand = ns * a.T;
   const int last = a.C - (ns - 1) * SLICE;  // slots of the last slice
   const int nreal = (ns - 1) * a.T + (last < a.T ? last : a.T);
-  const int per = (nreal + NT - 1) / NT;
   KernelTimer timer(H2O_K_EVICT, s);
   hipLaunchKernelGGL(evict_cand<POL>, dim3(ns, heads), dim3(NT_C), 0, s, a, cand);
-  if (per <= 1) {
-    hipLaunchKernelGGL((evict_pick<1, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
-  } else if (per <= 2) {
-    hipLaunchKernelGGL((evict_pick<2, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
-  } else if (per <= 4) {
-    hipLaunchKernelGGL((evict_pick<4, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
-  } else if (per <= 8) {
-    hipLaunchKernelGGL((evict_pick<8, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
-  } else if (per <= 16) {
-    hipLaunchKernelGGL((evict_pick<16, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  // short lists: one wavefront; longer ones: 256 or 1024 threads
+  if (nreal <= 64) {
+    hipLaunchKernelGGL((evict_pick<64, 1, POL>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal);
+  } else if (nreal <= 256) {
+    hipLaunchKernelGGL((evict_pick<64, 4, POL>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal);
+  } else if (nreal <= 1024) {
+    hipLaunchKernelGGL((evict_pick<256, 4, POL>), dim3(heads), dim3(256), 0, s, a, cand, ncand, nreal);
+  } else if (nreal <= 4096) {
+    hipLaunchKernelGGL((evict_pick<256, 16, POL>), dim3(heads), dim3(256), 0, s, a, cand, ncand, nreal);
+  } else if (nreal <= 16384) {
+    hipLaunchKernelGGL((evict_pick<NT, 16, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
   } else {
-    hipLaunchKernelGGL((evict_pick<32, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+    hipLaunchKernelGGL((evict_pick<NT, 32, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
   }
   return hipGetLastError();
 }
