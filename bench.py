@@ -246,6 +246,62 @@ def sweep_small_t(args):
             torch.cuda.empty_cache()
 
 
+def prefill(args):
+    """First chunk of a sequence on an empty cache: n_occ = 0, T = C, a causal
+    square with summed weights (the pages' length-N_C prefill)."""
+    import numpy as np
+    import torch
+
+    from h2o_kv_cache_sdpa_amd import api
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    from h2o_kv_cache_sdpa_amd.cache import H2OCache
+    dev = torch.device("cuda:0")
+    to_dev = lambda st: torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+    for C in (int(c) for c in args.prefill_sizes.split(",")):
+        w = W.WORKLOADS[3].scaled(C=C, T=C, name=f"prefill_bf16_{C // 1024}k")
+        gc = H2OCache(w.B, w.Hq, w.Hkv, w.D, C, C, dtype="bf16", cache_fmt="native", device=dev)
+        ch = W.chunk(w, 0)
+        q, kn, vn = to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"])
+        del ch
+        out, wsum, slot_log = gc.new_outputs(0)
+        bufs = gc.bufs()
+        stream = torch.cuda.current_stream()
+        reps = 5
+
+        def step():
+            api.h2o_chunk_step(gc.dims, bufs, 0, 0, q, kn, vn, out, wsum, slot_log, gc.ws, stream)
+
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        api.profile_reset()
+        api.profile_enable(True)
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        api.profile_enable(False)
+        prof = api.profile_read()
+        kms = {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()}
+        pairs = pairs_visible(w.B, w.Hq, C, 0)
+        a_tf = 4 * w.D * pairs / (kms["attn_a"] * 1e-3) / 1e12
+        b_tf = 2 * w.D * pairs / (kms["attn_b"] * 1e-3) / 1e12
+        print(json.dumps({
+            "prefill": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "chunk": C, "cache_slots": C,
+            "ms_per_step": ms, "tokens_per_s": w.B * C / (ms * 1e-3),
+            "step_mfma_frac_6d": 6 * w.D * pairs / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "attn_a_tflops": a_tf, "attn_b_tflops": b_tf, "kernel_ms": kms,
+        }), flush=True)
+        del gc, q, kn, vn, out, wsum, slot_log
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -259,11 +315,17 @@ def main():
     ap.add_argument("--sweep-small-t", action="store_true",
                     help="chunk lengths 1, 4, 16, 64, 128 on the 32K-slot cache in bf16, int8 and int4; "
                          "one JSON line each (HBM-bound regime)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the first chunk of a sequence (empty cache, T = C): one JSON line per size")
+    ap.add_argument("--prefill-sizes", default="16384,32768", help="cache sizes (= chunk lengths) of --prefill")
     ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
     ap.add_argument("--sweep-ts", default="1,4,16,64,128", help="chunk lengths of --sweep-small-t")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.workload, *args.traffic_from)
+        return
+    if args.prefill:
+        prefill(args)
         return
     if args.sweep_small_t:
         sweep_small_t(args)

@@ -49,6 +49,10 @@ R11 Policy variants ([LF] §3.1.1).  h2o_orig ranks slot j of KV head h by
    by its score divided by its age t - t(b,h,j), with t the number of tokens
    processed once this chunk is attended (pos + T), i.e. the number of queries
    that have contributed to the score; the stored score stays cumulative.
+R19 Gradients ([LF] §3.2, §A.10): the backward of the chunk attention is the
+   exact derivative of attend_chunk's output with respect to q, the cache
+   rows < n_occ and the chunk's keys and values (the summed weights carry no
+   gradient); dK and dV of a KV group are summed over its query heads.
 R10 Quantisers (fp32 operation sequences, IEEE round-to-nearest-even):
    int8 symmetric per slot:  a = max|x|;  s = fp16(fp32(a / 127));
         c = clamp(rne(fp32(x / fp32(s))), -127, 127);  x_hat = c * s
@@ -137,6 +141,55 @@ def attend_chunk(q, k_cache, v_cache, n_occ, k_new, v_new, scale, row_block=256)
 # --------------------------------------------------------------------------
 # Score update and bottom-T selection
 # --------------------------------------------------------------------------
+
+def attend_backward(q, k_cache, v_cache, n_occ, k_new, v_new, scale, dout):
+    """Gradients of the chunk attention of attend_chunk for an upstream
+    gradient dout = dL/d(out).
+
+    [LF] §3.2: the fine-tuning pass obtains gradients by reverse-mode
+    differentiation through each chunk's SDPA call; [LF] §A.10: the attention
+    interface that returns summed weights also has a backward.  The summed
+    weights only steer eviction and carry no gradient.  Reading R19.
+
+    With P = softmax of the masked scaled logits (attend_chunk), per query
+    row r of a KV group and key j of the group:
+      dV_j  = sum_r P_rj dO_r                 (summed over the group's heads)
+      dP_rj = <dO_r, v_j>
+      dS_rj = P_rj (dP_rj - sum_j' P_rj' dP_rj')
+      dQ_r  = scale sum_j dS_rj k_j
+      dK_j  = scale sum_r dS_rj q_r           (summed over the group's heads)
+    Masked pairs have P = 0 and contribute nothing.
+
+    Returns float64 arrays dq (B, Hq, T, D), dk_cache, dv_cache
+    (B, Hkv, n_occ, D), dk_new, dv_new (B, Hkv, T, D).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, Hq, T, D = q.shape
+    Hkv = k_new.shape[1]
+    qg = Hq // Hkv
+    n_keys = n_occ + T
+    dq = np.zeros((B, Hq, T, D))
+    dk = np.zeros((B, Hkv, n_keys, D))
+    dv = np.zeros((B, Hkv, n_keys, D))
+    hidden = np.arange(T)[None, :] > np.arange(T)[:, None]  # new key t' hidden from query i < t'
+    for b in range(B):
+        for g in range(Hkv):
+            keys = np.concatenate([k_cache[b, g, :n_occ], k_new[b, g]], axis=0)
+            vals = np.concatenate([v_cache[b, g, :n_occ], v_new[b, g]], axis=0)
+            for hh in range(qg):
+                h = g * qg + hh
+                logits = scale * (q[b, h] @ keys.T)
+                logits[:, n_occ:][hidden] = NEG_INF
+                e = np.exp(logits - logits.max(axis=1, keepdims=True))
+                p = e / e.sum(axis=1, keepdims=True)
+                dp = dout[b, h] @ vals.T
+                ds = p * (dp - (p * dp).sum(axis=1, keepdims=True))
+                dq[b, h] = scale * (ds @ keys)
+                dk[b, g] += scale * (ds.T @ q[b, h])
+                dv[b, g] += p.T @ dout[b, h]
+    return dq, dk[:, :, :n_occ], dv[:, :, :n_occ], dk[:, :, n_occ:], dv[:, :, n_occ:]
+
 
 def update_scores(phi, w, n_occ, C, T):
     """Add this chunk's summed weights to the running H2O scores of the

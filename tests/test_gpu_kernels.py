@@ -72,6 +72,10 @@ SDPA_CASES = [
     ("bf16", "int8", 1, 32, 8, 128, 8192, 1, 8192),     # int8 decode
     ("bf16", "int4", 1, 8, 2, 128, 900, 2, 64),
     ("bf16", "native", 1, 4, 1, 128, 64, 1, 0),         # one key in all
+    # prefill: the first chunk fills an empty cache (a causal square)
+    ("bf16", "native", 1, 8, 2, 128, 2048, 2048, 0),
+    ("bf16", "int8", 1, 8, 2, 128, 1024, 1024, 0),
+    ("bf16", "native", 2, 8, 4, 64, 640, 640, 0),
     ("bf16", "int8", 1, 8, 2, 128, 4096, 16, 4096),     # quantised pass A split 16 ways
     ("bf16", "int4", 1, 32, 8, 128, 4096, 1, 4096),     # quantised decode, split
     ("bf16", "int4", 2, 8, 2, 128, 3000, 40, 2960),     # split, ragged

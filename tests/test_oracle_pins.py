@@ -460,3 +460,84 @@ def test_replay_of_another_log_changes_only_the_named_slots():
     np.testing.assert_array_equal(oc.k[0, 0, 1], ch["k"].f64[0, 0, 1])
     assert oc.token_pos[0, 0, 6] == 8 and oc.token_pos[0, 0, 1] == 9
     assert (np.delete(oc.token_pos[0, 0], [1, 6]) == np.delete(tp0[0, 0], [1, 6])).all()
+
+
+# ---------------------------------------------------------------------------
+# backward of the chunk attention (reading R19)
+# ---------------------------------------------------------------------------
+
+def _bwd_case(seed, B, Hq, Hkv, D, n_occ, T, equal_values=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, T, D))
+    kc = rng.standard_normal((B, Hkv, n_occ, D))
+    vc = rng.standard_normal((B, Hkv, n_occ, D))
+    kn = rng.standard_normal((B, Hkv, T, D))
+    vn = rng.standard_normal((B, Hkv, T, D))
+    if equal_values:
+        row = rng.standard_normal(D)
+        vc[:] = row
+        vn[:] = row
+    dout = rng.standard_normal((B, Hq, T, D))
+    return q, kc, vc, kn, vn, dout
+
+
+@pytest.mark.parametrize("n_occ", [0, 5, 40])
+def test_backward_matches_torch_autograd(n_occ):
+    """torch autograd in float64 through a forward written from the
+    definition (keys = cache rows then chunk, causal chunk, GQA)."""
+    B, Hq, Hkv, D, T = 2, 4, 2, 8, 6
+    q, kc, vc, kn, vn, dout = _bwd_case([60, n_occ], B, Hq, Hkv, D, n_occ, T)
+    scale = 1.0 / math.sqrt(D)
+    tq, tkc, tvc, tkn, tvn = (torch.tensor(x, requires_grad=True) for x in (q, kc, vc, kn, vn))
+    qg = Hq // Hkv
+    keys = torch.cat([tkc, tkn], dim=2).repeat_interleave(qg, dim=1)
+    vals = torch.cat([tvc, tvn], dim=2).repeat_interleave(qg, dim=1)
+    allowed = torch.ones(T, n_occ + T, dtype=torch.bool)
+    allowed[:, n_occ:] = torch.tril(torch.ones(T, T, dtype=torch.bool))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, keys, vals, attn_mask=allowed, scale=scale)
+    (out * torch.tensor(dout)).sum().backward()
+    dq, dkc, dvc, dkn, dvn = O.attend_backward(q, kc, vc, n_occ, kn, vn, scale, dout)
+    for mine, ref in ((dq, tq), (dkc, tkc), (dvc, tvc), (dkn, tkn), (dvn, tvn)):
+        np.testing.assert_allclose(mine, ref.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_backward_central_differences():
+    """d(sum(dout * out)) / dx by central differences of attend_chunk."""
+    B, Hq, Hkv, D, n_occ, T = 1, 2, 1, 3, 3, 2
+    q, kc, vc, kn, vn, dout = _bwd_case(61, B, Hq, Hkv, D, n_occ, T)
+    scale = 0.7
+    grads = O.attend_backward(q, kc, vc, n_occ, kn, vn, scale, dout)
+    args = [q, kc, vc, kn, vn]
+
+    def loss(xs):
+        out, _, _ = O.attend_chunk(xs[0], xs[1], xs[2], n_occ, xs[3], xs[4], scale)
+        return float((out * dout).sum())
+
+    eps = 1e-6
+    rng = np.random.default_rng(62)
+    for a, grad in enumerate(grads):
+        for _ in range(4):
+            idx = tuple(int(rng.integers(0, n)) for n in args[a].shape)
+            up = [x.copy() for x in args]
+            dn = [x.copy() for x in args]
+            up[a][idx] += eps
+            dn[a][idx] -= eps
+            fd = (loss(up) - loss(dn)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (a, idx, fd, grad[idx])
+
+
+def test_backward_closed_forms():
+    """Rows of P sum to one, so dV summed over a group's keys is dO summed
+    over its rows; with every value row equal the output does not depend on
+    Q or K, so their gradients vanish."""
+    B, Hq, Hkv, D, n_occ, T = 2, 6, 2, 5, 9, 7
+    q, kc, vc, kn, vn, dout = _bwd_case(63, B, Hq, Hkv, D, n_occ, T)
+    _, _, dvc, _, dvn = O.attend_backward(q, kc, vc, n_occ, kn, vn, 0.4, dout)
+    qg = Hq // Hkv
+    total_dv = dvc.sum(axis=2) + dvn.sum(axis=2)
+    total_do = dout.reshape(B, Hkv, qg, T, D).sum(axis=(2, 3))
+    np.testing.assert_allclose(total_dv, total_do, rtol=1e-12, atol=1e-12)
+    q, kc, vc, kn, vn, dout = _bwd_case(64, B, Hq, Hkv, D, n_occ, T, equal_values=True)
+    dq, dkc, _, dkn, _ = O.attend_backward(q, kc, vc, n_occ, kn, vn, 0.4, dout)
+    for g in (dq, dkc, dkn):
+        assert np.abs(g).max() < 1e-12
