@@ -302,6 +302,74 @@ def prefill(args):
         torch.cuda.empty_cache()
 
 
+def backward(args):
+    """Gradients of the chunk attention (the fine-tuning pass): the evicting
+    step of the 32K cache (n_occ = C = 32768, T = 2048) and a 16K prefill
+    square.  Matrix work per visible pair: dq 6*D flops (S, dP, dS K),
+    dk/dv 8*D (S, dP, P^T dO, dS^T Q)."""
+    import numpy as np
+    import torch
+
+    from h2o_kv_cache_sdpa_amd import api
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    dev = torch.device("cuda:0")
+    to_dev = lambda st: torch.from_numpy(np.ascontiguousarray(st.raw).view(np.int16)).view(torch.bfloat16).to(dev)
+    for name, C, T, n_occ in (("bwd_bf16_32k_t2048", 32768, 2048, 32768), ("bwd_prefill_bf16_16k", 16384, 16384, 0)):
+        w = W.WORKLOADS[3].scaled(C=C, T=T, name=name)
+        B, Hq, Hkv, D = w.B, w.Hq, w.Hkv, w.D
+        dims = api.make_dims(B, Hq, Hkv, D, C, T)
+        ws = torch.empty(api.workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        kc = torch.randn(B, Hkv, C, D, device=dev).to(torch.bfloat16)
+        vc = torch.randn(B, Hkv, C, D, device=dev).to(torch.bfloat16)
+        ch = W.chunk(w, 0)
+        q, kn, vn = to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"])
+        del ch
+        dout = torch.randn(B, Hq, T, D, device=dev).to(torch.bfloat16)
+        bufs = api.cache_struct(kc, vc)
+        out = torch.empty_like(q)
+        wsum = torch.empty(B, Hkv, n_occ + T, dtype=torch.float32, device=dev)
+        lse = torch.empty(B, Hq, T, dtype=torch.float32, device=dev)
+        api.h2o_sdpa_scoresum(dims, bufs, n_occ, q, kn, vn, out, wsum, lse, ws)
+        dq = torch.empty(B, Hq, T, D, dtype=torch.float32, device=dev)
+        dkc = torch.empty(B, Hkv, C, D, dtype=torch.float32, device=dev)
+        dvc = torch.empty_like(dkc)
+        dkn = torch.empty(B, Hkv, T, D, dtype=torch.float32, device=dev)
+        dvn = torch.empty_like(dkn)
+        stream = torch.cuda.current_stream()
+        reps = 5
+
+        def step():
+            api.h2o_sdpa_backward(dims, bufs, n_occ, q, kn, vn, out, lse, dout, dq, dkc, dvc, dkn, dvn, ws, stream)
+
+        step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        api.profile_reset()
+        api.profile_enable(True)
+        for _ in range(reps):
+            step()
+        torch.cuda.synchronize()
+        api.profile_enable(False)
+        kms = {k: (v[0] / v[1] if v[1] else None) for k, v in api.profile_read().items() if v[1]}
+        pairs = pairs_visible(B, Hq, T, n_occ)
+        print(json.dumps({
+            "backward": name, "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "chunk": T, "cache_slots": C, "n_occ": n_occ,
+            "ms": ms, "tflops_14d": 14 * D * pairs / (ms * 1e-3) / 1e12,
+            "mfma_frac_14d": 14 * D * pairs / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "dq_tflops": 6 * D * pairs / (kms["bwd_dq"] * 1e-3) / 1e12,
+            "dkdv_tflops": 8 * D * pairs / (kms["bwd_dkdv"] * 1e-3) / 1e12,
+            "kernel_ms": kms,
+        }), flush=True)
+        del q, kn, vn, out, dout, dq, dkc, dvc, dkn, dvn, kc, vc, ws, wsum, lse
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,6 +385,8 @@ def main():
                          "one JSON line each (HBM-bound regime)")
     ap.add_argument("--prefill", action="store_true",
                     help="time the first chunk of a sequence (empty cache, T = C): one JSON line per size")
+    ap.add_argument("--backward", action="store_true",
+                    help="time h2o_sdpa_backward on the 32K evicting step and a 16K prefill square")
     ap.add_argument("--prefill-sizes", default="16384,32768", help="cache sizes (= chunk lengths) of --prefill")
     ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
     ap.add_argument("--sweep-ts", default="1,4,16,64,128", help="chunk lengths of --sweep-small-t")
@@ -326,6 +396,9 @@ def main():
         return
     if args.prefill:
         prefill(args)
+        return
+    if args.backward:
+        backward(args)
         return
     if args.sweep_small_t:
         sweep_small_t(args)

@@ -26,10 +26,11 @@ FORMATS = {"native": H2O_CACHE_NATIVE, "int8": H2O_CACHE_INT8, "int4": H2O_CACHE
 EXPORTS = (
     "h2o_abi_version", "h2o_status_str", "h2o_last_hip_error", "h2o_workspace_bytes",
     "h2o_sdpa_scoresum", "h2o_evict_topk", "kv_scatter", "kv_quant_pack",
-    "kv_dequant_unpack", "h2o_chunk_step", "h2o_replay_step", "h2o_profile_enable", "h2o_profile_read",
+    "kv_dequant_unpack", "h2o_chunk_step", "h2o_replay_step", "h2o_sdpa_backward",
+    "h2o_profile_enable", "h2o_profile_read",
     "h2o_profile_reset",
 )
-KERNEL_KINDS = ("attn_a", "attn_b", "evict", "kv_write", "attn_combine")
+KERNEL_KINDS = ("attn_a", "attn_b", "evict", "kv_write", "attn_combine", "bwd_rows", "bwd_dq", "bwd_dkdv")
 
 
 class H2ODims(ctypes.Structure):
@@ -95,6 +96,8 @@ def lib():
     L.h2o_chunk_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, P, S, P]
     L.h2o_replay_step.restype = ctypes.c_int
     L.h2o_replay_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, S, P]
+    L.h2o_sdpa_backward.restype = ctypes.c_int
+    L.h2o_sdpa_backward.argtypes = [pd, pc, I32] + [P] * 11 + [P, S, P]
     L.h2o_profile_enable.restype = ctypes.c_int
     L.h2o_profile_enable.argtypes = [ctypes.c_int]
     L.h2o_profile_read.restype = ctypes.c_int
@@ -190,6 +193,15 @@ def h2o_replay_step(dims, cache, n_occ, pos, q, k_new, v_new, out, slot_log, ws,
                                _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(slot_log),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("h2o_replay_step", st)
+
+
+def h2o_sdpa_backward(dims, cache, n_occ, q, k_new, v_new, out, lse, dout, dq, dk_cache, dv_cache,
+                      dk_new, dv_new, ws, stream=None):
+    st = lib().h2o_sdpa_backward(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), _ptr(q),
+                                 _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                 _ptr(dk_cache), _ptr(dv_cache), _ptr(dk_new), _ptr(dv_new),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("h2o_sdpa_backward", st)
 
 
 def profile_enable(on=True):

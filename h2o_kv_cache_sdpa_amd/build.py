@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh2o.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["h2o_abi.cpp", "profile.cpp", "attn_simple.hip", "attn_mfma.hip", "attn_native.hip", "attn_quant.hip", "evict.hip", "kvwrite.hip"]
+SOURCES = ["h2o_abi.cpp", "profile.cpp", "attn_simple.hip", "attn_mfma.hip", "attn_native.hip", "attn_quant.hip", "attn_bwd.hip", "evict.hip", "kvwrite.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is issued as a
 # scalar-per-lane instruction.  No fast-math: the quantisers rely on IEEE

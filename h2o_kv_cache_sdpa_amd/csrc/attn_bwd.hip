@@ -1,0 +1,441 @@
+// Backward of the chunk attention for bf16 queries, a native bf16 cache and
+// head dimension 128 ("Learning how to Forget", §3.2: gradients by reverse-mode
+// differentiation through each chunk's SDPA call; §A.10: the attention
+// interface that returns summed weights also has a backward).
+//
+// With P = softmax(mask(scale Q K^T)) as in the forward, per query row r of a
+// KV group and key j of the group:
+//   dP_rj = <dO_r, v_j>,  D_r = <dO_r, O_r> (= sum_j P_rj dP_rj),
+//   dS_rj = P_rj (dP_rj - D_r),
+//   dQ_r = scale sum_j dS_rj k_j,  dK_j = scale sum_r dS_rj q_r,  dV_j = sum_r P_rj dO_r.
+// P is recomputed from the forward's row normalisers, exp2(s * scale * log2 e - L2_r).
+//
+// Three kernels, no atomics (every output element has one writer):
+//  * bwd_rows: L2_r and D_r, one 16-lane group per row;
+//  * bwd_dq: 128 query rows per workgroup (4 waves x 32), K and V tiles of 64
+//    keys moved HBM -> LDS by buffer-load DMA, double-buffered.  S^T = K Q^T
+//    and dP^T = V dO^T on the matrix cores with Q and dO held in registers;
+//    dS in registers becomes the B operand of dQ^T += K^T dS^T, the K^T operand
+//    read from the row-major K tile by ds_read_b64_tr_b16 (as V^T in pass A);
+//  * bwd_dkdv: 128 keys per workgroup (4 waves x 32) held in registers as
+//    MFMA operands; 64-row blocks of Q and dO (and L2, D) stream through LDS,
+//    double-buffered.  Q rows enter S = Q K^T in the same permuted order pass A
+//    gives keys, so each half-wave holds runs of 8 consecutive rows of P and
+//    dS: those are the A operands of dV += P^T dO and dK += dS^T Q directly,
+//    and the dO / Q operands are transpose reads of the row blocks.
+// P and dS enter the products rounded to bf16; all accumulation is fp32.
+
+#include "device_util.hpp"
+#include "h2o_internal.hpp"
+#include "tile_util.hpp"
+
+namespace h2o {
+namespace {
+
+constexpr float LOG2E = 1.4426950408889634074f;
+
+__global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
+  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+  const size_t r = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float acc = 0.f;
+  if (r < rows) {
+    const uint4 o = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.out) + r * D + 8 * c);
+    const uint4 g = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.dout) + r * D + 8 * c);
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), acc);
+      acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+  if (r < rows && c == 0) {
+    a.dd[r] = acc;
+    a.l2[r] = a.lse[r] * LOG2E;
+  }
+}
+
+// Transpose read of a K/Q-swizzled tile: for lane l the 8 rows
+// 16*ks + 8*(l/32) + 0..7 at column 32*blk + l%32 (the A operand of a product
+// whose K dimension runs along the tile's rows).
+__device__ __forceinline__ bf16x8 tr_operand(const char *tb, int ks, int blk, int lane) {
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
+  const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row, col >> 3) + 2 * (col & 7)));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row + 4, col >> 3) + 2 * (col & 7)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// ---------------------------------------------------------------------------
+// dQ: 128 packed query rows per block (r = i * q_g + h), keys streamed
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hl = lane >> 5;
+  const int R = a.qg * a.T;
+  const int tiles_per_grp = (R + 127) / 128;
+  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
+  const int g = grp % a.Hkv, b = grp / a.Hkv;
+  const int row0 = rt * 128;
+  const int my_row = row0 + wave * 32 + n;
+  const bool row_ok = my_row < R;
+  const int i_q = row_ok ? my_row / a.qg : 0;
+  const int h_q = g * a.qg + (row_ok ? my_row % a.qg : 0);
+  const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
+  const int n_occ = a.n_occ;
+  const float sl2 = a.sl2;
+
+  // Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T
+  bf16x8 qf[8], gf[8];
+  {
+    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) + li * D;
+    const uint16_t *grow = static_cast<const uint16_t *>(a.dout) + li * D;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      uint4 vq = make_uint4(0, 0, 0, 0), vg = make_uint4(0, 0, 0, 0);
+      if (row_ok) {
+        vq = *reinterpret_cast<const uint4 *>(qrow + 16 * st + 8 * hl);
+        vg = *reinterpret_cast<const uint4 *>(grow + 16 * st + 8 * hl);
+      }
+      qf[st] = __builtin_bit_cast(bf16x8, vq);
+      gf[st] = __builtin_bit_cast(bf16x8, vg);
+    }
+  }
+  const float Lr = row_ok ? a.l2[li] : 0.f;
+  const float Dr = row_ok ? a.dd[li] : 0.f;
+
+  const int last_row = min(R, row0 + 128) - 1;
+  const int key_end = n_occ + last_row / a.qg + 1;
+  const int ntiles = (key_end + 63) / 64;
+  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
+  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
+  const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
+  const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
+  const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
+  const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
+  // both tiles in the K/Q swizzle: read row-wise for S^T / dP^T and (K) transposed for dQ
+  auto lane_off = [&](int q) -> uint32_t {
+    const int row = (wave * 4 + q) * 4 + (lane >> 4);
+    return static_cast<uint32_t>(row * ROW_BYTES + 16 * kq_chunk_at(row, lane & 15));
+  };
+  auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs) {
+    const int j0 = tile * 64;
+    if (j0 + 64 <= n_occ) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
+    } else {
+      const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = (wave * 4 + q) * 4 + (lane >> 4);
+        const uint32_t lo = lane_off(q);
+        if (dt + row >= 0) {
+          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+        } else {
+          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+        }
+      }
+    }
+  };
+
+  const int prow = perm_key(n);
+  f32x16 dq[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) dq[k] = f32x16{};
+
+  // One 64-key tile in two halves of 32 keys (keeps one S / dP pair live).
+  auto compute = [&](int t, const char *kb, const char *vb) {
+#pragma unroll 1
+    for (int half = 0; half < 2; ++half) {
+      const int kr = 32 * half + prow;  // K / V row of the lane's operand
+      f32x16 s0 = f32x16{}, p0 = f32x16{};
+      // operands one step ahead of their MFMAs; the barriers keep the compiler
+      // from hoisting every step's reads (and their registers) to the top
+      bf16x8 k0 = lds16(kb + kq_off(kr, hl)), v0 = lds16(vb + kq_off(kr, hl));
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 nk0 = k0, nv0 = v0;
+        if (st < 7) {
+          nk0 = lds16(kb + kq_off(kr, 2 * st + 2 + hl));
+          nv0 = lds16(vb + kq_off(kr, 2 * st + 2 + hl));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        s0 = mfma32(k0, qf[st], s0);
+        p0 = mfma32(v0, gf[st], p0);
+        k0 = nk0;
+        v0 = nv0;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // register r: key t*64 + 32*half + 16*(r/8) + 8*hl + r%8 of the lane's row
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ja = t * 64 + 32 * half + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
+        const bool vis = row_ok && ja <= i_q;
+        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr)) : 0.f;
+        dsb[r >> 3][r & 7] = static_cast<__bf16>(pp * (p0[r] - Dr));
+      }
+      // dQ^T += K^T dS^T over the half's keys (k-steps 2*half, 2*half + 1)
+      bf16x8 kt = tr_operand(kb, 2 * half, 0, lane);
+#pragma unroll
+      for (int step = 0; step < 8; ++step) {
+        const int ks = step >> 2, blk = step & 3;
+        bf16x8 nkt = kt;
+        if (step < 7) nkt = tr_operand(kb, 2 * half + ((step + 1) >> 2), (step + 1) & 3, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        dq[blk] = mfma32(kt, dsb[ks], dq[blk]);
+        kt = nkt;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    issue_tile(0, kb0, kc_rs, kn_rs);
+    issue_tile(0, vb0, vc_rs, vn_rs);
+  }
+  for (int t = 0; t < ntiles; t += 2) {
+    wait_dma_and_sync();  // tile t in kb0/vb0; everybody done with kb1/vb1
+    if (t + 1 < ntiles) {
+      issue_tile(t + 1, kb1, kc_rs, kn_rs);
+      issue_tile(t + 1, vb1, vc_rs, vn_rs);
+    }
+    compute(t, kb0, vb0);
+    if (t + 1 >= ntiles) break;
+    wait_dma_and_sync();  // tile t+1 in kb1/vb1; everybody done with kb0/vb0
+    if (t + 2 < ntiles) {
+      issue_tile(t + 2, kb0, kc_rs, kn_rs);
+      issue_tile(t + 2, vb0, vc_rs, vn_rs);
+    }
+    compute(t + 1, kb1, vb1);
+  }
+
+  if (!row_ok) return;
+  float *dst = a.dq + li * D;
+#pragma unroll
+  for (int blk = 0; blk < 4; ++blk) {
+#pragma unroll
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const int d = 32 * blk + 8 * a4 + 4 * hl;
+      *reinterpret_cast<float4 *>(dst + d) =
+          make_float4(dq[blk][4 * a4] * a.scale, dq[blk][4 * a4 + 1] * a.scale,
+                      dq[blk][4 * a4 + 2] * a.scale, dq[blk][4 * a4 + 3] * a.scale);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: 128 keys per block (4 waves x 32), query rows streamed in blocks of 64
+// ---------------------------------------------------------------------------
+constexpr int BK_KEYS = 128;
+constexpr int BR_ROWS = 64;
+constexpr int RBLK_BYTES = BR_ROWS * ROW_BYTES;  // 16 KB
+
+__global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
+  __shared__ __attribute__((aligned(1024))) char qb0[RBLK_BYTES];
+  __shared__ __attribute__((aligned(1024))) char qb1[RBLK_BYTES];
+  __shared__ __attribute__((aligned(1024))) char gb0[RBLK_BYTES];
+  __shared__ __attribute__((aligned(1024))) char gb1[RBLK_BYTES];
+  __shared__ __attribute__((aligned(256))) float lb0[BR_ROWS];
+  __shared__ __attribute__((aligned(256))) float lb1[BR_ROWS];
+  __shared__ __attribute__((aligned(256))) float db0[BR_ROWS];
+  __shared__ __attribute__((aligned(256))) float db1[BR_ROWS];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 31, hl = lane >> 5;
+  const int R = a.qg * a.T;
+  const int n_occ = a.n_occ, n_keys = n_occ + a.T;
+  const int kblocks = (n_keys + BK_KEYS - 1) / BK_KEYS;
+  const int wi = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = wi / kblocks, kbk = wi % kblocks;
+  const int g = grp % a.Hkv, b = grp / a.Hkv;
+  const int j_wg = kbk * BK_KEYS;
+  const int j_base = j_wg + wave * 32;
+  const int my_key = j_base + n;
+  const bool key_ok = my_key < n_keys;
+  const int t_key = my_key - n_occ;  // chunk position of the lane's key, < 0 for a cache slot
+  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
+  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
+  const float sl2 = a.sl2;
+
+  // K and V rows of the lane's key: B operands of S = Q K^T and dP = dO V^T
+  bf16x8 kf[8], vf[8];
+  {
+    const int kk = key_ok ? my_key : 0;
+    const size_t off = kk < n_occ ? (cache_row0 + kk) * ROW_BYTES : (new_row0 + (kk - n_occ)) * ROW_BYTES;
+    const char *ks = static_cast<const char *>(kk < n_occ ? a.kc : a.kn) + off;
+    const char *vs = static_cast<const char *>(kk < n_occ ? a.vc : a.vn) + off;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(ks + 32 * st + 16 * hl));
+      vf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(vs + 32 * st + 16 * hl));
+    }
+  }
+
+  // The group's rows r = i * q_g + hh live at (hh * T + i) rows from the
+  // group's first query head (heads of a group are adjacent).
+  const size_t head0 = static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg;
+  const rsrc_t q_rs = make_rsrc(static_cast<const char *>(a.q) + head0 * a.T * ROW_BYTES, R * ROW_BYTES);
+  const rsrc_t g_rs = make_rsrc(static_cast<const char *>(a.dout) + head0 * a.T * ROW_BYTES, R * ROW_BYTES);
+  const rsrc_t l_rs = make_rsrc(a.l2 + head0 * a.T, R * 4);
+  const rsrc_t d_rs = make_rsrc(a.dd + head0 * a.T, R * 4);
+  auto src_row = [&](int r) {  // offset in rows of packed row r (clamped to the last row)
+    const int rr = r < R ? r : R - 1;
+    return (rr % a.qg) * a.T + rr / a.qg;
+  };
+  auto issue_rows = [&](int rb, char *qdst, char *gdst, float *ldst, float *ddst) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int seg = wave * 4 + q;
+      const int rib = seg * 4 + (lane >> 4);
+      const uint32_t voff =
+          static_cast<uint32_t>(src_row(rb + rib) * ROW_BYTES + 16 * kq_chunk_at(rib, lane & 15));
+      dma16(q_rs, voff, 0, qdst + seg * 1024);
+      dma16(g_rs, voff, 0, gdst + seg * 1024);
+    }
+    if (wave == 0) {
+      const uint32_t off = static_cast<uint32_t>(src_row(rb + lane) * 4);
+      dma4(l_rs, off, 0, reinterpret_cast<char *>(ldst));
+      dma4(d_rs, off, 0, reinterpret_cast<char *>(ddst));
+    }
+  };
+
+  const int r_first = j_wg >= n_occ ? (j_wg - n_occ) * a.qg : 0;  // first row any key of the block sees
+  const int rb_begin = r_first / BR_ROWS * BR_ROWS;
+  const int nrb = (R - rb_begin + BR_ROWS - 1) / BR_ROWS;
+  const int prow = perm_key(n);
+
+  f32x16 dv[4], dk[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    dv[k] = f32x16{};
+    dk[k] = f32x16{};
+  }
+
+  auto compute = [&](int rb, const char *qb, const char *gb, const float *lb, const float *db) {
+#pragma unroll 1
+    for (int sub = 0; sub < 2; ++sub) {
+      const char *qs = qb + sub * 32 * ROW_BYTES;
+      const char *gs = gb + sub * 32 * ROW_BYTES;
+      f32x16 c = f32x16{}, dp = f32x16{};
+      bf16x8 qa = lds16(qs + kq_off(prow, hl)), ga = lds16(gs + kq_off(prow, hl));
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 nqa = qa, nga = ga;
+        if (st < 7) {
+          nqa = lds16(qs + kq_off(prow, 2 * st + 2 + hl));
+          nga = lds16(gs + kq_off(prow, 2 * st + 2 + hl));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        c = mfma32(qa, kf[st], c);
+        dp = mfma32(ga, vf[st], dp);
+        qa = nqa;
+        ga = nga;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // register r: row rb + 32*sub + 16*(r/8) + 8*hl + r%8 of the lane's key
+      bf16x8 pa[2], sa[2];
+#pragma unroll
+      for (int h8 = 0; h8 < 2; ++h8) {
+        const int rib0 = 32 * sub + 16 * h8 + 8 * hl;
+        const float4 L0 = *reinterpret_cast<const float4 *>(lb + rib0);
+        const float4 L1 = *reinterpret_cast<const float4 *>(lb + rib0 + 4);
+        const float4 D0 = *reinterpret_cast<const float4 *>(db + rib0);
+        const float4 D1 = *reinterpret_cast<const float4 *>(db + rib0 + 4);
+        const float Lv[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
+        const float Dv[8] = {D0.x, D0.y, D0.z, D0.w, D1.x, D1.y, D1.z, D1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = 8 * h8 + e;
+          const int row = rb + rib0 + e;
+          const bool vis = key_ok && row < R && row >= t_key * a.qg;  // t_key < 0: every row
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(c[r], sl2, -Lv[e])) : 0.f;
+          pa[h8][e] = static_cast<__bf16>(p);
+          sa[h8][e] = static_cast<__bf16>(p * (dp[r] - Dv[e]));
+        }
+      }
+      // dV += P^T dO, dK += dS^T Q; k-step ks covers rows 16*ks .. 16*ks + 15 of the sub-block
+      bf16x8 go = tr_operand(gs, 0, 0, lane), qo = tr_operand(qs, 0, 0, lane);
+#pragma unroll
+      for (int step = 0; step < 8; ++step) {
+        const int ks = step >> 2, blk = step & 3;
+        bf16x8 ngo = go, nqo = qo;
+        if (step < 7) {
+          ngo = tr_operand(gs, (step + 1) >> 2, (step + 1) & 3, lane);
+          nqo = tr_operand(qs, (step + 1) >> 2, (step + 1) & 3, lane);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dv[blk] = mfma32(pa[ks], go, dv[blk]);
+        dk[blk] = mfma32(sa[ks], qo, dk[blk]);
+        go = ngo;
+        qo = nqo;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  issue_rows(rb_begin, qb0, gb0, lb0, db0);
+  for (int it = 0; it < nrb; it += 2) {
+    const int rb = rb_begin + it * BR_ROWS;
+    wait_dma_and_sync();  // block it in the 0 buffers; everybody done with the 1 buffers
+    if (it + 1 < nrb) issue_rows(rb + BR_ROWS, qb1, gb1, lb1, db1);
+    compute(rb, qb0, gb0, lb0, db0);
+    if (it + 1 >= nrb) break;
+    wait_dma_and_sync();
+    if (it + 2 < nrb) issue_rows(rb + 2 * BR_ROWS, qb0, gb0, lb0, db0);
+    compute(rb + BR_ROWS, qb1, gb1, lb1, db1);
+  }
+
+  // output register r of block blk: key j_base + 8*(r/4) + 4*hl + r%4, d = 32*blk + n
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int kk = j_base + 8 * (r >> 2) + 4 * hl + (r & 3);
+    if (kk >= n_keys) continue;
+    float *dkrow, *dvrow;
+    if (kk < n_occ) {
+      dkrow = a.dkc + (cache_row0 + kk) * D;
+      dvrow = a.dvc + (cache_row0 + kk) * D;
+    } else {
+      dkrow = a.dkn + (new_row0 + (kk - n_occ)) * D;
+      dvrow = a.dvn + (new_row0 + (kk - n_occ)) * D;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      dkrow[32 * blk + n] = dk[blk][r] * a.scale;
+      dvrow[32 * blk + n] = dv[blk][r];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t s) {
+  const int groups = a.B * a.Hkv;
+  const int R = a.qg * a.T;
+  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+  {
+    KernelTimer timer(H2O_K_BWD_ROWS, s);
+    hipLaunchKernelGGL(bwd_rows, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, a);
+  }
+  {
+    KernelTimer timer(H2O_K_BWD_DQ, s);
+    hipLaunchKernelGGL(bwd_dq, dim3(groups * ((R + 127) / 128)), dim3(256), 0, s, a);
+  }
+  {
+    KernelTimer timer(H2O_K_BWD_DKDV, s);
+    const int n_keys = a.n_occ + a.T;
+    hipLaunchKernelGGL(bwd_dkdv, dim3(groups * ((n_keys + BK_KEYS - 1) / BK_KEYS)), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace h2o

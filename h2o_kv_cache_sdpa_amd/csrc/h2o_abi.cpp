@@ -268,6 +268,55 @@ int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
                                     ws ? ws_bytes : 0, static_cast<hipStream_t>(stream)));
 }
 
+int h2o_sdpa_backward(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
+                      const void *k_new, const void *v_new, const void *out, const float *lse,
+                      const void *dout, float *dq, float *dk_cache, float *dv_cache, float *dk_new,
+                      float *dv_new, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (d->dtype != H2O_BF16 || d->cache_fmt != H2O_CACHE_NATIVE || d->D != 128) return H2O_EUNSUPPORTED;
+  if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
+  const void *need[] = {q, k_new, v_new, out, lse, dout, dq, dk_new, dv_new};
+  for (const void *p : need)
+    if (!p || !aligned16(p)) return H2O_EINVAL;
+  if (n_occ > 0) {
+    if (!dk_cache || !dv_cache || !aligned16(dk_cache) || !aligned16(dv_cache)) return H2O_EINVAL;
+    st = check_cache_buffers(d, cache);
+    if (st != H2O_OK) return st;
+  }
+  if (!ws || !aligned16(ws) || ws_bytes < lse_bytes(d)) return H2O_EWORKSPACE;
+  h2o::BwdArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.q = q;
+  a.kn = k_new;
+  a.vn = v_new;
+  if (cache) {
+    a.kc = cache->k;
+    a.vc = cache->v;
+  }
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  const size_t rows = static_cast<size_t>(d->B) * d->Hq * d->T;
+  a.l2 = static_cast<float *>(ws);
+  a.dd = a.l2 + rows;
+  a.dq = dq;
+  a.dkc = dk_cache;
+  a.dvc = dv_cache;
+  a.dkn = dk_new;
+  a.dvn = dv_new;
+  a.B = d->B;
+  a.Hq = d->Hq;
+  a.Hkv = d->Hkv;
+  a.C = d->C;
+  a.T = d->T;
+  a.qg = d->Hq / d->Hkv;
+  a.n_occ = n_occ;
+  a.scale = softmax_scale(d);
+  a.sl2 = static_cast<float>(static_cast<double>(a.scale) * 1.4426950408889634074);
+  return from_hip(h2o::launch_attn_backward(a, static_cast<hipStream_t>(stream)));
+}
+
 int kv_scatter(const h2o_dims *d, h2o_cache *cache, const void *k_new, const void *v_new,
                const int32_t *slot_log, void *stream) {
   const int st = check_write(d, cache, k_new, v_new, slot_log);

@@ -59,6 +59,19 @@ struct KvWriteArgs {
   int dtype, cache_fmt;
 };
 
+// Backward of the chunk attention (bf16, native cache, D = 128).
+struct BwdArgs {
+  const void *q, *kn, *vn, *kc, *vc, *out, *dout;
+  const float *lse;  // (B,Hq,T) natural-log row normalisers of the forward
+  float *l2, *dd;    // workspace (B,Hq,T): lse * log2(e), rowsum(dout * out)
+  float *dq;         // (B,Hq,T,D)
+  float *dkc, *dvc;  // (B,Hkv,C,D), rows < n_occ
+  float *dkn, *dvn;  // (B,Hkv,T,D)
+  int B, Hq, Hkv, C, T, qg, n_occ;
+  float scale, sl2;
+};
+hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t s);
+
 // Brackets one kernel launch with hipEvents on `s` while timing is enabled
 // (h2o_profile_enable); kind is an enum h2o_kernel_kind value.
 class KernelTimer {

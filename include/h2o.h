@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define H2O_ABI_VERSION 2
+#define H2O_ABI_VERSION 3
 
 /* Status codes. */
 enum h2o_status {
@@ -203,6 +203,37 @@ int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t 
                     const void *q, const void *k_new, const void *v_new, void *out,
                     const int32_t *slot_log, void *ws, size_t ws_bytes, void *stream);
 
+/* Gradients of the chunk attention ("Learning how to Forget", §3.2: the
+ * fine-tuning pass differentiates each chunk's SDPA call by reverse mode;
+ * §A.10: the attention interface with summed weights has a backward).  For
+ * the attention of h2o_sdpa_scoresum with the same d, cache, n_occ and chunk,
+ * and an upstream gradient dout = dL/d(out):
+ *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
+ *   dS = P o (dout V^T - rowsum(dout o out)),
+ * with P the masked softmax (cache slots visible, chunk keys causal) and the
+ * keys K, V = the n_occ cache rows followed by the chunk's.  dk and dv of a KV
+ * head are summed over its q_g query heads.  The summed weights carry no
+ * gradient.  P is recomputed from lse; P and dS enter the products as bf16,
+ * all sums are fp32.
+ *   q, k_new, v_new, cache   as for h2o_sdpa_scoresum (read only)
+ *   out    (B,Hq,T,D) bf16: the forward's output
+ *   lse    (B,Hq,T) fp32: the forward's natural-log row normalisers (the lse
+ *          output of h2o_sdpa_scoresum)
+ *   dout   (B,Hq,T,D) bf16
+ *   dq     (B,Hq,T,D) fp32, written
+ *   dk_cache, dv_cache  (B,Hkv,C,D) fp32: rows < n_occ written, the rest
+ *          untouched (may be NULL when n_occ == 0)
+ *   dk_new, dv_new      (B,Hkv,T,D) fp32, written
+ *   ws     at least h2o_workspace_bytes(d) bytes (16-byte aligned)
+ * Supported: dtype H2O_BF16, cache_fmt H2O_CACHE_NATIVE, D = 128; otherwise
+ * H2O_EUNSUPPORTED.  Null or misaligned buffers: H2O_EINVAL.  Deterministic
+ * (no atomics). */
+int h2o_sdpa_backward(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ,
+                      const void *q, const void *k_new, const void *v_new,
+                      const void *out, const float *lse, const void *dout,
+                      float *dq, float *dk_cache, float *dv_cache, float *dk_new, float *dv_new,
+                      void *ws, size_t ws_bytes, void *stream);
+
 /* Kernel timing, for measurement.  While enabled, every kernel the library
  * launches is bracketed by two hipEvents recorded on the caller's stream (the
  * events come from a pool the library owns; no device memory is allocated).
@@ -215,7 +246,10 @@ enum h2o_kernel_kind {
   H2O_K_EVICT = 2,    /* score update, selection, replay log */
   H2O_K_KV_WRITE = 3, /* slot overwrite / quantise */
   H2O_K_ATTN_COMBINE = 4, /* merge of key-split partial outputs (small chunks) */
-  H2O_K_COUNT = 5
+  H2O_K_BWD_ROWS = 5, /* backward: row normalisers and rowsum(dout o out) */
+  H2O_K_BWD_DQ = 6,   /* backward: dq */
+  H2O_K_BWD_DKDV = 7, /* backward: dk, dv */
+  H2O_K_COUNT = 8
 };
 int h2o_profile_enable(int on);
 int h2o_profile_read(double *total_ms, int64_t *launches, int n);

@@ -541,3 +541,14 @@ def test_backward_closed_forms():
     dq, dkc, _, dkn, _ = O.attend_backward(q, kc, vc, n_occ, kn, vn, 0.4, dout)
     for g in (dq, dkc, dkn):
         assert np.abs(g).max() < 1e-12
+
+
+def test_backward_with_exact_output_equals_definition():
+    """Passing the exact forward output as the stored output changes nothing."""
+    B, Hq, Hkv, D, n_occ, T = 1, 4, 2, 6, 11, 5
+    q, kc, vc, kn, vn, dout = _bwd_case(65, B, Hq, Hkv, D, n_occ, T)
+    out, _, _ = O.attend_chunk(q, kc, vc, n_occ, kn, vn, 0.3)
+    a = O.attend_backward(q, kc, vc, n_occ, kn, vn, 0.3, dout)
+    b = O.attend_backward(q, kc, vc, n_occ, kn, vn, 0.3, dout, out=out)
+    for x, y in zip(a, b):
+        np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-13)
