@@ -682,7 +682,7 @@ hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
     e = hipGetLastError();
   }
   if (e != hipSuccess) return e;
-  if (a.nsplit > 1) {
+  if (a.nsplit > 1 && !a.lg) {  // with stored logits the weight-sum kernel merges the splits
     e = launch_attn_combine(a, s);
     if (e != hipSuccess) return e;
   }

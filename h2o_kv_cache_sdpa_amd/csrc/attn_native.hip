@@ -635,15 +635,101 @@ __global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // xs: factor that brings a stored logit to log2 units (sl2 for native caches,
 // whose pass A stores q.k; 1 for 8/4-bit caches, whose factors include sl2).
+// With key-split partials (nsplit > 1) the kernel also does the split
+// combine: every block forms its group's row normalisers from the partial
+// (m, l) pairs, and block x < R of a group merges output row x (the
+// attn_combine arithmetic for that row), so no separate combine runs.
 __global__ __launch_bounds__(256) void attn_b_logits(AttnArgs a, float xs) {
-  __shared__ float Ls[LOGIT_ROWS_MAX];
+  __shared__ float Ls[LOGIT_ROWS_MAX], Ms[LOGIT_ROWS_MAX], Ws[LOGIT_ROWS_MAX];
+  __shared__ float4 red_o[8][32];
   const int grp = blockIdx.y, g = grp % a.Hkv, b = grp / a.Hkv;
   const int R = a.qg * a.T;
-  if (threadIdx.x < R) {
-    const int r = threadIdx.x, i = r / a.qg, hh = r % a.qg;
-    Ls[r] = a.lse2[(static_cast<size_t>(b) * a.Hq + g * a.qg + hh) * a.T + i];
+  const int tid = threadIdx.x;
+  auto row_index = [&](int r) {
+    return (static_cast<size_t>(b) * a.Hq + g * a.qg + r % a.qg) * a.T + r / a.qg;
+  };
+  if (a.nsplit > 1) {
+    // 16 lanes per row, lane s takes splits s, s + 16, s + 32, s + 48 (nsplit
+    // <= 64), all loads issued before use; max, then the rescaled sum
+    const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+    const int r = tid >> 4, sl = tid & 15;
+    float2 ml[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sp = sl + 16 * k;
+      ml[k] = (r < R && sp < a.nsplit)
+                  ? *reinterpret_cast<const float2 *>(a.part_ml + 2 * (sp * rows + row_index(r)))
+                  : make_float2(-INFINITY, 0.f);
+    }
+    float m = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    float l = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (ml[k].x != -INFINITY) l = fmaf(ml[k].y, __builtin_amdgcn_exp2f(ml[k].x - m), l);
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    if (r < R && sl == 0) {
+      Ms[r] = m;
+      Ws[r] = l;
+      Ls[r] = m + log2f(l);
+    }
+  } else if (tid < R) {
+    Ls[tid] = a.lse2[row_index(tid)];
   }
   __syncthreads();
+  if (a.nsplit > 1 && static_cast<int>(blockIdx.x) < R) {
+    // output row x: sum_s 2^(m_s - M) O_s / l; 8 groups of 32 lanes (4
+    // components each), group k takes splits k, k + 8, ... (at most 8 each),
+    // loads first, groups added in order
+    const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+    const int r = blockIdx.x, grp8 = tid >> 5, c4 = tid & 31;
+    const size_t li = row_index(r);
+    float ms[8];
+    float4 po[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int sp = grp8 + 8 * k;
+      ms[k] = -INFINITY;
+      po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (sp < a.nsplit) {
+        const size_t pr = sp * rows + li;
+        ms[k] = a.part_ml[2 * pr];
+        po[k] = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c4);
+      }
+    }
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (ms[k] == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ms[k] - Ms[r]);
+      acc.x = fmaf(po[k].x, w, acc.x);
+      acc.y = fmaf(po[k].y, w, acc.y);
+      acc.z = fmaf(po[k].z, w, acc.z);
+      acc.w = fmaf(po[k].w, w, acc.w);
+    }
+    red_o[grp8][c4] = acc;
+    __syncthreads();
+    if (grp8 == 0) {
+      float4 t = red_o[0][c4];
+#pragma unroll
+      for (int k = 1; k < 8; ++k) {
+        const float4 u = red_o[k][c4];
+        t.x += u.x;
+        t.y += u.y;
+        t.z += u.z;
+        t.w += u.w;
+      }
+      const float inv = 1.f / Ws[r];
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + li * D + 4 * c4) =
+          make_uint2(pack_bf16_rne(t.x * inv, t.y * inv), pack_bf16_rne(t.z * inv, t.w * inv));
+      if (c4 == 0) {
+        a.lse2[li] = Ls[r];
+        if (a.lse_nat) a.lse_nat[li] = Ls[r] * 0.69314718055994530942f;
+      }
+    }
+  }
   const int n_keys = a.n_occ + a.T;
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= n_keys) return;
@@ -1012,7 +1098,8 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.nsplit > 1) {
+  // with stored logits the weight-sum kernel also merges the key splits
+  if (a.nsplit > 1 && !a.lg) {
     e = launch_attn_combine(a, s);
     if (e != hipSuccess) return e;
   }
@@ -1023,9 +1110,11 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
 
 hipError_t launch_attn_b_logits(const AttnArgs &a, hipStream_t s) {
   const int n_keys = a.n_occ + a.T;
+  // grid.x >= R, so that the blocks merging the split rows exist
+  const int nx = std::max((n_keys + 255) / 256, a.qg * a.T);
   KernelTimer timer(H2O_K_ATTN_B, s);
   const float xs = a.cache_fmt == FMT_NATIVE ? a.sl2 : 1.f;
-  hipLaunchKernelGGL(attn_b_logits, dim3((n_keys + 255) / 256, a.B * a.Hkv), dim3(256), 0, s, a, xs);
+  hipLaunchKernelGGL(attn_b_logits, dim3(nx, a.B * a.Hkv), dim3(256), 0, s, a, xs);
   return hipGetLastError();
 }
 
