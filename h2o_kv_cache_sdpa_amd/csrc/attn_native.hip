@@ -57,8 +57,11 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
 // ---------------------------------------------------------------------------
 
 // LG: also store the raw logits of every tile (short chunks; a.lg).
-template <bool LG>
-__global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
+// NW: wavefronts per block (4 or 8), 32 rows each; a K/V tile serves them all.
+template <bool LG, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
+  constexpr int ROWS = 32 * NW;  // packed rows per block
+  constexpr int SPW = 16 / NW;   // 1 KB DMA segments of a 16 KB tile per wavefront
   __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
@@ -67,13 +70,13 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hl = lane >> 5;
   const int R = a.qg * a.T;
-  const int tiles_per_grp = (R + 127) / 128;
+  const int tiles_per_grp = (R + ROWS - 1) / ROWS;
   const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
   const int split = wi_all % a.nsplit;  // key split of this block (0 when unsplit)
   const int wi = wi_all / a.nsplit;
   const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
-  const int row0 = rt * 128;
+  const int row0 = rt * ROWS;
   const int wrow0 = row0 + wave * 32;
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < R;
@@ -97,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
     }
   }
 
-  const int last_row = min(R, row0 + 128) - 1;
+  const int last_row = min(R, row0 + ROWS) - 1;
   const int key_end = n_occ + last_row / a.qg + 1;
   // key tiles t_lo .. t_lo + ntiles - 1 of the block's range (all of it when unsplit)
   const int ntiles_all = (key_end + 63) / 64;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
   const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
   const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
   auto lane_off = [&](int q, bool is_v) -> uint32_t {
-    const int row = (wave * 4 + q) * 4 + (lane >> 4);
+    const int row = (wave * SPW + q) * 4 + (lane >> 4);
     const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
     return static_cast<uint32_t>(row * ROW_BYTES + 16 * c);
   };
@@ -124,18 +127,18 @@ __global__ __launch_bounds__(256, 2) void attn_a_native(AttnArgs a) {
     const int j0 = (t_lo + tile) * 64;
     if (j0 + 64 <= n_occ) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
+      for (int q = 0; q < SPW; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * SPW + q) * 1024);
     } else {
       // chunk rows (and, in the one tile that straddles n_occ, cache rows)
       const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = (wave * 4 + q) * 4 + (lane >> 4);
+      for (int q = 0; q < SPW; ++q) {
+        const int row = (wave * SPW + q) * 4 + (lane >> 4);
         const uint32_t lo = lane_off(q, is_v);
         if (dt + row >= 0) {
-          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * SPW + q) * 1024);
         } else {
-          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * SPW + q) * 1024);
         }
       }
     }
@@ -1090,10 +1093,13 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
       } else {
         hipLaunchKernelGGL(attn_a_dec<false>, dim3(nD), dim3(256), 0, s, a);
       }
+    } else if (R >= 256 && !a.lg) {  // long chunks: 256 rows per block share each tile
+      const int n8 = groups * ((R + 255) / 256) * a.nsplit;
+      hipLaunchKernelGGL((attn_a_native<false, 8>), dim3(n8), dim3(512), 0, s, a);
     } else if (a.lg) {
-      hipLaunchKernelGGL(attn_a_native<true>, dim3(nA), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_a_native<true, 4>), dim3(nA), dim3(256), 0, s, a);
     } else {
-      hipLaunchKernelGGL(attn_a_native<false>, dim3(nA), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_a_native<false, 4>), dim3(nA), dim3(256), 0, s, a);
     }
   }
   hipError_t e = hipGetLastError();
