@@ -425,6 +425,290 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Short chunks (at most 16 packed rows per KV group): the same codes pipeline,
+// but each wavefront takes 16 keys of every tile on 16x16 MFMAs, as the native
+// short-chunk pass does; the four wavefronts merge at the end.
+// ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int FMT, bool LG>
+__global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
+  using Q = QTile<FMT>;
+  __shared__ __attribute__((aligned(1024))) char kb[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kc0[Q::CODE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vc0[Q::CODE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kc1[Q::CODE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vc1[Q::CODE_BYTES];
+  __shared__ __attribute__((aligned(256))) uint16_t fc0[Q::NFAC][64];
+  __shared__ __attribute__((aligned(256))) uint16_t fc1[Q::NFAC][64];
+  __shared__ __attribute__((aligned(256))) float fac[4][64];
+  __shared__ float red_m[4][16], red_l[4][16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g4 = lane >> 4;  // row of the lane; key / d group
+  const int R = a.qg * a.T;                 // <= 16
+  const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = wi_all % a.nsplit;
+  const int grp = wi_all / a.nsplit;
+  const int g = grp % a.Hkv, b = grp / a.Hkv;
+  const bool row_ok = n < R;
+  const int i_q = row_ok ? n / a.qg : 0;
+  const int h_q = g * a.qg + (row_ok ? n % a.qg : 0);
+  const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
+  const int n_occ = a.n_occ;
+
+  bf16x8 qf[4];
+  float qsum = 0.f;
+  {
+    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) + li * D;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (row_ok) v = *reinterpret_cast<const uint4 *>(qrow + 32 * st + 8 * g4);
+      qf[st] = __builtin_bit_cast(bf16x8, v);
+      if constexpr (FMT == FMT_INT4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qsum += static_cast<float>(qf[st][e]);
+      }
+    }
+    if constexpr (FMT == FMT_INT4) {
+      qsum += __shfl_xor(qsum, 16);
+      qsum += __shfl_xor(qsum, 32);
+      // per-row sum of q for the weight pass of int4 caches (second lse plane)
+      if (split == 0 && wave == 0 && g4 == 0 && row_ok)
+        a.lse2[static_cast<size_t>(a.B) * a.Hq * a.T + li] = qsum;
+    }
+  }
+
+  const int key_end = n_occ + (R - 1) / a.qg + 1;
+  const int ntiles_all = (key_end + 63) / 64;
+  const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
+  const int t_lo = split * per_split;
+  const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;
+  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
+  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
+  const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * Q::CODE_ROW,
+                                 n_occ * Q::CODE_ROW);
+  const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * Q::CODE_ROW,
+                                 n_occ * Q::CODE_ROW);
+  const uint16_t *fsrc[4] = {a.ks, a.vs, a.kz, a.vz};
+  // as in attn_a_quant: the tile that straddles n_occ reads through resources
+  // that end at n_occ
+  auto issue_codes = [&](int tile, char *kdst, char *vdst, uint16_t (*fdst)[64]) {
+    const int j0 = (t_lo + tile) * 64;
+    if (j0 >= n_occ) return;
+    const bool whole = j0 + 64 <= n_occ;
+    const uint32_t rows_left = static_cast<uint32_t>(n_occ - j0);
+    const rsrc_t kr = whole ? kc_rs
+                            : make_rsrc(static_cast<const char *>(a.kc) + (cache_row0 + j0) * Q::CODE_ROW,
+                                        rows_left * Q::CODE_ROW);
+    const rsrc_t vr = whole ? vc_rs
+                            : make_rsrc(static_cast<const char *>(a.vc) + (cache_row0 + j0) * Q::CODE_ROW,
+                                        rows_left * Q::CODE_ROW);
+    const uint32_t soff = whole ? static_cast<uint32_t>(j0 * Q::CODE_ROW) : 0u;
+    for (int sgm = wave; sgm < Q::SEGS; sgm += 4) {
+      const uint32_t off = static_cast<uint32_t>(sgm * 1024 + 16 * lane);
+      dma16(kr, off, soff, kdst + sgm * 1024);
+      dma16(vr, off, soff, vdst + sgm * 1024);
+    }
+    if (wave < Q::NFAC && lane < 32) {
+      const rsrc_t fr = make_rsrc(fsrc[wave] + cache_row0 + j0, rows_left * 2);
+      dma4(fr, 4 * lane, 0, reinterpret_cast<char *>(fdst[wave]));
+    }
+  };
+  const int crow = tid >> 2, cq = tid & 3;
+  auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64]) {
+    const int j0 = (t_lo + tile) * 64;
+    const int j = j0 + crow;
+    uint4 kw[4], vw[4];
+    if (j < n_occ) {
+      widen32<FMT>(kcs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), kw);
+      widen32<FMT>(vcs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), vw);
+    } else {
+      const int t = j - n_occ;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kw[i] = vw[i] = make_uint4(0, 0, 0, 0);
+        if (t < a.T) {
+          const size_t e = (new_row0 + t) * D + 32 * cq + 8 * i;
+          kw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.kn) + e);
+          vw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.vn) + e);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4 *>(kb + kq_off(crow, 4 * cq + i)) = kw[i];
+      *reinterpret_cast<uint4 *>(vb + v_off(crow, 4 * cq + i)) = vw[i];
+    }
+    if (tid < 64) {
+      const bool cached = j0 + tid < n_occ;
+      fac[0][tid] = cached ? f16_to_f32(fcs[0][tid]) * a.sl2 : a.sl2;
+      fac[2][tid] = cached ? f16_to_f32(fcs[1][tid]) : 1.f;
+      if constexpr (FMT == FMT_INT4) {
+        fac[1][tid] = cached ? f16_to_f32(fcs[2][tid]) * a.sl2 : 0.f;
+        fac[3][tid] = cached ? f16_to_f32(fcs[3][tid]) : 0.f;
+      }
+    }
+  };
+
+  f32x4 o[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o[k] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f, u_run = 0.f;
+  const int krow = 16 * wave + n;
+  const int kk0 = 16 * wave + 4 * g4;  // tile key of the lane's first value
+
+  auto compute = [&](int tile) {
+    const int j0 = (t_lo + tile) * 64;
+    f32x4 c = f32x4{};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(kb + kq_off(krow, 4 * st + g4)), qf[st], c, 0, 0, 0);
+    // c[i]: tile key kk0 + i of row n; factors bring it to log2 units
+    const float4 s4 = *reinterpret_cast<const float4 *>(&fac[0][kk0]);
+    const float sk[4] = {s4.x, s4.y, s4.z, s4.w};
+    float zk[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (FMT == FMT_INT4) {
+      const float4 z4 = *reinterpret_cast<const float4 *>(&fac[1][kk0]);
+      zk[0] = z4.x;
+      zk[1] = z4.y;
+      zk[2] = z4.z;
+      zk[3] = z4.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = (FMT == FMT_INT4) ? fmaf(c[i], sk[i], zk[i] * qsum) : c[i] * sk[i];
+    if constexpr (LG) {
+      if (row_ok)
+        *reinterpret_cast<float4 *>(a.lg + (static_cast<size_t>(grp) * R + n) * a.lg_stride + j0 + kk0) =
+            make_float4(c[0], c[1], c[2], c[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ja = j0 + kk0 + i - n_occ;
+      c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (mx > m_run + RESCALE_SLACK) {
+      const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mx);
+      l_run *= alpha;
+      u_run *= alpha;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k] *= alpha;
+      m_run = mx;
+    }
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
+    const float4 v4 = *reinterpret_cast<const float4 *>(&fac[2][kk0]);
+    const float sv[4] = {v4.x, v4.y, v4.z, v4.w};
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(c[i] + neg_m);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    if constexpr (FMT == FMT_INT4) {
+      const float4 w4 = *reinterpret_cast<const float4 *>(&fac[3][kk0]);
+      u_run = fmaf(p[0], w4.x, fmaf(p[1], w4.y, fmaf(p[2], w4.z, fmaf(p[3], w4.w, u_run))));
+    }
+    const i16x4 pb = __builtin_bit_cast(
+        i16x4, make_uint2(pack_bf16_rne(p[0] * sv[0], p[1] * sv[1]), pack_bf16_rne(p[2] * sv[2], p[3] * sv[3])));
+    const int vrow = 16 * wave + 4 * g4 + (n >> 2);
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk) {
+      const int col = 16 * dblk + 4 * (n & 3);
+      const i16x4 va = lds_tr(vb + v_off(vrow, col >> 3) + 2 * (col & 7));
+      o[dblk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dblk], 0, 0, 0);
+    }
+  };
+
+  if (ntiles > 0) issue_codes(0, kc0, vc0, fc0);
+  for (int t = 0; t < ntiles; t += 2) {
+    wait_dma_and_sync();
+    if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
+    widen_tile(t, kc0, vc0, fc0);
+    lds_barrier();
+    compute(t);
+    if (t + 1 >= ntiles) break;
+    wait_dma_and_sync();
+    if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
+    widen_tile(t + 1, kc1, vc1, fc1);
+    lds_barrier();
+    compute(t + 1);
+  }
+
+  // ---- merge the four wavefronts (u: the zero-point term, the same for every d) ----
+  float l_w = l_run + __shfl_xor(l_run, 16);
+  l_w += __shfl_xor(l_w, 32);
+  float u_w = u_run + __shfl_xor(u_run, 16);
+  u_w += __shfl_xor(u_w, 32);
+  if (g4 == 0) {
+    red_m[wave][n] = m_run;
+    red_l[wave][n] = l_w;
+  }
+  __syncthreads();  // also: every wavefront is done with the tiles
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][n]);
+  const float my_scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
+  auto red_o = [&](int w) { return reinterpret_cast<float *>(w < 2 ? kb : vb) + (w & 1) * 16 * D; };
+  {
+    float *mine = red_o(wave);
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk)
+      *reinterpret_cast<float4 *>(mine + n * D + 16 * dblk + 4 * g4) =
+          make_float4((o[dblk][0] + u_w) * my_scale, (o[dblk][1] + u_w) * my_scale,
+                      (o[dblk][2] + u_w) * my_scale, (o[dblk][3] + u_w) * my_scale);
+  }
+  __syncthreads();
+  const int rr = tid >> 4, d0 = 8 * (tid & 15);
+  if (rr >= R) return;
+  const int ri = rr / a.qg, rh = g * a.qg + rr % a.qg;
+  const size_t lr = (static_cast<size_t>(b) * a.Hq + rh) * a.T + ri;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+#pragma unroll
+    for (int e4 = 0; e4 < 2; ++e4) {
+      const float4 v = *reinterpret_cast<const float4 *>(red_o(w) + rr * D + d0 + 4 * e4);
+      acc[4 * e4] += v.x;
+      acc[4 * e4 + 1] += v.y;
+      acc[4 * e4 + 2] += v.z;
+      acc[4 * e4 + 3] += v.w;
+    }
+  }
+  float Mr = -INFINITY, lr_tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, red_m[w][rr]);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float mw = red_m[w][rr];
+    lr_tot += (mw == -INFINITY) ? 0.f : red_l[w][rr] * __builtin_amdgcn_exp2f(mw - Mr);
+  }
+  const size_t plane = static_cast<size_t>(a.B) * a.Hq * a.T;
+  if (a.nsplit > 1) {
+    const size_t pr = static_cast<size_t>(split) * plane + lr;
+    float *po = a.part + pr * D + d0;
+    *reinterpret_cast<float4 *>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *reinterpret_cast<float4 *>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    if (d0 == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * pr) = make_float2(Mr, lr_tot);
+    return;
+  }
+  const float inv = 1.f / lr_tot;
+  uint16_t *orow = static_cast<uint16_t *>(a.out) + lr * D + d0;
+  *reinterpret_cast<uint4 *>(orow) =
+      make_uint4(pack_bf16_rne(acc[0] * inv, acc[1] * inv), pack_bf16_rne(acc[2] * inv, acc[3] * inv),
+                 pack_bf16_rne(acc[4] * inv, acc[5] * inv), pack_bf16_rne(acc[6] * inv, acc[7] * inv));
+  if (d0 == 0) {
+    const float L = Mr + log2f(lr_tot);
+    a.lse2[lr] = L;
+    if (a.lse_nat) a.lse_nat[lr] = L * 0.69314718055994530942f;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s) {
@@ -432,6 +716,21 @@ hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s) {
   const int R = a.qg * a.T;
   const int nA = groups * ((R + 127) / 128) * a.nsplit;
   KernelTimer timer(H2O_K_ATTN_A, s);
+  if (R <= 16) {  // short chunks: 16 keys of each tile per wavefront
+    const int nD = groups * a.nsplit;
+    if (a.cache_fmt == FMT_INT8) {
+      if (a.lg) {
+        hipLaunchKernelGGL((attn_a_qdec<FMT_INT8, true>), dim3(nD), dim3(256), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((attn_a_qdec<FMT_INT8, false>), dim3(nD), dim3(256), 0, s, a);
+      }
+    } else if (a.lg) {
+      hipLaunchKernelGGL((attn_a_qdec<FMT_INT4, true>), dim3(nD), dim3(256), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_a_qdec<FMT_INT4, false>), dim3(nD), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (a.cache_fmt == FMT_INT8) {
     if (a.lg) {
       hipLaunchKernelGGL((attn_a_quant<FMT_INT8, true>), dim3(nA), dim3(256), 0, s, a);
