@@ -229,3 +229,40 @@ def test_full_step_cfg4():
 
 def test_full_step_cfg5():
     _full_step(W.WORKLOADS[5], [(0, 0), (3, 7)])
+
+
+# short chunks on the full 32K-slot cache, in the launch configuration the
+# small-T sweep times (key-split short-chunk pass A, stored logits with the
+# folded combine, two-pass slot selection): every KV group recomputed
+
+@pytest.mark.parametrize("fmt,T", [("native", 1), ("native", 4), ("native", 16), ("int8", 1), ("int4", 4)])
+def test_full_step_short_chunks(fmt, T):
+    w = W.WORKLOADS[3].scaled(T=T, cache_fmt=fmt, name=f"short_{fmt}_32k_t{T}")
+    _full_step(w, [(0, g) for g in range(w.Hkv)])
+
+
+def test_prefill_square_8k():
+    """First chunk on an empty cache: n_occ = 0, T = C = 8192 (a causal square
+    with summed weights); one KV group recomputed completely, the fill log and
+    the per-group invariant sum(w) = T*q_g everywhere."""
+    w = W.WORKLOADS[3].scaled(C=8192, T=8192, name="prefill_8k")
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+    qg = w.qg
+    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype="bf16", cache_fmt="native", device=DEV)
+    ch = W.chunk(w, 0)
+    out, wsum, slots = gc.step(to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"]))
+    torch.cuda.synchronize()
+    wsum_np = wsum.cpu().numpy()
+    np.testing.assert_allclose(wsum_np.astype(np.float64).sum(-1), T * qg, rtol=1e-4)
+    assert (slots.cpu().numpy() == np.arange(T)).all(), "fill log"
+    g = 3
+    sl = slice(g * qg, (g + 1) * qg)
+    empty = np.zeros((1, 1, 0, D))
+    ref_o, ref_w, _ = O.attend_chunk(ch["q"].f64[:, sl], empty, empty, 0, ch["k"].f64[:, g:g + 1],
+                                     ch["v"].f64[:, g:g + 1], float(np.float32(1 / np.sqrt(D))))
+    check_out(out[:, sl], ref_o, "bf16", "prefill out")
+    check_rel(wsum_np[:, g:g + 1], ref_w, T, qg, "prefill wsum")
+    # the cache now holds the chunk and its own sums
+    np.testing.assert_array_equal(gc.k[:, g].cpu().view(torch.int16).numpy(),
+                                  np.ascontiguousarray(ch["k"].raw[:, g]).view(np.int16))
+    np.testing.assert_array_equal(gc.scores[:, g].cpu().numpy(), wsum_np[:, g])
