@@ -761,6 +761,7 @@ __global__ __launch_bounds__(256) void attn_b_logits(AttnArgs a, float xs) {
 
 constexpr int PB_KEYS = 256;
 constexpr int PB_ROWS = 128;
+constexpr int SLICE_KEYS = 32;  // chunk keys folded into one key block
 constexpr int QBLK_BYTES = PB_ROWS * ROW_BYTES;  // 32 KB
 
 // 8 codes of one key row (int8: 8 bytes, int4: 4 bytes with element 2k in the
@@ -793,10 +794,21 @@ __device__ __forceinline__ bf16x8 widen8(const char *codes) {
 
 // FMT: cache format.  For 8/4-bit caches the K operands are the widened codes
 // and the per-key factors enter the exponent: x = s_j*sl2*acc (+ z_j*sl2*sum(q_i)) - L_i.
-template <int FMT>
+//
+// SL (folded chunk keys): blocks are launched only for the key blocks that
+// start below n_occ, which see every query row.  The keys past them (chunk
+// keys only, visible to a shrinking suffix of the rows) would otherwise form a
+// few extra blocks that run as a nearly empty last wave of the grid; instead
+// they are cut into 32-key slices and block k also sums slice k: wavefront w
+// takes 32-row sub-block w of every row block against the slice's keys, which
+// sit in LDS for the whole block, and the four partial column sums are added
+// in a fixed order at the end.
+template <int FMT, bool SL>
 __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char qb0[QBLK_BYTES];
   __shared__ __attribute__((aligned(1024))) char qb1[QBLK_BYTES];
+  __shared__ __attribute__((aligned(1024))) char sk[SL ? SLICE_KEYS * ROW_BYTES : 16];
+  __shared__ float sred[SL ? 4 * SLICE_KEYS : 1];
   __shared__ __attribute__((aligned(512))) float lb0[PB_ROWS];
   __shared__ __attribute__((aligned(512))) float lb1[PB_ROWS];
   // int4: per-row sum(q) beside the normalisers
@@ -808,7 +820,8 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   const int n_occ = a.n_occ;
   const int n_keys = n_occ + a.T;
   const int R = a.qg * a.T;
-  const int kblocks = (n_keys + PB_KEYS - 1) / PB_KEYS;
+  const int n_main = (n_occ + PB_KEYS - 1) / PB_KEYS;  // key blocks starting below n_occ
+  const int kblocks = SL ? n_main : (n_keys + PB_KEYS - 1) / PB_KEYS;
   const int wi = xcd_remap(blockIdx.x, gridDim.x);
   const int grp = wi / kblocks, kbk = wi % kblocks;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
@@ -851,6 +864,24 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     load_key(key0, kf0, ksl0, kzl0);
     load_key(key1, kf1, ksl1, kzl1);
   }
+
+  // Slice kbk: keys s_key0 .. s_key0 + 31 (those below n_keys), chunk
+  // positions ts0 + n; row r sees key n of the slice iff r >= (ts0 + n) * q_g.
+  const int s_key0 = n_main * PB_KEYS + SLICE_KEYS * kbk;
+  const int ts0 = s_key0 - n_occ;
+  const bool has_slice = SL && s_key0 < n_keys;
+  const int s_first = (ts0 + n) * a.qg;
+  if (has_slice) {  // 8 segments of 4 rows, same chunk swizzle as a Q block
+    const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int seg = wave * 2 + q;
+      const int rr = seg * 4 + (lane >> 4);
+      const int t = ts0 + rr < a.T ? ts0 + rr : a.T - 1;  // keys past the chunk: any row, never written
+      dma16(kn_rs, t * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, sk + seg * 1024);
+    }
+  }
+  float sacc = 0.f, scomp = 0.f;
 
   const int row_first = (j_base >= n_occ) ? (j_base - n_occ) * a.qg : 0;
   const int rb_begin = row_first / PB_ROWS * PB_ROWS;
@@ -1022,12 +1053,51 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
       }
     }
   };
+  // The slice against this wavefront's 32 rows of the block.  The slice keys
+  // are chunk keys in bf16, so x = acc * sl2 - L for every cache format.
+  auto slice_rows = [&](const char *qb, const float *lb, int rb) {
+    const int r0 = rb + 32 * wave;
+    if (r0 >= R || r0 + 31 < ts0 * a.qg) return;  // no row here sees a slice key
+    uint32_t qa_l = q_lane;
+    asm volatile("" : "+v"(qa_l));
+    const char *qs = qb + wave * (32 * ROW_BYTES);
+    f32x16 cs = f32x16{};
+    bf16x8 qa = lds16(qs + qa_l), ka = lds16(sk + qa_l);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      bf16x8 qn = qa, kn = ka;
+      if (st < 7) {
+        qn = lds16(qs + (qa_l ^ ((st + 1) << 5)));
+        kn = lds16(sk + (qa_l ^ ((st + 1) << 5)));
+      }
+      cs = mfma32(qa, ka, cs);
+      qa = qn;
+      ka = kn;
+    }
+    float Ls[16];
+    load_l(lb, wave, Ls);
+    const bool sfull = r0 + 31 < R && r0 >= (ts0 + SLICE_KEYS - 1) * a.qg;
+    float ps[2] = {0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = fmaf(cs[r], sl2, -Ls[r]);
+      if (!sfull) {
+        const int row = r0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        x = (row < R && row >= s_first) ? x : -INFINITY;
+      }
+      ps[r & 1] += __builtin_amdgcn_exp2f(x);
+    }
+    add_comp(sacc, scomp, ps[0] + ps[1]);
+  };
   auto block = [&](const char *qb, const float *lb, const float *sb, int rb) {
     const bool full = (rb + PB_ROWS <= R) && (j_base + PB_KEYS <= n_occ || rb / a.qg >= t_last);
     if (full) {
       do_block(std::true_type{}, qb, lb, sb, rb);
     } else {
       do_block(std::false_type{}, qb, lb, sb, rb);
+    }
+    if constexpr (SL) {
+      if (has_slice) slice_rows(qb, lb, rb);
     }
   };
 
@@ -1049,6 +1119,18 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
     if (key0 < n_keys) w[key0] = mine0 + other0;
     if (key1 < n_keys) w[key1] = mine1 + other1;
+  }
+  if constexpr (SL) {
+    if (has_slice) {
+      const float sm = sacc - scomp;
+      const float so = __shfl_xor(sm, 32);
+      if (hl == 0) sred[wave * SLICE_KEYS + n] = sm + so;
+      __syncthreads();
+      if (wave == 0 && hl == 0 && s_key0 + n < n_keys) {
+        const float tot = ((sred[n] + sred[SLICE_KEYS + n]) + sred[2 * SLICE_KEYS + n]) + sred[3 * SLICE_KEYS + n];
+        a.wsum[static_cast<size_t>(grp) * n_keys + s_key0 + n] = tot;
+      }
+    }
   }
 }
 
@@ -1124,14 +1206,39 @@ hipError_t launch_attn_b_logits(const AttnArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s) {
+// Fold the chunk-only keys into the full key blocks when there is a full
+// block for every 32-key slice and folding lowers the number of blocks the
+// busiest of the 256 CUs runs (a CU's throughput is about the same with one
+// or two resident blocks, so that count sets the kernel's duration).
+static bool fold_chunk_keys(const AttnArgs &a) {
+  constexpr long long kCUs = 256;
+  const int n_keys = a.n_occ + a.T;
+  const int n_main = (a.n_occ + PB_KEYS - 1) / PB_KEYS;
+  const int slices = (n_keys - n_main * PB_KEYS + SLICE_KEYS - 1) / SLICE_KEYS;
+  const long long groups = static_cast<long long>(a.B) * a.Hkv;
+  const long long per_cu = (groups * ((n_keys + PB_KEYS - 1) / PB_KEYS) + kCUs - 1) / kCUs;
+  const long long per_cu_fold = (groups * n_main + kCUs - 1) / kCUs;
+  return a.n_occ > 0 && slices >= 1 && slices <= n_main && per_cu_fold < per_cu;
+}
+
+template <int FMT>
+static void launch_b_fmt(const AttnArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
-  const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
+  if (fold_chunk_keys(a)) {
+    const int nB = groups * ((a.n_occ + PB_KEYS - 1) / PB_KEYS);
+    hipLaunchKernelGGL((attn_b_native<FMT, true>), dim3(nB), dim3(256), 0, s, a);
+  } else {
+    const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
+    hipLaunchKernelGGL((attn_b_native<FMT, false>), dim3(nB), dim3(256), 0, s, a);
+  }
+}
+
+hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s) {
   KernelTimer timer(H2O_K_ATTN_B, s);
   switch (a.cache_fmt) {
-    case FMT_INT8: hipLaunchKernelGGL(attn_b_native<FMT_INT8>, dim3(nB), dim3(256), 0, s, a); break;
-    case FMT_INT4: hipLaunchKernelGGL(attn_b_native<FMT_INT4>, dim3(nB), dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(attn_b_native<FMT_NATIVE>, dim3(nB), dim3(256), 0, s, a); break;
+    case FMT_INT8: launch_b_fmt<FMT_INT8>(a, s); break;
+    case FMT_INT4: launch_b_fmt<FMT_INT4>(a, s); break;
+    default: launch_b_fmt<FMT_NATIVE>(a, s); break;
   }
   return hipGetLastError();
 }

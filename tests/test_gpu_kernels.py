@@ -83,6 +83,12 @@ SDPA_CASES = [
     ("bf16", "int8", 1, 8, 2, 64, 300, 40, 300),
     ("bf16", "int4", 2, 8, 2, 128, 512, 96, 512),
     ("bf16", "int4", 1, 8, 2, 64, 300, 40, 200),
+    # more than 512 pass-B blocks: chunk-only keys folded into the full key
+    # blocks as 32-key slices (ragged last slice, ragged rows, q_g 1/2/4)
+    ("bf16", "native", 2, 16, 16, 128, 4096, 300, 4000),
+    ("bf16", "native", 1, 128, 32, 128, 4096, 200, 4040),
+    ("bf16", "int8", 2, 32, 16, 128, 4096, 256, 4096),
+    ("bf16", "int4", 2, 32, 16, 128, 4096, 200, 3900),
     ("f32", "native", 1, 4, 1, 64, 256, 32, 256),
     ("f32", "native", 1, 8, 2, 128, 300, 50, 123),
     ("f32", "native", 1, 8, 2, 128, 300, 50, 0),
