@@ -123,16 +123,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
     return static_cast<uint32_t>(row * ROW_BYTES + 16 * c);
   };
-  auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs, bool is_v) {
+  // Segments qa .. qb-1 of this wavefront's share of one tile.
+  auto issue_segs = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs, bool is_v, int qa, int qb) {
     const int j0 = (t_lo + tile) * 64;
     if (j0 + 64 <= n_occ) {
 #pragma unroll
-      for (int q = 0; q < SPW; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * SPW + q) * 1024);
+      for (int q = qa; q < qb; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * SPW + q) * 1024);
     } else {
       // chunk rows (and, in the one tile that straddles n_occ, cache rows)
       const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
 #pragma unroll
-      for (int q = 0; q < SPW; ++q) {
+      for (int q = qa; q < qb; ++q) {
         const int row = (wave * SPW + q) * 4 + (lane >> 4);
         const uint32_t lo = lane_off(q, is_v);
         if (dt + row >= 0) {
@@ -143,8 +144,19 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
       }
     }
   };
-  auto issue_k = [&](int tile, char *dst) { issue_tile(tile, dst, kc_rs, kn_rs, false); };
-  auto issue_v = [&](int tile, char *dst) { issue_tile(tile, dst, vc_rs, vn_rs, true); };
+  auto issue_k = [&](int tile, char *dst) { issue_segs(tile, dst, kc_rs, kn_rs, false, 0, SPW); };
+  auto issue_v = [&](int tile, char *dst) { issue_segs(tile, dst, vc_rs, vn_rs, true, 0, SPW); };
+  // Part p (0..3) of the loads issued during a tile: K segments for p < 2, V
+  // segments for p >= 2, half of the wavefront's share each.  Spreading them
+  // over the tile keeps 8 wavefronts from queueing 32 loads at one instant.
+  auto issue_part = [&](int p, int tile_k, char *kdst, int tile_v, char *vdst) {
+    constexpr int H = SPW / 2;
+    if (p < 2) {
+      if (tile_k >= 0) issue_segs(tile_k, kdst, kc_rs, kn_rs, false, p * H, (p + 1) * H);
+    } else {
+      if (tile_v >= 0) issue_segs(tile_v, vdst, vc_rs, vn_rs, true, (p - 2) * H, (p - 1) * H);
+    }
+  };
 
   const int prow = perm_key(n);
   const uint32_t k_lane = static_cast<uint32_t>(prow * ROW_BYTES + ((hl ^ (prow & 15)) << 4));
@@ -171,7 +183,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
   // one straight-line block, the MFMAs of S(t+1) = K(t+1) Q^T from kb_next
   // interleaved with the exponentials of tile t, and O^T += V(t)^T P(t)^T.
   auto tile_step = [&](int t, f32x16 c0, f32x16 c1, const char *kb_next, f32x16 &n0, f32x16 &n1,
-                       const char *vb) {
+                       const char *vb, auto &&dma) {
     const int j0 = (t_lo + t) * 64;
     if constexpr (LG) {
       if (row_ok) store_logits(a.lg + (static_cast<size_t>(grp) * R + my_row) * a.lg_stride + j0 + 8 * hl, c0, c1);
@@ -202,6 +214,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     }
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
+    // P(t) in four 16-key quarters: quarter ks holds keys 16ks .. 16ks+15 of
+    // the lane's row, from S register c{ks/2}[8(ks&1) + e] (perm_key order).
+    // Quarter ks's exponentials run beside S(t+1) steps 2ks, 2ks+1 and the
+    // O^T += V^T P^T MFMAs of quarter ks-1, so that every stretch of the
+    // tile has matrix and vector work in flight.
     bf16x8 pb[4];
     float ls[4] = {0.f, 0.f, 0.f, 0.f};
     n0 = f32x16{};
@@ -211,39 +228,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     // v_xor each instead of eight registers held across the loop.
     uint32_t ka = k_lane;
     asm volatile("" : "+v"(ka));
-    bf16x8 kc0 = lds16(kb_next + ka), kc1 = lds16(kb_next + ka + 32 * ROW_BYTES);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      bf16x8 kn0 = kc0, kn1 = kc1;
-      if (st < 7) {
-        const char *kp = kb_next + (ka ^ ((st + 1) << 5));
-        kn0 = lds16(kp);
-        kn1 = lds16(kp + 32 * ROW_BYTES);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      n0 = mfma32(kc0, qf[st], n0);
-      n1 = mfma32(kc1, qf[st], n1);
-      kc0 = kn0;
-      kc1 = kn1;
-      const float p00 = __builtin_amdgcn_exp2f(fmaf(c0[st], sl2, neg_m));
-      const float p01 = __builtin_amdgcn_exp2f(fmaf(c0[8 + st], sl2, neg_m));
-      const float p10 = __builtin_amdgcn_exp2f(fmaf(c1[st], sl2, neg_m));
-      const float p11 = __builtin_amdgcn_exp2f(fmaf(c1[8 + st], sl2, neg_m));
-      ls[0] += p00;
-      ls[1] += p01;
-      ls[2] += p10;
-      ls[3] += p11;
-      pb[0][st] = static_cast<__bf16>(p00);
-      pb[1][st] = static_cast<__bf16>(p01);
-      pb[2][st] = static_cast<__bf16>(p10);
-      pb[3][st] = static_cast<__bf16>(p11);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     // keys 16ks + 8h + 0..3 and + 4..7 at d = 32 blk + (lane % 32)
     auto v_operand = [&](int ks, int blk) {
       const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
@@ -252,14 +236,67 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
       const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(vb + v_off(row + 4, col >> 3) + 2 * (col & 7)));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
-    bf16x8 vc = v_operand(0, 0);
+    bf16x8 kc0 = lds16(kb_next + ka), kc1 = lds16(kb_next + ka + 32 * ROW_BYTES);
+    bf16x8 vc = kc0;
 #pragma unroll
-    for (int step = 0; step < 16; ++step) {
-      const int ks = step >> 2, blk = step & 3;
-      bf16x8 vn = vc;
-      if (step < 15) vn = v_operand((step + 1) >> 2, (step + 1) & 3);
+    for (int ks = 0; ks < 4; ++ks) {
+      const f32x16 &cs = (ks < 2) ? c0 : c1;
+      const int e0 = 8 * (ks & 1);
+      dma(ks);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {  // S(t+1) step st = 2ks + h
+        const int st = 2 * ks + h;
+        bf16x8 kn0 = kc0, kn1 = kc1;
+        if (st < 7) {
+          const char *kp = kb_next + (ka ^ ((st + 1) << 5));
+          kn0 = lds16(kp);
+          kn1 = lds16(kp + 32 * ROW_BYTES);
+        }
+        if (ks > 0 && h == 0) vc = v_operand(ks - 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        n0 = mfma32(kc0, qf[st], n0);
+        n1 = mfma32(kc1, qf[st], n1);
+        kc0 = kn0;
+        kc1 = kn1;
+#pragma unroll
+        for (int e = 4 * h; e < 4 * h + 4; ++e) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(cs[e0 + e], sl2, neg_m));
+          ls[ks] += p;
+          pb[ks][e] = static_cast<__bf16>(p);
+        }
+        if (ks > 0) {  // O^T += V^T P^T for quarter ks-1, columns 64h .. 64h+63
+#pragma unroll
+          for (int b2 = 0; b2 < 2; ++b2) {
+            const int blk = 2 * h + b2;
+            const bf16x8 vn = (blk < 3) ? v_operand(ks - 1, blk + 1) : vc;
+            o[blk] = mfma32(vc, pb[ks - 1], o[blk]);
+            vc = vn;
+          }
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 7, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    // quarter 3: its MFMAs run on while the next tile's max is taken
+    vc = v_operand(3, 0);
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const bf16x8 vn = (blk < 3) ? v_operand(3, blk + 1) : vc;
       __builtin_amdgcn_sched_barrier(0);
-      o[blk] = mfma32(vc, pb[ks], o[blk]);
+      o[blk] = mfma32(vc, pb[3], o[blk]);
       vc = vn;
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -279,15 +316,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     // even tile t: K(t+1) in kb1, V(t) in vb0 (for the last tile, kb1 is stale
     // and the S it yields is discarded: one copy of the body per parity)
     wait_dma_and_sync();
-    if (t + 2 < ntiles) issue_k(t + 2, kb0);
-    if (t + 1 < ntiles) issue_v(t + 1, vb1);
-    tile_step(t, sa0, sa1, kb1, sb0, sb1, vb0);
+    const int ke = t + 2 < ntiles ? t + 2 : -1, ve = t + 1 < ntiles ? t + 1 : -1;
+    tile_step(t, sa0, sa1, kb1, sb0, sb1, vb0, [&](int p) { issue_part(p, ke, kb0, ve, vb1); });
     if (t + 1 >= ntiles) break;
     // odd tile t+1: K(t+2) in kb0, V(t+1) in vb1
     wait_dma_and_sync();
-    if (t + 3 < ntiles) issue_k(t + 3, kb1);
-    if (t + 2 < ntiles) issue_v(t + 2, vb0);
-    tile_step(t + 1, sb0, sb1, kb0, sa0, sa1, vb1);
+    const int ko = t + 3 < ntiles ? t + 3 : -1, vo = t + 2 < ntiles ? t + 2 : -1;
+    tile_step(t + 1, sb0, sb1, kb0, sa0, sa1, vb1, [&](int p) { issue_part(p, ko, kb1, vo, vb0); });
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
