@@ -129,9 +129,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     if (j0 + 64 <= n_occ) {
 #pragma unroll
       for (int q = qa; q < qb; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * SPW + q) * 1024);
+    } else if (j0 >= n_occ) {  // chunk rows only
+#pragma unroll
+      for (int q = qa; q < qb; ++q)  // offset in voffset: rows past T fail the range check, read 0
+        dma16(nrs, lane_off(q, is_v) + (j0 - n_occ) * ROW_BYTES, 0, dst + (wave * SPW + q) * 1024);
     } else {
-      // chunk rows (and, in the one tile that straddles n_occ, cache rows)
-      const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
+      // the one tile that straddles n_occ: cache rows, then chunk rows
+      const int dt = j0 - n_occ;  // chunk index of the tile's first row, < 0
 #pragma unroll
       for (int q = qa; q < qb; ++q) {
         const int row = (wave * SPW + q) * 4 + (lane >> 4);
@@ -430,7 +434,11 @@ __global__ __launch_bounds__(256, 2) void attn_a_dec(AttnArgs a) {
     if (j0 + 64 <= n_occ) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
-    } else {
+    } else if (j0 >= n_occ) {  // chunk rows only
+#pragma unroll
+      for (int q = 0; q < 4; ++q)  // offset in voffset: rows past T fail the range check, read 0
+        dma16(nrs, lane_off(q, is_v) + (j0 - n_occ) * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+    } else {  // the tile that straddles n_occ
       const int dt = j0 - n_occ;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
