@@ -37,6 +37,7 @@ namespace {
 constexpr int NT = 1024;     // threads of the per-head workgroups
 constexpr int SLICE = 1024;  // slots per candidate workgroup
 constexpr int NT_C = 256;    // threads of the candidate workgroups (4 slots each)
+constexpr int KV_FUSE_T = 64;  // chunks up to this length: the pick writes the K/V rows
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -429,12 +430,36 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
 // of the slices follow one another in slot order, so list order breaks ties
 // as slot order does.  ncand: list length per head (the last slice may fill
 // fewer than T entries: nreal counts the filled ones, which come first).
-template <int NTH, int ITEMS, int POL>
-__global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand, int ncand, int nreal) {
+//
+// KV: also copy the chunk's K and V rows (native cache) into the slots this
+// head took, replacing the separate write kernel for short chunks: the slots
+// stay in LDS, and the rows of T <= KV_FUSE_T tokens are a few KB per head.
+template <int NTH, int ITEMS, int POL, bool KV>
+__global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand, int ncand, int nreal,
+                                                 KvWriteArgs kv) {
   __shared__ SelShared sh;
+  __shared__ int chosen[KV ? KV_FUSE_T : 1];
   const int tid = threadIdx.x;
   const int C = a.C, T = a.T, n_keys = a.n_occ + T;
   const int head = blockIdx.x;
+  auto write_rows = [&]() {
+    __syncthreads();  // chosen[] complete
+    const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+    const int row_bytes = kv.D * (kv.dtype == DT_F32 ? 4 : 2);
+    const int cpr = row_bytes / 16;
+    const int total = nb * T * 2 * cpr;
+    for (int i = tid; i < total; i += NTH) {
+      const int chunk = i % cpr;
+      int rest = i / cpr;
+      const int isv = rest & 1;
+      rest >>= 1;
+      const int t = rest % T, bb = rest / T;
+      const size_t g = (POL == H2O_POLICY_ORIG) ? static_cast<size_t>(bb) * a.Hkv + head : head;
+      const char *src = static_cast<const char *>(isv ? kv.vn : kv.kn) + (g * T + t) * row_bytes + chunk * 16;
+      char *dst = static_cast<char *>(isv ? kv.vc : kv.kc) + (g * C + chosen[t]) * row_bytes + chunk * 16;
+      *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(src);
+    }
+  };
   const uint2 *src = cand + static_cast<size_t>(head) * ncand;
   const int base = tid * ITEMS;
   const int nvalid = nreal - base;
@@ -454,7 +479,12 @@ __global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand
       if (k < nvalid && u < v) v = u;
     }
     v = block_min_u64<NTH>(v, sh.m64);
-    if (tid == 0) take_slot<POL>(a, head, static_cast<int>(static_cast<uint32_t>(v)), 0, a.wsum[static_cast<size_t>(head) * n_keys + C]);
+    if (tid == 0) {
+      const int j = static_cast<int>(static_cast<uint32_t>(v));
+      take_slot<POL>(a, head, j, 0, a.wsum[static_cast<size_t>(head) * n_keys + C]);
+      if constexpr (KV) chosen[0] = j;
+    }
+    if constexpr (KV) write_rows();
     return;
   }
   uint32_t theta, take_eq;
@@ -481,9 +511,14 @@ __global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand
 #pragma unroll
     for (int u = 0; u < UB; ++u) seed[u] = out[u] >= 0 ? w0[C + out[u]] : 0.f;
 #pragma unroll
-    for (int u = 0; u < UB; ++u)
-      if (out[u] >= 0) take_slot<POL>(a, head, slot[k0 + u], out[u], seed[u]);
+    for (int u = 0; u < UB; ++u) {
+      if (out[u] >= 0) {
+        take_slot<POL>(a, head, slot[k0 + u], out[u], seed[u]);
+        if constexpr (KV) chosen[out[u]] = slot[k0 + u];
+      }
+    }
   }
+  if constexpr (KV) write_rows();
 }
 
 template <int ITEMS, int POL>
@@ -515,8 +550,28 @@ int n_slices(int C) { return (C + SLICE - 1) / SLICE; }
 // Candidate lists of at most half the slots: the two-pass shape pays off.
 bool two_pass_fits(int C, int T) { return 2LL * n_slices(C) * T <= C; }
 
+template <int POL, bool KV>
+void launch_pick(const EvictArgs &a, const uint2 *cand, int ncand, int nreal, const KvWriteArgs &kv,
+                 int heads, hipStream_t s) {
+  // short lists: one wavefront; longer ones: 256 or 1024 threads
+  if (nreal <= 64) {
+    hipLaunchKernelGGL((evict_pick<64, 1, POL, KV>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal, kv);
+  } else if (nreal <= 256) {
+    hipLaunchKernelGGL((evict_pick<64, 4, POL, KV>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal, kv);
+  } else if (nreal <= 1024) {
+    hipLaunchKernelGGL((evict_pick<256, 4, POL, KV>), dim3(heads), dim3(256), 0, s, a, cand, ncand, nreal, kv);
+  } else if (nreal <= 4096) {
+    hipLaunchKernelGGL((evict_pick<256, 16, POL, KV>), dim3(heads), dim3(256), 0, s, a, cand, ncand, nreal, kv);
+  } else if (nreal <= 16384) {
+    hipLaunchKernelGGL((evict_pick<NT, 16, POL, KV>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal, kv);
+  } else {
+    hipLaunchKernelGGL((evict_pick<NT, 32, POL, KV>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal, kv);
+  }
+}
+
+// kv: when set, the pick also writes the chunk's K/V rows (native cache).
 template <int POL>
-hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, hipStream_t s) {
+hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, const KvWriteArgs *kv, hipStream_t s) {
   const int heads = (POL == H2O_POLICY_ORIG) ? a.Hkv : a.groups;
   const int ns = n_slices(a.C);
   const int ncand = ns * a.T;
@@ -524,19 +579,10 @@ hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, hipStream_t s) {
   const int nreal = (ns - 1) * a.T + (last < a.T ? last : a.T);
   KernelTimer timer(H2O_K_EVICT, s);
   hipLaunchKernelGGL(evict_cand<POL>, dim3(ns, heads), dim3(NT_C), 0, s, a, cand);
-  // short lists: one wavefront; longer ones: 256 or 1024 threads
-  if (nreal <= 64) {
-    hipLaunchKernelGGL((evict_pick<64, 1, POL>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal);
-  } else if (nreal <= 256) {
-    hipLaunchKernelGGL((evict_pick<64, 4, POL>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal);
-  } else if (nreal <= 1024) {
-    hipLaunchKernelGGL((evict_pick<256, 4, POL>), dim3(heads), dim3(256), 0, s, a, cand, ncand, nreal);
-  } else if (nreal <= 4096) {
-    hipLaunchKernelGGL((evict_pick<256, 16, POL>), dim3(heads), dim3(256), 0, s, a, cand, ncand, nreal);
-  } else if (nreal <= 16384) {
-    hipLaunchKernelGGL((evict_pick<NT, 16, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+  if (kv) {
+    launch_pick<POL, true>(a, cand, ncand, nreal, *kv, heads, s);
   } else {
-    hipLaunchKernelGGL((evict_pick<NT, 32, POL>), dim3(heads), dim3(NT), 0, s, a, cand, ncand, nreal);
+    launch_pick<POL, false>(a, cand, ncand, nreal, KvWriteArgs{}, heads, s);
   }
   return hipGetLastError();
 }
@@ -548,13 +594,19 @@ size_t evict_workspace_bytes(int groups, int C, int T) {
   return sizeof(uint2) * static_cast<size_t>(groups) * n_slices(C) * T;
 }
 
-hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s) {
+hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s, const KvWriteArgs *kv,
+                        bool *kv_done) {
+  if (kv_done) *kv_done = false;
   const size_t need = evict_workspace_bytes(a.groups, a.C, a.T);
   if (a.n_occ == a.C && need && ws && ws_bytes >= need) {
     uint2 *cand = static_cast<uint2 *>(ws);
-    if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, s);
-    if (a.policy == H2O_POLICY_ORIG) return launch_two_pass<H2O_POLICY_ORIG>(a, cand, s);
-    return launch_two_pass<H2O_POLICY_H2O>(a, cand, s);
+    // fuse the K/V write into the pick: native cache, short chunk, evict-only bookkeeping
+    const bool fuse = kv && kv_done && kv->cache_fmt == FMT_NATIVE && a.T <= KV_FUSE_T && !kv->token_pos;
+    const KvWriteArgs *kvp = fuse ? kv : nullptr;
+    if (fuse) *kv_done = true;
+    if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, kvp, s);
+    if (a.policy == H2O_POLICY_ORIG) return launch_two_pass<H2O_POLICY_ORIG>(a, cand, kvp, s);
+    return launch_two_pass<H2O_POLICY_H2O>(a, cand, kvp, s);
   }
   const int per = (a.C + NT - 1) / NT;
   if (per <= 1) return launch_items<1>(a, s);

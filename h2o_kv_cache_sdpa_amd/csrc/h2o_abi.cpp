@@ -367,10 +367,12 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
   if (st != H2O_OK) return st;
   // the rest of the workspace, if any, holds the selection's candidate lists
   const size_t used = need;
+  const h2o::KvWriteArgs kv = write_args(d, cache, k_new, v_new, slot_log);
+  bool kv_done = false;
   st = from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, w, slot_log),
-                                  static_cast<char *>(ws) + used, ws_bytes - used, s));
-  if (st != H2O_OK) return st;
-  return from_hip(h2o::launch_kv_write(write_args(d, cache, k_new, v_new, slot_log), s));
+                                  static_cast<char *>(ws) + used, ws_bytes - used, s, &kv, &kv_done));
+  if (st != H2O_OK || kv_done) return st;
+  return from_hip(h2o::launch_kv_write(kv, s));
 }
 
 int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,

@@ -105,7 +105,11 @@ hipError_t launch_attn_combine(const AttnArgs &a, hipStream_t s);
 size_t attn_split_floats(int B, int Hq, int D, int T, int nsplit);
 // ws / ws_bytes: optional candidate buffer of evict_workspace_bytes() bytes;
 // with it, short chunks select over many workgroups per head.
-hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s);
+// kv (optional): the chunk's K/V write.  When the selection can do it in the
+// same launch (two-pass shape, native cache, short chunk) it does and sets
+// *kv_done; otherwise the caller launches launch_kv_write afterwards.
+hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s,
+                        const KvWriteArgs *kv = nullptr, bool *kv_done = nullptr);
 size_t evict_workspace_bytes(int groups, int C, int T);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_dequant(const KvWriteArgs &a, int n_slots, float *kout, float *vout, hipStream_t s);
