@@ -45,11 +45,14 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int SMALL_T = 8;  // up to this many slots: T rounds of a block minimum (radix select beyond)
+
 struct SelShared {
   uint32_t hist[256];
   uint32_t sel, k;
   uint32_t a[16], b[16];
-  uint64_t m64[16];
+  uint64_t m64[32];  // two banks of up to 16 wavefronts (alternate rounds)
+  uint32_t ps[SMALL_T];
 };
 
 // Block-wide exclusive scan of two counters; returns the prefixes for this thread.
@@ -406,6 +409,25 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
       if (k < nvalid) dst[base + k - s0] = make_uint2(key[k], static_cast<uint32_t>(base + k));
     return;
   }
+  if (T <= SMALL_T) {
+    // T rounds of the slice's smallest (key, slot), listed in that order (the
+    // pick compares (key, slot) pairs, so list order carries no tie-break).
+    // Consecutive rounds use alternate LDS slots of the block minimum.
+    uint64_t u[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      u[k] = k < nvalid ? (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(base + k) : ~0ull;
+    for (int r = 0; r < T; ++r) {
+      uint64_t m = u[0];
+#pragma unroll
+      for (int k = 1; k < ITEMS; ++k) m = u[k] < m ? u[k] : m;
+      m = block_min_u64<NT_C>(m, sh.m64 + 16 * (r & 1));
+      if (tid == 0) dst[r] = make_uint2(static_cast<uint32_t>(m >> 32), static_cast<uint32_t>(m));
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) u[k] = u[k] == m ? ~0ull : u[k];
+    }
+    return;
+  }
   uint32_t theta, take_eq;
   select_smallest<NT_C, ITEMS>(rel, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
   uint32_t nl = 0, ne = 0;
@@ -483,6 +505,33 @@ __global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand
       const int j = static_cast<int>(static_cast<uint32_t>(v));
       take_slot<POL>(a, head, j, 0, a.wsum[static_cast<size_t>(head) * n_keys + C]);
       if constexpr (KV) chosen[0] = j;
+    }
+    if constexpr (KV) write_rows();
+    return;
+  }
+  if (T <= SMALL_T) {
+    // T rounds of the smallest (key, slot); then each winner's place in slot
+    // order is the number of winners with a lower slot.
+    uint64_t u[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      u[k] = k < nvalid ? (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(slot[k]) : ~0ull;
+    for (int r = 0; r < T; ++r) {
+      uint64_t m = u[0];
+#pragma unroll
+      for (int k = 1; k < ITEMS; ++k) m = u[k] < m ? u[k] : m;
+      m = block_min_u64<NTH>(m, sh.m64 + 16 * (r & 1));
+      if (tid == 0) sh.ps[r] = static_cast<uint32_t>(m);
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k) u[k] = u[k] == m ? ~0ull : u[k];
+    }
+    __syncthreads();
+    if (tid < T) {
+      const uint32_t j = sh.ps[tid];
+      int out = 0;
+      for (int r = 0; r < T; ++r) out += sh.ps[r] < j;
+      take_slot<POL>(a, head, static_cast<int>(j), out, a.wsum[static_cast<size_t>(head) * n_keys + C + out]);
+      if constexpr (KV) chosen[out] = static_cast<int>(j);
     }
     if constexpr (KV) write_rows();
     return;

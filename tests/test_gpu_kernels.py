@@ -194,6 +194,10 @@ EVICT_CASES = [
     (1, 8, 32768, 16, 32768),
     (2, 3, 16384, 128, 16384),
     (1, 2, 3082, 64, 3082),    # last 1024-slot slice shorter than the chunk
+    # chunks of 2..8 tokens: rounds of the block minimum in both selection passes
+    (1, 8, 32768, 4, 32768),
+    (2, 3, 4096, 8, 4096),
+    (1, 2, 3075, 5, 3075),     # last slice (3 slots) shorter than the chunk
 ]
 
 
@@ -272,7 +276,7 @@ def test_evict_policy_parity(case, policy, two_pass):
 
 
 @pytest.mark.parametrize("two_pass", [False, True], ids=["one_pass", "ws"])
-@pytest.mark.parametrize("T", [512, 1])
+@pytest.mark.parametrize("T", [512, 16, 8, 4, 1])
 def test_evict_ties_resolve_to_lower_index(T, two_pass):
     rng = np.random.default_rng(41)
     B, H, C = 2, 4, 4096
