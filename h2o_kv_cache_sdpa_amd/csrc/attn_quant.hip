@@ -435,15 +435,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int FMT, bool LG>
 __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   using Q = QTile<FMT>;
-  __shared__ __attribute__((aligned(1024))) char kb[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kc0[Q::CODE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vc0[Q::CODE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kc1[Q::CODE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vc1[Q::CODE_BYTES];
-  __shared__ __attribute__((aligned(256))) uint16_t fc0[Q::NFAC][64];
-  __shared__ __attribute__((aligned(256))) uint16_t fc1[Q::NFAC][64];
-  __shared__ __attribute__((aligned(256))) float fac[4][64];
+  // widened bf16 tiles and their per-key factors, double-buffered
+  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(256))) float fac0[4][64];
+  __shared__ __attribute__((aligned(256))) float fac1[4][64];
   __shared__ float red_m[4][16], red_l[4][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -489,43 +487,70 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
-  const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * Q::CODE_ROW,
-                                 n_occ * Q::CODE_ROW);
-  const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * Q::CODE_ROW,
-                                 n_occ * Q::CODE_ROW);
+  // Codes move HBM -> registers with plain vector loads, PD tiles ahead of
+  // their use: thread tid holds the 32 codes of key row tid / 4, quarter
+  // tid % 4, of K and of V (int8: 2 x 16 bytes each, int4: 16 bytes), and
+  // threads 0..63 the fp16 factors of key tid.  Loads into registers keep
+  // their order in the vector-memory counter, so each tile waits only for
+  // its own loads; an LDS-DMA pipeline this deep would wait for all.
+  constexpr int CW = Q::CODE_ROW / 4 / 16;  // 16-byte words of one thread's share
+  constexpr int PD = (FMT == FMT_INT8) ? 3 : 4;
+  struct Codes {
+    uint4 k[CW], v[CW];
+    uint16_t f[Q::NFAC];
+  };
   const uint16_t *fsrc[4] = {a.ks, a.vs, a.kz, a.vz};
-  // as in attn_a_quant: the tile that straddles n_occ reads through resources
-  // that end at n_occ
-  auto issue_codes = [&](int tile, char *kdst, char *vdst, uint16_t (*fdst)[64]) {
-    const int j0 = (t_lo + tile) * 64;
-    if (j0 >= n_occ) return;
-    const bool whole = j0 + 64 <= n_occ;
-    const uint32_t rows_left = static_cast<uint32_t>(n_occ - j0);
-    const rsrc_t kr = whole ? kc_rs
-                            : make_rsrc(static_cast<const char *>(a.kc) + (cache_row0 + j0) * Q::CODE_ROW,
-                                        rows_left * Q::CODE_ROW);
-    const rsrc_t vr = whole ? vc_rs
-                            : make_rsrc(static_cast<const char *>(a.vc) + (cache_row0 + j0) * Q::CODE_ROW,
-                                        rows_left * Q::CODE_ROW);
-    const uint32_t soff = whole ? static_cast<uint32_t>(j0 * Q::CODE_ROW) : 0u;
-    for (int sgm = wave; sgm < Q::SEGS; sgm += 4) {
-      const uint32_t off = static_cast<uint32_t>(sgm * 1024 + 16 * lane);
-      dma16(kr, off, soff, kdst + sgm * 1024);
-      dma16(vr, off, soff, vdst + sgm * 1024);
+  const int crow = tid >> 2, cq = tid & 3;
+  // Tiles 0 .. nfull-1 of the split lie wholly in the cache: their loads
+  // are unconditional, so the compiler can count them (a tile past nfull
+  // reloads tile nfull - 1, an L2 hit; every wavefront loads the factors of
+  // key tid % 64).  The rest (the tile that straddles n_occ, chunk rows)
+  // take a direct path after the main loop.
+  const int nfull = max(0, min(ntiles, n_occ / 64 - t_lo));
+  auto load_codes = [&](int tile, Codes &c) {
+    const int j0 = (t_lo + (tile < nfull ? tile : nfull - 1)) * 64;
+    const size_t off = (cache_row0 + j0 + crow) * Q::CODE_ROW + cq * (Q::CODE_ROW / 4);
+#pragma unroll
+    for (int w = 0; w < CW; ++w) {
+      c.k[w] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.kc) + off + 16 * w);
+      c.v[w] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.vc) + off + 16 * w);
     }
-    if (wave < Q::NFAC && lane < 32) {
-      const rsrc_t fr = make_rsrc(fsrc[wave] + cache_row0 + j0, rows_left * 2);
-      dma4(fr, 4 * lane, 0, reinterpret_cast<char *>(fdst[wave]));
+#pragma unroll
+    for (int f = 0; f < Q::NFAC; ++f) c.f[f] = fsrc[f][cache_row0 + j0 + (tid & 63)];
+  };
+  auto store = [&](char *kb, char *vb, const uint4 (&kw)[4], const uint4 (&vw)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<uint4 *>(kb + kq_off(crow, 4 * cq + i)) = kw[i];
+      *reinterpret_cast<uint4 *>(vb + v_off(crow, 4 * cq + i)) = vw[i];
     }
   };
-  const int crow = tid >> 2, cq = tid & 3;
-  auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64]) {
+  auto store_fac = [&](float (*fac)[64], bool cached, const uint16_t *f) {
+    fac[0][tid] = cached ? f16_to_f32(f[0]) * a.sl2 : a.sl2;
+    fac[2][tid] = cached ? f16_to_f32(f[1]) : 1.f;
+    if constexpr (FMT == FMT_INT4) {
+      fac[1][tid] = cached ? f16_to_f32(f[2]) * a.sl2 : 0.f;
+      fac[3][tid] = cached ? f16_to_f32(f[3]) : 0.f;
+    }
+  };
+  // a tile wholly in the cache, from the prefetched registers
+  auto widen_full = [&](const Codes &c, char *kb, char *vb, float (*fac)[64]) {
+    uint4 kw[4], vw[4];
+    widen32<FMT>(reinterpret_cast<const char *>(c.k), kw);
+    widen32<FMT>(reinterpret_cast<const char *>(c.v), vw);
+    store(kb, vb, kw, vw);
+    if (tid < 64) store_fac(fac, true, c.f);
+  };
+  // any other tile, loading as it goes: codes of rows below n_occ, new keys
+  // (bf16) above, zeros past the chunk
+  auto widen_direct = [&](int tile, char *kb, char *vb, float (*fac)[64]) {
     const int j0 = (t_lo + tile) * 64;
     const int j = j0 + crow;
     uint4 kw[4], vw[4];
     if (j < n_occ) {
-      widen32<FMT>(kcs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), kw);
-      widen32<FMT>(vcs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), vw);
+      const size_t off = (cache_row0 + j) * Q::CODE_ROW + cq * (Q::CODE_ROW / 4);
+      widen32<FMT>(static_cast<const char *>(a.kc) + off, kw);
+      widen32<FMT>(static_cast<const char *>(a.vc) + off, vw);
     } else {
       const int t = j - n_occ;
 #pragma unroll
@@ -538,19 +563,15 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4 *>(kb + kq_off(crow, 4 * cq + i)) = kw[i];
-      *reinterpret_cast<uint4 *>(vb + v_off(crow, 4 * cq + i)) = vw[i];
-    }
+    store(kb, vb, kw, vw);
     if (tid < 64) {
       const bool cached = j0 + tid < n_occ;
-      fac[0][tid] = cached ? f16_to_f32(fcs[0][tid]) * a.sl2 : a.sl2;
-      fac[2][tid] = cached ? f16_to_f32(fcs[1][tid]) : 1.f;
-      if constexpr (FMT == FMT_INT4) {
-        fac[1][tid] = cached ? f16_to_f32(fcs[2][tid]) * a.sl2 : 0.f;
-        fac[3][tid] = cached ? f16_to_f32(fcs[3][tid]) : 0.f;
+      uint16_t f[4] = {0, 0, 0, 0};
+      if (cached) {
+#pragma unroll
+        for (int q = 0; q < Q::NFAC; ++q) f[q] = fsrc[q][cache_row0 + j0 + tid];
       }
+      store_fac(fac, cached, f);
     }
   };
 
@@ -561,7 +582,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   const int krow = 16 * wave + n;
   const int kk0 = 16 * wave + 4 * g4;  // tile key of the lane's first value
 
-  auto compute = [&](int tile) {
+  auto compute = [&](int tile, const char *kb, const char *vb, const float (*fac)[64]) {
     const int j0 = (t_lo + tile) * 64;
     f32x4 c = f32x4{};
 #pragma unroll
@@ -623,19 +644,40 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     }
   };
 
-  if (ntiles > 0) issue_codes(0, kc0, vc0, fc0);
-  for (int t = 0; t < ntiles; t += 2) {
-    wait_dma_and_sync();
-    if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
-    widen_tile(t, kc0, vc0, fc0);
-    lds_barrier();
-    compute(t);
-    if (t + 1 >= ntiles) break;
-    wait_dma_and_sync();
-    if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
-    widen_tile(t + 1, kc1, vc1, fc1);
-    lds_barrier();
-    compute(t + 1);
+  // Tile t: widen into buffer t & 1, refill its registers with tile t + PD,
+  // one barrier, compute.  The barrier also orders every wavefront's compute
+  // of tile t - 1 before the widening of tile t + 1 into the same buffer.
+  // Groups of G tiles are unrolled straight-line: the compiler counts the
+  // loads in flight exactly there, while across a loop back-edge it waits
+  // for all of them (so it drains once per group, not once per tile).
+  if (nfull > 0) {
+    constexpr int G = 3 * PD;
+    Codes cr[PD];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) load_codes(p, cr[p]);
+    for (int t0 = 0; t0 < nfull; t0 += G) {
+#pragma unroll
+      for (int p = 0; p < G; ++p) {
+        const int t = t0 + p;
+        char *kb = (p & 1) ? kb1 : kb0;  // t0 is even: t & 1 == p & 1
+        char *vb = (p & 1) ? vb1 : vb0;
+        float (*fac)[64] = (p & 1) ? fac1 : fac0;
+        if (t < nfull) widen_full(cr[p % PD], kb, vb, fac);
+        load_codes(t + PD, cr[p % PD]);
+        if (t < nfull) {
+          __syncthreads();
+          compute(t, kb, vb, fac);
+        }
+      }
+    }
+  }
+  for (int t = nfull; t < ntiles; ++t) {
+    char *kb = (t & 1) ? kb1 : kb0;
+    char *vb = (t & 1) ? vb1 : vb0;
+    float (*fac)[64] = (t & 1) ? fac1 : fac0;
+    widen_direct(t, kb, vb, fac);
+    __syncthreads();
+    compute(t, kb, vb, fac);
   }
 
   // ---- merge the four wavefronts (u: the zero-point term, the same for every d) ----
@@ -652,7 +694,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][n]);
   const float my_scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  auto red_o = [&](int w) { return reinterpret_cast<float *>(w < 2 ? kb : vb) + (w & 1) * 16 * D; };
+  auto red_o = [&](int w) { return reinterpret_cast<float *>(w < 2 ? kb0 : vb0) + (w & 1) * 16 * D; };
   {
     float *mine = red_o(wave);
 #pragma unroll
