@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
   const int R = a.qg * a.T;
   const int tiles_per_grp = (R + 127) / 128;
   const int wi = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
+  // Row blocks go out last first: under the causal mask the last rows see the
+  // most keys, and starting the longest blocks first evens out the tail.
+  const int grp = wi / tiles_per_grp, rt = tiles_per_grp - 1 - wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
   const int row0 = rt * 128;
   const int my_row = row0 + wave * 32 + n;

@@ -110,7 +110,9 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
   const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
   const int split = wi_all % a.nsplit;
   const int wi = wi_all / a.nsplit;
-  const int grp = wi / tiles_per_grp, rt = wi % tiles_per_grp;
+  // Row blocks go out last first: under the causal mask the last rows see the
+  // most keys, and starting the longest blocks first evens out the tail.
+  const int grp = wi / tiles_per_grp, rt = tiles_per_grp - 1 - wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
   const int row0 = rt * 128;
   const int wrow0 = row0 + wave * 32;
