@@ -807,6 +807,7 @@ __global__ __launch_bounds__(256) void attn_b_logits(AttnArgs a, float xs) {
 constexpr int PB_KEYS = 256;
 constexpr int PB_ROWS = 128;
 constexpr int SLICE_KEYS = 32;  // chunk keys folded into one key block
+constexpr int PB_PLAIN = 0, PB_FOLD = 1, PB_PAIR = 2;  // attn_b_native work mappings
 constexpr int QBLK_BYTES = PB_ROWS * ROW_BYTES;  // 32 KB
 
 // 8 codes of one key row (int8: 8 bytes, int4: 4 bytes with element 2k in the
@@ -848,8 +849,9 @@ __device__ __forceinline__ bf16x8 widen8(const char *codes) {
 // takes 32-row sub-block w of every row block against the slice's keys, which
 // sit in LDS for the whole block, and the four partial column sums are added
 // in a fixed order at the end.
-template <int FMT, bool SL>
+template <int FMT, int MODE>
 __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
+  constexpr bool SL = MODE == PB_FOLD, PAIR = MODE == PB_PAIR;
   __shared__ __attribute__((aligned(1024))) char qb0[QBLK_BYTES];
   __shared__ __attribute__((aligned(1024))) char qb1[QBLK_BYTES];
   __shared__ __attribute__((aligned(1024))) char sk[SL ? SLICE_KEYS * ROW_BYTES : 16];
@@ -866,314 +868,322 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
   const int n_keys = n_occ + a.T;
   const int R = a.qg * a.T;
   const int n_main = (n_occ + PB_KEYS - 1) / PB_KEYS;  // key blocks starting below n_occ
-  const int kblocks = SL ? n_main : (n_keys + PB_KEYS - 1) / PB_KEYS;
+  const int kblocks_all = (n_keys + PB_KEYS - 1) / PB_KEYS;
+  const int kblocks = SL ? n_main : PAIR ? (kblocks_all + 1) / 2 : kblocks_all;  // work items per group
   const int wi = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = wi / kblocks, kbk = wi % kblocks;
+  const int grp = wi / kblocks, item = wi % kblocks;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
-  const int j_base = kbk * PB_KEYS;
-  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
-  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
-  const float sl2 = a.sl2;
+  // PAIR: item i sums key blocks i and kblocks_all - 1 - i, one after the other
+  const int npass = (PAIR && item != kblocks_all - 1 - item) ? 2 : 1;
+#pragma unroll 1
+  for (int pass = 0; pass < npass; ++pass) {
+    const int kbk = pass == 0 ? item : kblocks_all - 1 - item;
+    if (pass > 0) __syncthreads();  // every wavefront is done with the LDS row buffers
+    const int j_base = kbk * PB_KEYS;
+    const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
+    const size_t new_row0 = static_cast<size_t>(grp) * a.T;
+    const float sl2 = a.sl2;
 
-  // K^T operands of the wave's two 32-key sub-blocks
-  int key0 = j_base + wave * 64 + n, key1 = key0 + 32;
-  const int tnew0 = key0 - n_occ, tnew1 = key1 - n_occ;
-  bf16x8 kf0[8], kf1[8];
-  // per-key factors of the exponent: sl2 * s_k, sl2 * z_k (chunk keys: sl2, 0)
-  float ksl0 = sl2, ksl1 = sl2, kzl0 = 0.f, kzl1 = 0.f;
-  if constexpr (FMT == FMT_NATIVE) {
-    const char *src0 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key0 < n_keys ? key0 : 0);
-    const char *src1 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key1 < n_keys ? key1 : 0);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      kf0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src0 + 32 * st + 16 * hl));
-      kf1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src1 + 32 * st + 16 * hl));
-    }
-  } else {
-    constexpr int CROW = (FMT == FMT_INT8) ? D : D / 2;  // code bytes per key
-    auto load_key = [&](int key, bf16x8 (&kf)[8], float &ksl, float &kzl) {
-      const int kk = key < n_keys ? key : 0;
-      if (kk < n_occ) {
-        const char *src = static_cast<const char *>(a.kc) + (cache_row0 + kk) * CROW;
-#pragma unroll
-        for (int st = 0; st < 8; ++st) kf[st] = widen8<FMT>(src + (16 * st + 8 * hl) * CROW / D);
-        ksl = f16_to_f32(a.ks[cache_row0 + kk]) * sl2;
-        if constexpr (FMT == FMT_INT4) kzl = f16_to_f32(a.kz[cache_row0 + kk]) * sl2;
-      } else {
-        const char *src = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, kk);
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-          kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src + 32 * st + 16 * hl));
-      }
-    };
-    load_key(key0, kf0, ksl0, kzl0);
-    load_key(key1, kf1, ksl1, kzl1);
-  }
-
-  // Slice kbk: keys s_key0 .. s_key0 + 31 (those below n_keys), chunk
-  // positions ts0 + n; row r sees key n of the slice iff r >= (ts0 + n) * q_g.
-  const int s_key0 = n_main * PB_KEYS + SLICE_KEYS * kbk;
-  const int ts0 = s_key0 - n_occ;
-  const bool has_slice = SL && s_key0 < n_keys;
-  const int s_first = (ts0 + n) * a.qg;
-  if (has_slice) {  // 8 segments of 4 rows, same chunk swizzle as a Q block
-    const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int seg = wave * 2 + q;
-      const int rr = seg * 4 + (lane >> 4);
-      const int t = ts0 + rr < a.T ? ts0 + rr : a.T - 1;  // keys past the chunk: any row, never written
-      dma16(kn_rs, t * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, sk + seg * 1024);
-    }
-  }
-  float sacc = 0.f, scomp = 0.f;
-
-  const int row_first = (j_base >= n_occ) ? (j_base - n_occ) * a.qg : 0;
-  const int rb_begin = row_first / PB_ROWS * PB_ROWS;
-  const int nrb = (R - rb_begin + PB_ROWS - 1) / PB_ROWS;
-  const int t_last = j_base + PB_KEYS - 1 - n_occ;
-  const size_t lse_base = static_cast<size_t>(b) * a.Hq * a.T;
-
-  // DMA of a 128-row Q block (32 KB: 32 segments, 8 per wavefront) and its
-  // normalisers.  When q_g divides the block height, row rb + rr is query
-  // rb/q_g + rr/q_g of head g*q_g + rr%q_g: a per-lane constant offset plus a
-  // wave-uniform base.
-  const bool rows_split = (PB_ROWS % a.qg) == 0;
-  // The group's q_g query heads (q_g*T rows of Q) and their normalisers are
-  // contiguous: row r = i*q_g + hh lives at (hh*T + i).
-  const rsrc_t q_rs = make_rsrc(static_cast<const char *>(a.q) +
-                                    (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg) * a.T * ROW_BYTES,
-                                R * ROW_BYTES);
-  const rsrc_t l_rs = make_rsrc(a.lse2 + lse_base + static_cast<size_t>(g) * a.qg * a.T, R * 4);
-  const rsrc_t s_rs = make_rsrc(a.lse2 + static_cast<size_t>(a.B) * a.Hq * a.T + lse_base +
-                                    static_cast<size_t>(g) * a.qg * a.T,
-                                R * 4);
-  uint32_t qoff[8];
-  uint32_t loff = 0;
-  if (rows_split) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int rr = (wave * 8 + q) * 4 + (lane >> 4);
-      qoff[q] = ((rr % a.qg) * a.T + rr / a.qg) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15);
-    }
-    const int rl = (wave & 1) * 64 + lane;
-    loff = ((rl % a.qg) * a.T + rl / a.qg) * 4;
-  }
-  // L rows by waves 0-1; for int4 the sum(q) rows by waves 2-3
-  auto issue_rows = [&](int rb, char *qdst, float *ldst, float *sdst) {
-    if (rows_split && rb + PB_ROWS <= R) {
-      const uint32_t shift = static_cast<uint32_t>(rb / a.qg);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) dma16(q_rs, qoff[q], shift * ROW_BYTES, qdst + (wave * 8 + q) * 1024);
-      if (wave < 2) {
-        dma4(l_rs, loff, shift * 4, reinterpret_cast<char *>(ldst + wave * 64));
-      } else if (FMT == FMT_INT4) {
-        dma4(s_rs, loff, shift * 4, reinterpret_cast<char *>(sdst + (wave - 2) * 64));
-      }
-      return;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int seg = wave * 8 + q;
-      const int rr = seg * 4 + (lane >> 4);
-      int row = rb + rr;
-      row = row < R ? row : R - 1;  // rows past the end are masked
-      const int ii = row / a.qg, hh = row % a.qg;
-      dma16(q_rs, (hh * a.T + ii) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, qdst + seg * 1024);
-    }
-    {
-      int row = rb + (wave & 1) * 64 + lane;
-      row = row < R ? row : R - 1;
-      const int ii = row / a.qg, hh = row % a.qg;
-      if (wave < 2) {
-        dma4(l_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(ldst + wave * 64));
-      } else if (FMT == FMT_INT4) {
-        dma4(s_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(sdst + (wave - 2) * 64));
-      }
-    }
-  };
-
-  float acc0 = 0.f, comp0 = 0.f, acc1 = 0.f, comp1 = 0.f;
-  auto add_comp = [](float &acc, float &comp, float part) {
-    const float y = part - comp;
-    const float tt = acc + y;
-    comp = (tt - acc) - y;
-    acc = tt;
-  };
-  auto load_l = [&](const float *lb, int sub, float (&Lv)[16]) {
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const float4 L = *reinterpret_cast<const float4 *>(lb + 32 * sub + 8 * a4 + 4 * hl);
-      Lv[4 * a4] = L.x;
-      Lv[4 * a4 + 1] = L.y;
-      Lv[4 * a4 + 2] = L.z;
-      Lv[4 * a4 + 3] = L.w;
-    }
-  };
-
-  const uint32_t q_lane = static_cast<uint32_t>(n * ROW_BYTES + ((hl ^ (n & 15)) << 4));
-  // Row r sees chunk key t iff floor(r / q_g) >= t, i.e. r >= t * q_g.
-  const int first_row0 = tnew0 > 0 ? tnew0 * a.qg : 0;
-  const int first_row1 = tnew1 > 0 ? tnew1 * a.qg : 0;
-
-  // One 128-row block: the MFMAs of sub-block k+1 run while the VALU sums
-  // the exponentials of sub-block k.  FULL: every row sees every key.
-  auto do_block = [&](auto full_tag, const char *qb, const float *lb, const float *sb, int rb) {
-    constexpr bool FULL = decltype(full_tag)::value;
-    // Q operand of sub-block sub, step st: sub * 32 rows + (q_lane ^ (st << 5));
-    // q_lane is made opaque per block (one v_xor per read, no held addresses).
-    uint32_t qa_l = q_lane;
-    asm volatile("" : "+v"(qa_l));
-    auto qop = [&](int sub, int st) { return lds16(qb + sub * (32 * ROW_BYTES) + (qa_l ^ (st << 5))); };
-    f32x16 c0 = f32x16{}, c1 = f32x16{};
-    float Lc[16], Sc[16];
-    bf16x8 qc = qop(0, 0);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const bf16x8 qn = st < 7 ? qop(0, st + 1) : qop(1, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      c0 = mfma32(qc, kf0[st], c0);
-      c1 = mfma32(qc, kf1[st], c1);
-      qc = qn;
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    load_l(lb, 0, Lc);
-    if constexpr (FMT == FMT_INT4) load_l(sb, 0, Sc);
-#pragma unroll
-    for (int sub = 1; sub <= 4; ++sub) {
-      f32x16 n0 = f32x16{}, n1 = f32x16{};
-      float p0[2] = {0.f, 0.f}, p1[2] = {0.f, 0.f};
-      const int rsub = rb + 32 * (sub - 1);  // rows of the block being summed
+    // K^T operands of the wave's two 32-key sub-blocks
+    int key0 = j_base + wave * 64 + n, key1 = key0 + 32;
+    const int tnew0 = key0 - n_occ, tnew1 = key1 - n_occ;
+    bf16x8 kf0[8], kf1[8];
+    // per-key factors of the exponent: sl2 * s_k, sl2 * z_k (chunk keys: sl2, 0)
+    float ksl0 = sl2, ksl1 = sl2, kzl0 = 0.f, kzl1 = 0.f;
+    if constexpr (FMT == FMT_NATIVE) {
+      const char *src0 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key0 < n_keys ? key0 : 0);
+      const char *src1 = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, key1 < n_keys ? key1 : 0);
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
-        if (sub < 4) {
-          bf16x8 qn = qc;
-          if (st < 7) {
-            qn = qop(sub, st + 1);
-          } else if (sub < 3) {
-            qn = qop(sub + 1, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          n0 = mfma32(qc, kf0[st], n0);
-          n1 = mfma32(qc, kf1[st], n1);
-          qc = qn;
-        }
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-          const int r = 2 * st + h2;
-          float x0, x1;
-          if constexpr (FMT == FMT_NATIVE) {
-            x0 = fmaf(c0[r], sl2, -Lc[r]);
-            x1 = fmaf(c1[r], sl2, -Lc[r]);
-          } else if constexpr (FMT == FMT_INT8) {
-            x0 = fmaf(c0[r], ksl0, -Lc[r]);
-            x1 = fmaf(c1[r], ksl1, -Lc[r]);
-          } else {
-            x0 = fmaf(c0[r], ksl0, fmaf(kzl0, Sc[r], -Lc[r]));
-            x1 = fmaf(c1[r], ksl1, fmaf(kzl1, Sc[r], -Lc[r]));
-          }
-          if constexpr (!FULL) {
-            const int row = rsub + 8 * (r >> 2) + 4 * hl + (r & 3);
-            x0 = (row < R && row >= first_row0) ? x0 : -INFINITY;
-            x1 = (row < R && row >= first_row1) ? x1 : -INFINITY;
-          }
-          p0[h2] += __builtin_amdgcn_exp2f(x0);
-          p1[h2] += __builtin_amdgcn_exp2f(x1);
-        }
-        if (sub < 4) {
-          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 6 : 10, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 6 : 10, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        kf0[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src0 + 32 * st + 16 * hl));
+        kf1[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src1 + 32 * st + 16 * hl));
       }
-      add_comp(acc0, comp0, p0[0] + p0[1]);
-      add_comp(acc1, comp1, p1[0] + p1[1]);
-      if (sub < 4) {
-        c0 = n0;
-        c1 = n1;
-        load_l(lb, sub, Lc);
-        if constexpr (FMT == FMT_INT4) load_l(sb, sub, Sc);
-      }
-    }
-  };
-  // The slice against this wavefront's 32 rows of the block.  The slice keys
-  // are chunk keys in bf16, so x = acc * sl2 - L for every cache format.
-  auto slice_rows = [&](const char *qb, const float *lb, int rb) {
-    const int r0 = rb + 32 * wave;
-    if (r0 >= R || r0 + 31 < ts0 * a.qg) return;  // no row here sees a slice key
-    uint32_t qa_l = q_lane;
-    asm volatile("" : "+v"(qa_l));
-    const char *qs = qb + wave * (32 * ROW_BYTES);
-    f32x16 cs = f32x16{};
-    bf16x8 qa = lds16(qs + qa_l), ka = lds16(sk + qa_l);
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      bf16x8 qn = qa, kn = ka;
-      if (st < 7) {
-        qn = lds16(qs + (qa_l ^ ((st + 1) << 5)));
-        kn = lds16(sk + (qa_l ^ ((st + 1) << 5)));
-      }
-      cs = mfma32(qa, ka, cs);
-      qa = qn;
-      ka = kn;
-    }
-    float Ls[16];
-    load_l(lb, wave, Ls);
-    const bool sfull = r0 + 31 < R && r0 >= (ts0 + SLICE_KEYS - 1) * a.qg;
-    float ps[2] = {0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = fmaf(cs[r], sl2, -Ls[r]);
-      if (!sfull) {
-        const int row = r0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-        x = (row < R && row >= s_first) ? x : -INFINITY;
-      }
-      ps[r & 1] += __builtin_amdgcn_exp2f(x);
-    }
-    add_comp(sacc, scomp, ps[0] + ps[1]);
-  };
-  auto block = [&](const char *qb, const float *lb, const float *sb, int rb) {
-    const bool full = (rb + PB_ROWS <= R) && (j_base + PB_KEYS <= n_occ || rb / a.qg >= t_last);
-    if (full) {
-      do_block(std::true_type{}, qb, lb, sb, rb);
     } else {
-      do_block(std::false_type{}, qb, lb, sb, rb);
+      constexpr int CROW = (FMT == FMT_INT8) ? D : D / 2;  // code bytes per key
+      auto load_key = [&](int key, bf16x8 (&kf)[8], float &ksl, float &kzl) {
+        const int kk = key < n_keys ? key : 0;
+        if (kk < n_occ) {
+          const char *src = static_cast<const char *>(a.kc) + (cache_row0 + kk) * CROW;
+#pragma unroll
+          for (int st = 0; st < 8; ++st) kf[st] = widen8<FMT>(src + (16 * st + 8 * hl) * CROW / D);
+          ksl = f16_to_f32(a.ks[cache_row0 + kk]) * sl2;
+          if constexpr (FMT == FMT_INT4) kzl = f16_to_f32(a.kz[cache_row0 + kk]) * sl2;
+        } else {
+          const char *src = key_row(a.kc, a.kn, cache_row0, new_row0, n_occ, a.T, kk);
+#pragma unroll
+          for (int st = 0; st < 8; ++st)
+            kf[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(src + 32 * st + 16 * hl));
+        }
+      };
+      load_key(key0, kf0, ksl0, kzl0);
+      load_key(key1, kf1, ksl1, kzl1);
+    }
+
+    // Slice kbk: keys s_key0 .. s_key0 + 31 (those below n_keys), chunk
+    // positions ts0 + n; row r sees key n of the slice iff r >= (ts0 + n) * q_g.
+    const int s_key0 = n_main * PB_KEYS + SLICE_KEYS * kbk;
+    const int ts0 = s_key0 - n_occ;
+    const bool has_slice = SL && s_key0 < n_keys;
+    const int s_first = (ts0 + n) * a.qg;
+    if (has_slice) {  // 8 segments of 4 rows, same chunk swizzle as a Q block
+      const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int seg = wave * 2 + q;
+        const int rr = seg * 4 + (lane >> 4);
+        const int t = ts0 + rr < a.T ? ts0 + rr : a.T - 1;  // keys past the chunk: any row, never written
+        dma16(kn_rs, t * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, sk + seg * 1024);
+      }
+    }
+    float sacc = 0.f, scomp = 0.f;
+
+    const int row_first = (j_base >= n_occ) ? (j_base - n_occ) * a.qg : 0;
+    const int rb_begin = row_first / PB_ROWS * PB_ROWS;
+    const int nrb = (R - rb_begin + PB_ROWS - 1) / PB_ROWS;
+    const int t_last = j_base + PB_KEYS - 1 - n_occ;
+    const size_t lse_base = static_cast<size_t>(b) * a.Hq * a.T;
+
+    // DMA of a 128-row Q block (32 KB: 32 segments, 8 per wavefront) and its
+    // normalisers.  When q_g divides the block height, row rb + rr is query
+    // rb/q_g + rr/q_g of head g*q_g + rr%q_g: a per-lane constant offset plus a
+    // wave-uniform base.
+    const bool rows_split = (PB_ROWS % a.qg) == 0;
+    // The group's q_g query heads (q_g*T rows of Q) and their normalisers are
+    // contiguous: row r = i*q_g + hh lives at (hh*T + i).
+    const rsrc_t q_rs = make_rsrc(static_cast<const char *>(a.q) +
+                                      (static_cast<size_t>(b) * a.Hq + static_cast<size_t>(g) * a.qg) * a.T * ROW_BYTES,
+                                  R * ROW_BYTES);
+    const rsrc_t l_rs = make_rsrc(a.lse2 + lse_base + static_cast<size_t>(g) * a.qg * a.T, R * 4);
+    const rsrc_t s_rs = make_rsrc(a.lse2 + static_cast<size_t>(a.B) * a.Hq * a.T + lse_base +
+                                      static_cast<size_t>(g) * a.qg * a.T,
+                                  R * 4);
+    uint32_t qoff[8];
+    uint32_t loff = 0;
+    if (rows_split) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int rr = (wave * 8 + q) * 4 + (lane >> 4);
+        qoff[q] = ((rr % a.qg) * a.T + rr / a.qg) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15);
+      }
+      const int rl = (wave & 1) * 64 + lane;
+      loff = ((rl % a.qg) * a.T + rl / a.qg) * 4;
+    }
+    // L rows by waves 0-1; for int4 the sum(q) rows by waves 2-3
+    auto issue_rows = [&](int rb, char *qdst, float *ldst, float *sdst) {
+      if (rows_split && rb + PB_ROWS <= R) {
+        const uint32_t shift = static_cast<uint32_t>(rb / a.qg);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) dma16(q_rs, qoff[q], shift * ROW_BYTES, qdst + (wave * 8 + q) * 1024);
+        if (wave < 2) {
+          dma4(l_rs, loff, shift * 4, reinterpret_cast<char *>(ldst + wave * 64));
+        } else if (FMT == FMT_INT4) {
+          dma4(s_rs, loff, shift * 4, reinterpret_cast<char *>(sdst + (wave - 2) * 64));
+        }
+        return;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int seg = wave * 8 + q;
+        const int rr = seg * 4 + (lane >> 4);
+        int row = rb + rr;
+        row = row < R ? row : R - 1;  // rows past the end are masked
+        const int ii = row / a.qg, hh = row % a.qg;
+        dma16(q_rs, (hh * a.T + ii) * ROW_BYTES + 16 * kq_chunk_at(rr, lane & 15), 0, qdst + seg * 1024);
+      }
+      {
+        int row = rb + (wave & 1) * 64 + lane;
+        row = row < R ? row : R - 1;
+        const int ii = row / a.qg, hh = row % a.qg;
+        if (wave < 2) {
+          dma4(l_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(ldst + wave * 64));
+        } else if (FMT == FMT_INT4) {
+          dma4(s_rs, (hh * a.T + ii) * 4, 0, reinterpret_cast<char *>(sdst + (wave - 2) * 64));
+        }
+      }
+    };
+
+    float acc0 = 0.f, comp0 = 0.f, acc1 = 0.f, comp1 = 0.f;
+    auto add_comp = [](float &acc, float &comp, float part) {
+      const float y = part - comp;
+      const float tt = acc + y;
+      comp = (tt - acc) - y;
+      acc = tt;
+    };
+    auto load_l = [&](const float *lb, int sub, float (&Lv)[16]) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 L = *reinterpret_cast<const float4 *>(lb + 32 * sub + 8 * a4 + 4 * hl);
+        Lv[4 * a4] = L.x;
+        Lv[4 * a4 + 1] = L.y;
+        Lv[4 * a4 + 2] = L.z;
+        Lv[4 * a4 + 3] = L.w;
+      }
+    };
+
+    const uint32_t q_lane = static_cast<uint32_t>(n * ROW_BYTES + ((hl ^ (n & 15)) << 4));
+    // Row r sees chunk key t iff floor(r / q_g) >= t, i.e. r >= t * q_g.
+    const int first_row0 = tnew0 > 0 ? tnew0 * a.qg : 0;
+    const int first_row1 = tnew1 > 0 ? tnew1 * a.qg : 0;
+
+    // One 128-row block: the MFMAs of sub-block k+1 run while the VALU sums
+    // the exponentials of sub-block k.  FULL: every row sees every key.
+    auto do_block = [&](auto full_tag, const char *qb, const float *lb, const float *sb, int rb) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      // Q operand of sub-block sub, step st: sub * 32 rows + (q_lane ^ (st << 5));
+      // q_lane is made opaque per block (one v_xor per read, no held addresses).
+      uint32_t qa_l = q_lane;
+      asm volatile("" : "+v"(qa_l));
+      auto qop = [&](int sub, int st) { return lds16(qb + sub * (32 * ROW_BYTES) + (qa_l ^ (st << 5))); };
+      f32x16 c0 = f32x16{}, c1 = f32x16{};
+      float Lc[16], Sc[16];
+      bf16x8 qc = qop(0, 0);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        const bf16x8 qn = st < 7 ? qop(0, st + 1) : qop(1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        c0 = mfma32(qc, kf0[st], c0);
+        c1 = mfma32(qc, kf1[st], c1);
+        qc = qn;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      load_l(lb, 0, Lc);
+      if constexpr (FMT == FMT_INT4) load_l(sb, 0, Sc);
+#pragma unroll
+      for (int sub = 1; sub <= 4; ++sub) {
+        f32x16 n0 = f32x16{}, n1 = f32x16{};
+        float p0[2] = {0.f, 0.f}, p1[2] = {0.f, 0.f};
+        const int rsub = rb + 32 * (sub - 1);  // rows of the block being summed
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+          if (sub < 4) {
+            bf16x8 qn = qc;
+            if (st < 7) {
+              qn = qop(sub, st + 1);
+            } else if (sub < 3) {
+              qn = qop(sub + 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            n0 = mfma32(qc, kf0[st], n0);
+            n1 = mfma32(qc, kf1[st], n1);
+            qc = qn;
+          }
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int r = 2 * st + h2;
+            float x0, x1;
+            if constexpr (FMT == FMT_NATIVE) {
+              x0 = fmaf(c0[r], sl2, -Lc[r]);
+              x1 = fmaf(c1[r], sl2, -Lc[r]);
+            } else if constexpr (FMT == FMT_INT8) {
+              x0 = fmaf(c0[r], ksl0, -Lc[r]);
+              x1 = fmaf(c1[r], ksl1, -Lc[r]);
+            } else {
+              x0 = fmaf(c0[r], ksl0, fmaf(kzl0, Sc[r], -Lc[r]));
+              x1 = fmaf(c1[r], ksl1, fmaf(kzl1, Sc[r], -Lc[r]));
+            }
+            if constexpr (!FULL) {
+              const int row = rsub + 8 * (r >> 2) + 4 * hl + (r & 3);
+              x0 = (row < R && row >= first_row0) ? x0 : -INFINITY;
+              x1 = (row < R && row >= first_row1) ? x1 : -INFINITY;
+            }
+            p0[h2] += __builtin_amdgcn_exp2f(x0);
+            p1[h2] += __builtin_amdgcn_exp2f(x1);
+          }
+          if (sub < 4) {
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 6 : 10, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(SG_VALU, FULL ? 6 : 10, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        add_comp(acc0, comp0, p0[0] + p0[1]);
+        add_comp(acc1, comp1, p1[0] + p1[1]);
+        if (sub < 4) {
+          c0 = n0;
+          c1 = n1;
+          load_l(lb, sub, Lc);
+          if constexpr (FMT == FMT_INT4) load_l(sb, sub, Sc);
+        }
+      }
+    };
+    // The slice against this wavefront's 32 rows of the block.  The slice keys
+    // are chunk keys in bf16, so x = acc * sl2 - L for every cache format.
+    auto slice_rows = [&](const char *qb, const float *lb, int rb) {
+      const int r0 = rb + 32 * wave;
+      if (r0 >= R || r0 + 31 < ts0 * a.qg) return;  // no row here sees a slice key
+      uint32_t qa_l = q_lane;
+      asm volatile("" : "+v"(qa_l));
+      const char *qs = qb + wave * (32 * ROW_BYTES);
+      f32x16 cs = f32x16{};
+      bf16x8 qa = lds16(qs + qa_l), ka = lds16(sk + qa_l);
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 qn = qa, kn = ka;
+        if (st < 7) {
+          qn = lds16(qs + (qa_l ^ ((st + 1) << 5)));
+          kn = lds16(sk + (qa_l ^ ((st + 1) << 5)));
+        }
+        cs = mfma32(qa, ka, cs);
+        qa = qn;
+        ka = kn;
+      }
+      float Ls[16];
+      load_l(lb, wave, Ls);
+      const bool sfull = r0 + 31 < R && r0 >= (ts0 + SLICE_KEYS - 1) * a.qg;
+      float ps[2] = {0.f, 0.f};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = fmaf(cs[r], sl2, -Ls[r]);
+        if (!sfull) {
+          const int row = r0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          x = (row < R && row >= s_first) ? x : -INFINITY;
+        }
+        ps[r & 1] += __builtin_amdgcn_exp2f(x);
+      }
+      add_comp(sacc, scomp, ps[0] + ps[1]);
+    };
+    auto block = [&](const char *qb, const float *lb, const float *sb, int rb) {
+      const bool full = (rb + PB_ROWS <= R) && (j_base + PB_KEYS <= n_occ || rb / a.qg >= t_last);
+      if (full) {
+        do_block(std::true_type{}, qb, lb, sb, rb);
+      } else {
+        do_block(std::false_type{}, qb, lb, sb, rb);
+      }
+      if constexpr (SL) {
+        if (has_slice) slice_rows(qb, lb, rb);
+      }
+    };
+
+    issue_rows(rb_begin, qb0, lb0, sb0);
+    for (int it = 0; it < nrb; it += 2) {
+      const int rb = rb_begin + it * PB_ROWS;
+      wait_dma_and_sync();  // block it in qb0; everybody done with qb1
+      if (it + 1 < nrb) issue_rows(rb + PB_ROWS, qb1, lb1, sb1);
+      block(qb0, lb0, sb0, rb);
+      if (it + 1 >= nrb) break;
+      wait_dma_and_sync();  // block it+1 in qb1; everybody done with qb0
+      if (it + 2 < nrb) issue_rows(rb + 2 * PB_ROWS, qb0, lb0, sb0);
+      block(qb1, lb1, sb1, rb + PB_ROWS);
+    }
+
+    const float mine0 = acc0 - comp0, mine1 = acc1 - comp1;
+    const float other0 = __shfl_xor(mine0, 32), other1 = __shfl_xor(mine1, 32);
+    if (hl == 0) {
+      float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
+      if (key0 < n_keys) w[key0] = mine0 + other0;
+      if (key1 < n_keys) w[key1] = mine1 + other1;
     }
     if constexpr (SL) {
-      if (has_slice) slice_rows(qb, lb, rb);
-    }
-  };
-
-  issue_rows(rb_begin, qb0, lb0, sb0);
-  for (int it = 0; it < nrb; it += 2) {
-    const int rb = rb_begin + it * PB_ROWS;
-    wait_dma_and_sync();  // block it in qb0; everybody done with qb1
-    if (it + 1 < nrb) issue_rows(rb + PB_ROWS, qb1, lb1, sb1);
-    block(qb0, lb0, sb0, rb);
-    if (it + 1 >= nrb) break;
-    wait_dma_and_sync();  // block it+1 in qb1; everybody done with qb0
-    if (it + 2 < nrb) issue_rows(rb + 2 * PB_ROWS, qb0, lb0, sb0);
-    block(qb1, lb1, sb1, rb + PB_ROWS);
-  }
-
-  const float mine0 = acc0 - comp0, mine1 = acc1 - comp1;
-  const float other0 = __shfl_xor(mine0, 32), other1 = __shfl_xor(mine1, 32);
-  if (hl == 0) {
-    float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
-    if (key0 < n_keys) w[key0] = mine0 + other0;
-    if (key1 < n_keys) w[key1] = mine1 + other1;
-  }
-  if constexpr (SL) {
-    if (has_slice) {
-      const float sm = sacc - scomp;
-      const float so = __shfl_xor(sm, 32);
-      if (hl == 0) sred[wave * SLICE_KEYS + n] = sm + so;
-      __syncthreads();
-      if (wave == 0 && hl == 0 && s_key0 + n < n_keys) {
-        const float tot = ((sred[n] + sred[SLICE_KEYS + n]) + sred[2 * SLICE_KEYS + n]) + sred[3 * SLICE_KEYS + n];
-        a.wsum[static_cast<size_t>(grp) * n_keys + s_key0 + n] = tot;
+      if (has_slice) {
+        const float sm = sacc - scomp;
+        const float so = __shfl_xor(sm, 32);
+        if (hl == 0) sred[wave * SLICE_KEYS + n] = sm + so;
+        __syncthreads();
+        if (wave == 0 && hl == 0 && s_key0 + n < n_keys) {
+          const float tot = ((sred[n] + sred[SLICE_KEYS + n]) + sred[2 * SLICE_KEYS + n]) + sred[3 * SLICE_KEYS + n];
+          a.wsum[static_cast<size_t>(grp) * n_keys + s_key0 + n] = tot;
+        }
       }
     }
   }
@@ -1266,15 +1276,20 @@ static bool fold_chunk_keys(const AttnArgs &a) {
   return a.n_occ > 0 && slices >= 1 && slices <= n_main && per_cu_fold < per_cu;
 }
 
+// An empty cache (a prefill chunk): key block k sees the rows from k*256/q_g
+// on, a linear profile, so blocks k and K-1-k together make one even item.
 template <int FMT>
 static void launch_b_fmt(const AttnArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
+  const int kblocks = (a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS;
   if (fold_chunk_keys(a)) {
     const int nB = groups * ((a.n_occ + PB_KEYS - 1) / PB_KEYS);
-    hipLaunchKernelGGL((attn_b_native<FMT, true>), dim3(nB), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_b_native<FMT, PB_FOLD>), dim3(nB), dim3(256), 0, s, a);
+  } else if (a.n_occ == 0 && kblocks >= 2) {
+    const int nB = groups * ((kblocks + 1) / 2);
+    hipLaunchKernelGGL((attn_b_native<FMT, PB_PAIR>), dim3(nB), dim3(256), 0, s, a);
   } else {
-    const int nB = groups * ((a.n_occ + a.T + PB_KEYS - 1) / PB_KEYS);
-    hipLaunchKernelGGL((attn_b_native<FMT, false>), dim3(nB), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_b_native<FMT, PB_PLAIN>), dim3(groups * kblocks), dim3(256), 0, s, a);
   }
 }
 

@@ -76,6 +76,8 @@ SDPA_CASES = [
     ("bf16", "native", 1, 8, 2, 128, 2048, 2048, 0),
     ("bf16", "int8", 1, 8, 2, 128, 1024, 1024, 0),
     ("bf16", "native", 2, 8, 4, 64, 640, 640, 0),
+    ("bf16", "native", 1, 8, 2, 128, 1100, 1100, 0),   # pass B pairs key blocks (5: middle one alone)
+    ("bf16", "int4", 1, 8, 2, 128, 768, 768, 0),       # 3 key blocks
     ("bf16", "int8", 1, 8, 2, 128, 4096, 16, 4096),     # quantised pass A split 16 ways
     ("bf16", "int4", 1, 32, 8, 128, 4096, 1, 4096),     # quantised decode, split
     ("bf16", "int4", 2, 8, 2, 128, 3000, 40, 2960),     # split, ragged
