@@ -91,6 +91,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
   const int my_row = row0 + wave * 32 + n;
   const bool row_ok = my_row < R;
   const int i_q = row_ok ? my_row / a.qg : 0;
+  // wave-uniform: all 32 rows exist; the smallest chunk position among them
+  const bool wave_rows_ok = row0 + wave * 32 + 31 < R;
+  const int wave_i_min = (row0 + wave * 32) / a.qg;
   const int h_q = g * a.qg + (row_ok ? my_row % a.qg : 0);
   const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
   const int n_occ = a.n_occ;
@@ -179,12 +182,22 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
       }
       // register r: key t*64 + 32*half + 16*(r/8) + 8*hl + r%8 of the lane's row
       bf16x8 dsb[2];
+      // wave-uniform: every row of the wave exists and sees every key of the half
+      const bool half_full = wave_rows_ok && t * 64 + 32 * half + 31 - n_occ <= wave_i_min;
+      if (half_full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ja = t * 64 + 32 * half + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
-        const bool vis = row_ok && ja <= i_q;
-        const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr)) : 0.f;
-        dsb[r >> 3][r & 7] = static_cast<__bf16>(pp * (p0[r] - Dr));
+        for (int r = 0; r < 16; ++r) {
+          const float pp = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr));
+          dsb[r >> 3][r & 7] = static_cast<__bf16>(pp * (p0[r] - Dr));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ja = t * 64 + 32 * half + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
+          const bool vis = row_ok && ja <= i_q;
+          const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr)) : 0.f;
+          dsb[r >> 3][r & 7] = static_cast<__bf16>(pp * (p0[r] - Dr));
+        }
       }
       // dQ^T += K^T dS^T over the half's keys (k-steps 2*half, 2*half + 1)
       bf16x8 kt = tr_operand(kb, 2 * half, 0, lane);
@@ -265,6 +278,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
   const int my_key = j_base + n;
   const bool key_ok = my_key < n_keys;
   const int t_key = my_key - n_occ;  // chunk position of the lane's key, < 0 for a cache slot
+  // wave-uniform: all 32 keys of the wave exist; the chunk position of its last key
+  const bool wave_keys_ok = j_base + 31 < n_keys;
+  const int wave_tmax = j_base + 31 - n_occ;
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
   const float sl2 = a.sl2;
@@ -345,6 +361,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // register r: row rb + 32*sub + 16*(r/8) + 8*hl + r%8 of the lane's key
+      const int r0 = rb + 32 * sub;
+      const bool sub_full = wave_keys_ok && r0 + 31 < R && r0 >= wave_tmax * a.qg;
       bf16x8 pa[2], sa[2];
 #pragma unroll
       for (int h8 = 0; h8 < 2; ++h8) {
@@ -355,14 +373,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
         const float4 D1 = *reinterpret_cast<const float4 *>(db + rib0 + 4);
         const float Lv[8] = {L0.x, L0.y, L0.z, L0.w, L1.x, L1.y, L1.z, L1.w};
         const float Dv[8] = {D0.x, D0.y, D0.z, D0.w, D1.x, D1.y, D1.z, D1.w};
+        if (sub_full) {  // every row of the sub-block sees all the wave's keys
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int r = 8 * h8 + e;
-          const int row = rb + rib0 + e;
-          const bool vis = key_ok && row < R && row >= t_key * a.qg;  // t_key < 0: every row
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(c[r], sl2, -Lv[e])) : 0.f;
-          pa[h8][e] = static_cast<__bf16>(p);
-          sa[h8][e] = static_cast<__bf16>(p * (dp[r] - Dv[e]));
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * h8 + e;
+            const float p = __builtin_amdgcn_exp2f(fmaf(c[r], sl2, -Lv[e]));
+            pa[h8][e] = static_cast<__bf16>(p);
+            sa[h8][e] = static_cast<__bf16>(p * (dp[r] - Dv[e]));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int r = 8 * h8 + e;
+            const int row = rb + rib0 + e;
+            const bool vis = key_ok && row < R && row >= t_key * a.qg;  // t_key < 0: every row
+            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(c[r], sl2, -Lv[e])) : 0.f;
+            pa[h8][e] = static_cast<__bf16>(p);
+            sa[h8][e] = static_cast<__bf16>(p * (dp[r] - Dv[e]));
+          }
         }
       }
       // dV += P^T dO, dK += dS^T Q; k-step ks covers rows 16*ks .. 16*ks + 15 of the sub-block
