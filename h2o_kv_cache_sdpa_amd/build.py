@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libh2o.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["h2o_abi.cpp", "profile.cpp", "attn_simple.hip", "attn_mfma.hip", "attn_native.hip", "attn_quant.hip", "attn_bwd.hip", "evict.hip", "kvwrite.hip"]
+SOURCES = ["h2o_abi.cpp", "profile.cpp", "attn_simple.hip", "attn_mfma.hip", "attn_native.hip", "attn_quant.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "evict.hip", "kvwrite.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is issued as a
 # scalar-per-lane instruction.  No fast-math: the quantisers rely on IEEE
@@ -34,9 +34,17 @@ COMMON = [
 ]
 
 
+# Per-source flags.  The dQ kernel runs one wavefront per SIMD with more than
+# 256 registers; by default the S / dP results of its MFMAs land in
+# accumulation registers and are copied out before every exponential.  The
+# VGPR form of the MFMAs keeps them where the vector ALU reads them (measured
+# faster for dQ, slower for the dK/dV kernel, which keeps the default).
+EXTRA = {"attn_bwd_dq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

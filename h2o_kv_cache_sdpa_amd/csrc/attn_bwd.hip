@@ -12,11 +12,8 @@
 //
 // Three kernels, no atomics (every output element has one writer):
 //  * bwd_rows: L2_r and D_r, one 16-lane group per row;
-//  * bwd_dq: 128 query rows per workgroup (4 waves x 32), K and V tiles of 64
-//    keys moved HBM -> LDS by buffer-load DMA, double-buffered.  S^T = K Q^T
-//    and dP^T = V dO^T on the matrix cores with Q and dO held in registers;
-//    dS in registers becomes the B operand of dQ^T += K^T dS^T, the K^T operand
-//    read from the row-major K tile by ds_read_b64_tr_b16 (as V^T in pass A);
+//  * bwd_dq (attn_bwd_dq.hip): 128 query rows per workgroup, K and V tiles
+//    streamed (its own file: it is compiled with MFMA results in VGPRs);
 //  * bwd_dkdv: 128 keys per workgroup (4 waves x 32) held in registers as
 //    MFMA operands; 64-row blocks of Q and dO (and L2, D) stream through LDS,
 //    double-buffered.  Q rows enter S = Q K^T in the same permuted order pass A
@@ -54,197 +51,6 @@ __global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
   if (r < rows && c == 0) {
     a.dd[r] = acc;
     a.l2[r] = a.lse[r] * LOG2E;
-  }
-}
-
-// Transpose read of a K/Q-swizzled tile: for lane l the 8 rows
-// 16*ks + 8*(l/32) + 0..7 at column 32*blk + l%32 (the A operand of a product
-// whose K dimension runs along the tile's rows).
-__device__ __forceinline__ bf16x8 tr_operand(const char *tb, int ks, int blk, int lane) {
-  const int grp16 = lane >> 4, i16 = lane & 15;
-  const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
-  const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
-  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row, col >> 3) + 2 * (col & 7)));
-  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row + 4, col >> 3) + 2 * (col & 7)));
-  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// ---------------------------------------------------------------------------
-// dQ: 128 packed query rows per block (r = i * q_g + h), keys streamed
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 31, hl = lane >> 5;
-  const int R = a.qg * a.T;
-  const int tiles_per_grp = (R + 127) / 128;
-  const int wi = xcd_remap(blockIdx.x, gridDim.x);
-  // Row blocks go out last first: under the causal mask the last rows see the
-  // most keys, and starting the longest blocks first evens out the tail.
-  const int grp = wi / tiles_per_grp, rt = tiles_per_grp - 1 - wi % tiles_per_grp;
-  const int g = grp % a.Hkv, b = grp / a.Hkv;
-  const int row0 = rt * 128;
-  const int my_row = row0 + wave * 32 + n;
-  const bool row_ok = my_row < R;
-  const int i_q = row_ok ? my_row / a.qg : 0;
-  // wave-uniform: all 32 rows exist; the smallest chunk position among them
-  const bool wave_rows_ok = row0 + wave * 32 + 31 < R;
-  const int wave_i_min = (row0 + wave * 32) / a.qg;
-  const int h_q = g * a.qg + (row_ok ? my_row % a.qg : 0);
-  const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
-  const int n_occ = a.n_occ;
-  const float sl2 = a.sl2;
-
-  // Q and dO rows: B operands of S^T = K Q^T and dP^T = V dO^T
-  bf16x8 qf[8], gf[8];
-  {
-    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) + li * D;
-    const uint16_t *grow = static_cast<const uint16_t *>(a.dout) + li * D;
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      uint4 vq = make_uint4(0, 0, 0, 0), vg = make_uint4(0, 0, 0, 0);
-      if (row_ok) {
-        vq = *reinterpret_cast<const uint4 *>(qrow + 16 * st + 8 * hl);
-        vg = *reinterpret_cast<const uint4 *>(grow + 16 * st + 8 * hl);
-      }
-      qf[st] = __builtin_bit_cast(bf16x8, vq);
-      gf[st] = __builtin_bit_cast(bf16x8, vg);
-    }
-  }
-  const float Lr = row_ok ? a.l2[li] : 0.f;
-  const float Dr = row_ok ? a.dd[li] : 0.f;
-
-  const int last_row = min(R, row0 + 128) - 1;
-  const int key_end = n_occ + last_row / a.qg + 1;
-  const int ntiles = (key_end + 63) / 64;
-  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
-  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
-  const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
-  const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
-  const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
-  const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
-  // both tiles in the K/Q swizzle: read row-wise for S^T / dP^T and (K) transposed for dQ
-  auto lane_off = [&](int q) -> uint32_t {
-    const int row = (wave * 4 + q) * 4 + (lane >> 4);
-    return static_cast<uint32_t>(row * ROW_BYTES + 16 * kq_chunk_at(row, lane & 15));
-  };
-  auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs) {
-    const int j0 = tile * 64;
-    if (j0 + 64 <= n_occ) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
-    } else {
-      const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = (wave * 4 + q) * 4 + (lane >> 4);
-        const uint32_t lo = lane_off(q);
-        if (dt + row >= 0) {
-          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
-        } else {
-          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
-        }
-      }
-    }
-  };
-
-  const int prow = perm_key(n);
-  f32x16 dq[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) dq[k] = f32x16{};
-
-  // One 64-key tile in two halves of 32 keys (keeps one S / dP pair live).
-  auto compute = [&](int t, const char *kb, const char *vb) {
-#pragma unroll 1
-    for (int half = 0; half < 2; ++half) {
-      const int kr = 32 * half + prow;  // K / V row of the lane's operand
-      f32x16 s0 = f32x16{}, p0 = f32x16{};
-      // operands one step ahead of their MFMAs; the barriers keep the compiler
-      // from hoisting every step's reads (and their registers) to the top
-      bf16x8 k0 = lds16(kb + kq_off(kr, hl)), v0 = lds16(vb + kq_off(kr, hl));
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        bf16x8 nk0 = k0, nv0 = v0;
-        if (st < 7) {
-          nk0 = lds16(kb + kq_off(kr, 2 * st + 2 + hl));
-          nv0 = lds16(vb + kq_off(kr, 2 * st + 2 + hl));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        s0 = mfma32(k0, qf[st], s0);
-        p0 = mfma32(v0, gf[st], p0);
-        k0 = nk0;
-        v0 = nv0;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // register r: key t*64 + 32*half + 16*(r/8) + 8*hl + r%8 of the lane's row
-      bf16x8 dsb[2];
-      // wave-uniform: every row of the wave exists and sees every key of the half
-      const bool half_full = wave_rows_ok && t * 64 + 32 * half + 31 - n_occ <= wave_i_min;
-      if (half_full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pp = __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr));
-          dsb[r >> 3][r & 7] = static_cast<__bf16>(pp * (p0[r] - Dr));
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ja = t * 64 + 32 * half + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
-          const bool vis = row_ok && ja <= i_q;
-          const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr)) : 0.f;
-          dsb[r >> 3][r & 7] = static_cast<__bf16>(pp * (p0[r] - Dr));
-        }
-      }
-      // dQ^T += K^T dS^T over the half's keys (k-steps 2*half, 2*half + 1)
-      bf16x8 kt = tr_operand(kb, 2 * half, 0, lane);
-#pragma unroll
-      for (int step = 0; step < 8; ++step) {
-        const int ks = step >> 2, blk = step & 3;
-        bf16x8 nkt = kt;
-        if (step < 7) nkt = tr_operand(kb, 2 * half + ((step + 1) >> 2), (step + 1) & 3, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        dq[blk] = mfma32(kt, dsb[ks], dq[blk]);
-        kt = nkt;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  };
-
-  if (ntiles > 0) {
-    issue_tile(0, kb0, kc_rs, kn_rs);
-    issue_tile(0, vb0, vc_rs, vn_rs);
-  }
-  for (int t = 0; t < ntiles; t += 2) {
-    wait_dma_and_sync();  // tile t in kb0/vb0; everybody done with kb1/vb1
-    if (t + 1 < ntiles) {
-      issue_tile(t + 1, kb1, kc_rs, kn_rs);
-      issue_tile(t + 1, vb1, vc_rs, vn_rs);
-    }
-    compute(t, kb0, vb0);
-    if (t + 1 >= ntiles) break;
-    wait_dma_and_sync();  // tile t+1 in kb1/vb1; everybody done with kb0/vb0
-    if (t + 2 < ntiles) {
-      issue_tile(t + 2, kb0, kc_rs, kn_rs);
-      issue_tile(t + 2, vb0, vc_rs, vn_rs);
-    }
-    compute(t + 1, kb1, vb1);
-  }
-
-  if (!row_ok) return;
-  float *dst = a.dq + li * D;
-#pragma unroll
-  for (int blk = 0; blk < 4; ++blk) {
-#pragma unroll
-    for (int a4 = 0; a4 < 4; ++a4) {
-      const int d = 32 * blk + 8 * a4 + 4 * hl;
-      *reinterpret_cast<float4 *>(dst + d) =
-          make_float4(dq[blk][4 * a4] * a.scale, dq[blk][4 * a4 + 1] * a.scale,
-                      dq[blk][4 * a4 + 2] * a.scale, dq[blk][4 * a4 + 3] * a.scale);
-    }
   }
 }
 
@@ -450,15 +256,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
 
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
-  const int R = a.qg * a.T;
   const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
   {
     KernelTimer timer(H2O_K_BWD_ROWS, s);
     hipLaunchKernelGGL(bwd_rows, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, a);
   }
   {
-    KernelTimer timer(H2O_K_BWD_DQ, s);
-    hipLaunchKernelGGL(bwd_dq, dim3(groups * ((R + 127) / 128)), dim3(256), 0, s, a);
+    const hipError_t e = launch_bwd_dq(a, s);
+    if (e != hipSuccess) return e;
   }
   {
     KernelTimer timer(H2O_K_BWD_DKDV, s);

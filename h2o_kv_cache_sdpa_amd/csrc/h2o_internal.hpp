@@ -70,6 +70,7 @@ struct BwdArgs {
   int B, Hq, Hkv, C, T, qg, n_occ;
   float scale, sl2;
 };
+hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t s);  // dQ kernel (attn_bwd_dq.hip)
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t s);
 
 // Brackets one kernel launch with hipEvents on `s` while timing is enabled

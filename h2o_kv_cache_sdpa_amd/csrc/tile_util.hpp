@@ -71,6 +71,18 @@ __device__ __forceinline__ i16x4 lds_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
+// Transpose read of a K/Q-swizzled tile: for lane l the 8 rows
+// 16*ks + 8*(l/32) + 0..7 at column 32*blk + l%32 (the A operand of a product
+// whose K dimension runs along the tile's rows).
+__device__ __forceinline__ bf16x8 tr_operand(const char *tb, int ks, int blk, int lane) {
+  const int grp16 = lane >> 4, i16 = lane & 15;
+  const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
+  const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row, col >> 3) + 2 * (col & 7)));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row + 4, col >> 3) + 2 * (col & 7)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ int perm_key(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
