@@ -244,6 +244,7 @@ POLICY_CASES = [
     (2, 2, 512, 64, 128),        # filling: the same under every policy
     (2, 1, 300, 300, 300),       # T == C
     (2, 2, 8192, 16, 8192),      # short chunk
+    (2, 2, 8192, 4, 8192),       # 2..8 tokens: rounds of the block minimum
 ]
 
 

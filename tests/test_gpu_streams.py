@@ -127,6 +127,14 @@ def test_stream_policies_bf16_batch(policy):
 
 
 @pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
+def test_stream_policies_short_chunks_batch(policy):
+    """Four-token chunks, B = 2: the rounds selection, and the pick writing
+    the K/V rows of every batch row it serves (one selection per KV head
+    under h2o_orig)."""
+    _run_stream(W.WORKLOADS[3].scaled(B=2, C=256, T=4, n_fill=64, n_evict=6), policy=policy)
+
+
+@pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
 def test_stream_policies_int4_batch(policy):
     _run_stream(W.WORKLOADS[5].scaled(C=512, T=32, n_fill=16, n_evict=8), policy=policy)
 
