@@ -89,8 +89,10 @@ __device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4]) {
 }
 
 // LG: also store every tile's logits (in log2 units) for short chunks (a.lg).
-template <int FMT, bool LG>
-__global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
+// NW: wavefronts per block (4 or 8), 32 rows each; a widened tile serves them all.
+template <int FMT, bool LG, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
+  constexpr int ROWS = 32 * NW;
   using Q = QTile<FMT>;
   __shared__ __attribute__((aligned(1024))) char kb[TILE_BYTES];  // bf16 K tile (K/Q swizzle)
   __shared__ __attribute__((aligned(1024))) char vb[TILE_BYTES];  // bf16 V tile (V swizzle)
@@ -106,7 +108,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hl = lane >> 5;
   const int R = a.qg * a.T;
-  const int tiles_per_grp = (R + 127) / 128;
+  const int tiles_per_grp = (R + ROWS - 1) / ROWS;
   const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
   const int split = wi_all % a.nsplit;
   const int wi = wi_all / a.nsplit;
@@ -114,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
   // most keys, and starting the longest blocks first evens out the tail.
   const int grp = wi / tiles_per_grp, rt = tiles_per_grp - 1 - wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
-  const int row0 = rt * 128;
+  const int row0 = rt * ROWS;
   const int wrow0 = row0 + wave * 32;
   const int my_row = wrow0 + n;
   const bool row_ok = my_row < R;
@@ -142,7 +144,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
     if constexpr (FMT == FMT_INT4) qsum += __shfl_xor(qsum, 32);
   }
 
-  const int last_row = min(R, row0 + 128) - 1;
+  const int last_row = min(R, row0 + ROWS) - 1;
   const int key_end = n_occ + last_row / a.qg + 1;
   const int ntiles_all = (key_end + 63) / 64;
   const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
                             : make_rsrc(static_cast<const char *>(a.vc) + (cache_row0 + j0) * Q::CODE_ROW,
                                         rows_left * Q::CODE_ROW);
     const uint32_t soff = whole ? static_cast<uint32_t>(j0 * Q::CODE_ROW) : 0u;
-    for (int sgm = wave; sgm < Q::SEGS; sgm += 4) {
+    for (int sgm = wave; sgm < Q::SEGS; sgm += NW) {
       const uint32_t off = static_cast<uint32_t>(sgm * 1024 + 16 * lane);
       dma16(kr, off, soff, kdst + sgm * 1024);
       dma16(vr, off, soff, vdst + sgm * 1024);
@@ -372,13 +374,13 @@ __global__ __launch_bounds__(256, 2) void attn_a_quant(AttnArgs a) {
   for (int t = 0; t < ntiles; t += 2) {
     wait_dma_and_sync();  // codes(t) in slot 0; everyone done with tile t-1
     if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
-    widen_tile(t, kc0, vc0, fc0);
+    if (wave < 4) widen_tile(t, kc0, vc0, fc0);  // 256 threads: 4 per key row
     lds_barrier();
     compute_tile(t);
     if (t + 1 >= ntiles) break;
     wait_dma_and_sync();  // codes(t+1) in slot 1
     if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
-    widen_tile(t + 1, kc1, vc1, fc1);
+    if (wave < 4) widen_tile(t + 1, kc1, vc1, fc1);
     lds_barrier();
     compute_tile(t + 1);
   }
@@ -775,18 +777,21 @@ hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s) {
     }
     return hipGetLastError();
   }
+  auto launch_long = [&](auto fmt_tag) {
+    constexpr int FMT = decltype(fmt_tag)::value;
+    if (a.lg) {
+      hipLaunchKernelGGL((attn_a_quant<FMT, true, 4>), dim3(nA), dim3(256), 0, s, a);
+    } else if (R >= 256) {  // long chunks: 256 rows per block share each widened tile
+      const int n8 = groups * ((R + 255) / 256) * a.nsplit;
+      hipLaunchKernelGGL((attn_a_quant<FMT, false, 8>), dim3(n8), dim3(512), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((attn_a_quant<FMT, false, 4>), dim3(nA), dim3(256), 0, s, a);
+    }
+  };
   if (a.cache_fmt == FMT_INT8) {
-    if (a.lg) {
-      hipLaunchKernelGGL((attn_a_quant<FMT_INT8, true>), dim3(nA), dim3(256), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((attn_a_quant<FMT_INT8, false>), dim3(nA), dim3(256), 0, s, a);
-    }
+    launch_long(std::integral_constant<int, FMT_INT8>{});
   } else {
-    if (a.lg) {
-      hipLaunchKernelGGL((attn_a_quant<FMT_INT4, true>), dim3(nA), dim3(256), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((attn_a_quant<FMT_INT4, false>), dim3(nA), dim3(256), 0, s, a);
-    }
+    launch_long(std::integral_constant<int, FMT_INT4>{});
   }
   return hipGetLastError();
 }
