@@ -350,10 +350,26 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
   }
   uint32_t less_before, eq_before;
   block_scan2<NT>(nl, ne, less_before, eq_before, sh);
+  const float *w0 = a.wsum + grp0 * n_keys;
+  if constexpr (STAGE) {
+    // Each taken slot goes to LDS at its position in the log (the staging
+    // buffer is free: the keys are in registers); then thread i serves
+    // position i, so the seeds (the chunk's own sums) are read and the log
+    // written in order and only the score / position stores scatter.
+    int *taken = reinterpret_cast<int *>(stage);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const int out = k < nvalid ? rank_in_selection(key[k], theta, take_eq, less_before, eq_before) : -1;
+      if (out >= 0) taken[out] = base + k;
+    }
+    __syncthreads();
+    for (int i = tid; i < T; i += NT) take_slot<POL>(a, head, taken[i], i, w0[C + i]);
+    return;
+  }
   // UB slots at a time: positions, then the batch's seeds, then its stores
   // (see update_scores)
   constexpr int UB = ITEMS < 8 ? ITEMS : 8;
-  const float *w0 = a.wsum + grp0 * n_keys;
 #pragma unroll
   for (int k0 = 0; k0 < ITEMS; k0 += UB) {
     int out[UB];
