@@ -174,13 +174,25 @@ __device__ __forceinline__ void select_smallest(uint32_t (&key)[ITEMS], int nval
         }
         sh.sel = d;
         sh.k = need - c;
+        const uint32_t dd = d - 4u * tid;
+        sh.b[0] = dd == 0 ? c0 : dd == 1 ? c1 : dd == 2 ? c2 : c3;  // keys in the digit
       }
     }
     __syncthreads();
     prefix |= sh.sel << shift;
     pmask |= dmask << shift;
     need = sh.k;
+    // Every key of the boundary digit is taken: the keys below prefix + 2^shift
+    // are exactly the selection, no lower digit to resolve (common for
+    // distinct scores after two digits).
+    const bool whole = shift > 0 && need == sh.b[0] &&
+                       static_cast<uint64_t>(prefix) + (1ull << shift) <= 0xffffffffull;
     __syncthreads();
+    if (whole) {
+      theta = prefix + (1u << shift);
+      take_eq = 0;
+      return;
+    }
   }
   theta = prefix;
   take_eq = need;
