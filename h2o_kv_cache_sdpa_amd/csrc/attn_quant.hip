@@ -39,6 +39,15 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Orders LDS accesses between the lanes of one wavefront.  A wavefront's LDS
+// instructions execute in issue order, so no wait is needed: the fences only
+// keep the compiler from moving memory operations across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int FMT>
 struct QTile {
   static constexpr int CODE_ROW = (FMT == FMT_INT8) ? 128 : 64;  // bytes of codes per key
@@ -494,21 +503,25 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   // Codes move HBM -> registers with plain vector loads, PD tiles ahead of
   // their use: thread tid holds the 32 codes of key row tid / 4, quarter
   // tid % 4, of K and of V (int8: 2 x 16 bytes each, int4: 16 bytes), and
-  // threads 0..63 the fp16 factors of key tid.  Loads into registers keep
-  // their order in the vector-memory counter, so each tile waits only for
-  // its own loads; an LDS-DMA pipeline this deep would wait for all.
+  // lane l < 16 of wavefront w the fp16 factors of key 16w + l.  Loads into
+  // registers keep their order in the vector-memory counter, so each tile
+  // waits only for its own loads; an LDS-DMA pipeline this deep would wait
+  // for all.  Wavefront w widens, stores and reads back only the rows of its
+  // own keys 16w .. 16w + 15, so the wavefronts never wait for each other
+  // inside the tile loop.
   constexpr int CW = Q::CODE_ROW / 4 / 16;  // 16-byte words of one thread's share
-  constexpr int PD = (FMT == FMT_INT8) ? 3 : 4;
+  constexpr int PD = (FMT == FMT_INT8) ? 2 : 3;
   struct Codes {
     uint4 k[CW], v[CW];
     uint16_t f[Q::NFAC];
   };
   const uint16_t *fsrc[4] = {a.ks, a.vs, a.kz, a.vz};
-  const int crow = tid >> 2, cq = tid & 3;
+  const int crow = tid >> 2, cq = tid & 3;   // crow = 16 * wave + lane / 4
+  const int fkey = 16 * wave + (lane & 15);  // key of the factors lane < 16 holds
   // Tiles 0 .. nfull-1 of the split lie wholly in the cache: their loads
   // are unconditional, so the compiler can count them (a tile past nfull
-  // reloads tile nfull - 1, an L2 hit; every wavefront loads the factors of
-  // key tid % 64).  The rest (the tile that straddles n_occ, chunk rows)
+  // reloads tile nfull - 1, an L2 hit; every lane loads the factors of key
+  // fkey).  The rest (the tile that straddles n_occ, chunk rows)
   // take a direct path after the main loop.
   const int nfull = max(0, min(ntiles, n_occ / 64 - t_lo));
   auto load_codes = [&](int tile, Codes &c) {
@@ -520,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
       c.v[w] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.vc) + off + 16 * w);
     }
 #pragma unroll
-    for (int f = 0; f < Q::NFAC; ++f) c.f[f] = fsrc[f][cache_row0 + j0 + (tid & 63)];
+    for (int f = 0; f < Q::NFAC; ++f) c.f[f] = fsrc[f][cache_row0 + j0 + fkey];
   };
   auto store = [&](char *kb, char *vb, const uint4 (&kw)[4], const uint4 (&vw)[4]) {
 #pragma unroll
@@ -530,11 +543,11 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     }
   };
   auto store_fac = [&](float (*fac)[64], bool cached, const uint16_t *f) {
-    fac[0][tid] = cached ? f16_to_f32(f[0]) * a.sl2 : a.sl2;
-    fac[2][tid] = cached ? f16_to_f32(f[1]) : 1.f;
+    fac[0][fkey] = cached ? f16_to_f32(f[0]) * a.sl2 : a.sl2;
+    fac[2][fkey] = cached ? f16_to_f32(f[1]) : 1.f;
     if constexpr (FMT == FMT_INT4) {
-      fac[1][tid] = cached ? f16_to_f32(f[2]) * a.sl2 : 0.f;
-      fac[3][tid] = cached ? f16_to_f32(f[3]) : 0.f;
+      fac[1][fkey] = cached ? f16_to_f32(f[2]) * a.sl2 : 0.f;
+      fac[3][fkey] = cached ? f16_to_f32(f[3]) : 0.f;
     }
   };
   // a tile wholly in the cache, from the prefetched registers
@@ -543,7 +556,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     widen32<FMT>(reinterpret_cast<const char *>(c.k), kw);
     widen32<FMT>(reinterpret_cast<const char *>(c.v), vw);
     store(kb, vb, kw, vw);
-    if (tid < 64) store_fac(fac, true, c.f);
+    if (lane < 16) store_fac(fac, true, c.f);
   };
   // any other tile, loading as it goes: codes of rows below n_occ, new keys
   // (bf16) above, zeros past the chunk
@@ -568,12 +581,12 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
       }
     }
     store(kb, vb, kw, vw);
-    if (tid < 64) {
-      const bool cached = j0 + tid < n_occ;
+    if (lane < 16) {
+      const bool cached = j0 + fkey < n_occ;
       uint16_t f[4] = {0, 0, 0, 0};
       if (cached) {
 #pragma unroll
-        for (int q = 0; q < Q::NFAC; ++q) f[q] = fsrc[q][cache_row0 + j0 + tid];
+        for (int q = 0; q < Q::NFAC; ++q) f[q] = fsrc[q][cache_row0 + j0 + fkey];
       }
       store_fac(fac, cached, f);
     }
@@ -649,8 +662,10 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   };
 
   // Tile t: widen into buffer t & 1, refill its registers with tile t + PD,
-  // one barrier, compute.  The barrier also orders every wavefront's compute
-  // of tile t - 1 before the widening of tile t + 1 into the same buffer.
+  // compute.  Lanes read rows that other lanes of their wavefront wrote;
+  // wave_lds_sync keeps the reads of tile t after its writes, and (one tile
+  // on) the reads of tile t - 1 before the writes of tile t + 1 into the
+  // same buffer.
   // Groups of G tiles are unrolled straight-line: the compiler counts the
   // loads in flight exactly there, while across a loop back-edge it waits
   // for all of them (so it drains once per group, not once per tile).
@@ -669,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
         if (t < nfull) widen_full(cr[p % PD], kb, vb, fac);
         load_codes(t + PD, cr[p % PD]);
         if (t < nfull) {
-          __syncthreads();
+          wave_lds_sync();
           compute(t, kb, vb, fac);
         }
       }
@@ -680,7 +695,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     char *vb = (t & 1) ? vb1 : vb0;
     float (*fac)[64] = (t & 1) ? fac1 : fac0;
     widen_direct(t, kb, vb, fac);
-    __syncthreads();
+    wave_lds_sync();
     compute(t, kb, vb, fac);
   }
 
