@@ -54,12 +54,12 @@ def dominant_kernel(w):
 
 
 def kernel_sources_digest():
-    """Digest of the sources the attention kernels are built from; a stored
-    HBM-traffic measurement is only reported while it still matches."""
+    """Digest of the sources the measured pass-A kernel (attn_a_native) and
+    its dispatch are built from; a stored HBM-traffic measurement is only
+    reported while it still matches."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "h2o_kv_cache_sdpa_amd", "csrc")
-    for name in ("attn_native.hip", "attn_mfma.hip", "attn_quant.hip", "tile_util.hpp", "device_util.hpp",
-                 "h2o_internal.hpp"):
+    for name in ("attn_native.hip", "attn_mfma.hip", "tile_util.hpp", "device_util.hpp", "h2o_internal.hpp"):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
