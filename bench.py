@@ -249,6 +249,65 @@ def sweep_small_t(args):
             torch.cuda.empty_cache()
 
 
+def replay(args):
+    """Replay steps: the chunk's attention and the overwrite of the slots a
+    recorded log row names, with no weight sums, scores or selection.  The
+    log rows are recorded by chunk steps over the same rotation of chunks;
+    the chunk step is timed beside the replay step on the same cache."""
+    import torch
+
+    from h2o_kv_cache_sdpa_amd import api
+    from h2o_kv_cache_sdpa_amd import workloads as W
+    dev = torch.device("cuda:0")
+    for wid in (int(x) for x in args.replay_workloads.split(",")):
+        w = W.WORKLOADS[wid]
+        B, T, C = w.B, w.T, w.C
+        gc, chunks = _resident_setup(w, "h2o", dev)
+        out, wsum, slot_log = gc.new_outputs(C)
+        bufs = gc.bufs()
+        stream = torch.cuda.current_stream()
+        logs = []
+
+        def chunk_step(i):
+            q, kn, vn = chunks[i % N_CHUNKS]
+            api.h2o_chunk_step(gc.dims, bufs, C, gc.pos, q, kn, vn, out, wsum, slot_log, gc.ws, stream)
+            gc.pos += T
+
+        def replay_step(i):
+            q, kn, vn = chunks[i % N_CHUNKS]
+            api.h2o_replay_step(gc.dims, bufs, C, gc.pos, q, kn, vn, out, logs[i % N_CHUNKS], gc.ws, stream)
+            gc.pos += T
+
+        for i in range(N_CHUNKS):
+            chunk_step(i)
+            logs.append(slot_log.clone())
+        res = {}
+        for name, fn in (("chunk_step", chunk_step), ("replay_step", replay_step)):
+            for i in range(args.warmup):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            api.profile_reset()
+            api.profile_enable(True)
+            for i in range(args.steps):
+                fn(i)
+            torch.cuda.synchronize()
+            api.profile_enable(False)
+            prof = api.profile_read()
+            res[name] = {"ms_per_step": ms, "tokens_per_s": B * T / (ms * 1e-3),
+                         "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items() if v[1]}}
+        print(json.dumps({"mode": "replay", "workload": w.name, "B": B, "cache_slots": C, "chunk": T,
+                          "cache_fmt": w.cache_fmt, **res}), flush=True)
+        del gc, chunks, out, wsum, slot_log, logs
+        torch.cuda.empty_cache()
+
+
 def prefill(args):
     """First chunk of a sequence on an empty cache: n_occ = 0, T = C, a causal
     square with summed weights (the pages' length-N_C prefill)."""
@@ -391,6 +450,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time h2o_sdpa_backward on the 32K evicting step and a 16K prefill square")
     ap.add_argument("--prefill-sizes", default="16384,32768", help="cache sizes (= chunk lengths) of --prefill")
+    ap.add_argument("--replay", action="store_true",
+                    help="time h2o_replay_step beside h2o_chunk_step on full caches: one JSON line per workload")
+    ap.add_argument("--replay-workloads", default="3,4,5", help="workloads of --replay")
     ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
     ap.add_argument("--sweep-ts", default="1,4,16,64,128", help="chunk lengths of --sweep-small-t")
     args = ap.parse_args()
@@ -402,6 +464,9 @@ def main():
         return
     if args.backward:
         backward(args)
+        return
+    if args.replay:
+        replay(args)
         return
     if args.sweep_small_t:
         sweep_small_t(args)
