@@ -195,31 +195,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   };
 
   // ---- codes (or chunk rows) of the current tile -> bf16 tiles, factors ----
-  const int crow = tid >> 2, cq = tid & 3;  // key row and 32-element quarter this thread widens
-  auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64]) {
-    const int j0 = (t_lo + tile) * 64;
-    const int j = j0 + crow;
-    uint4 kw[4], vw[4];
+  // Thread tid widens the 32-element quarter tid % 4 of key row (tid % 256) / 4:
+  // of K and V with 4 wavefronts, of K (wavefronts 0-3) or V (4-7) with 8.
+  const int crow = (tid & 255) >> 2, cq = tid & 3;
+  auto widen_rows = [&](int j, const char *cs, const void *nsrc, char *dst, bool is_v) {
+    uint4 w[4];
     if (j < n_occ) {
-      widen32<FMT>(kcs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), kw);
-      widen32<FMT>(vcs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), vw);
+      widen32<FMT>(cs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), w);
     } else {
       const int t = j - n_occ;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        kw[i] = vw[i] = make_uint4(0, 0, 0, 0);
-        if (t < a.T) {
-          const size_t e = (new_row0 + t) * D + 32 * cq + 8 * i;
-          kw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.kn) + e);
-          vw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.vn) + e);
-        }
+        w[i] = make_uint4(0, 0, 0, 0);
+        if (t < a.T) w[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(nsrc) +
+                                                               (new_row0 + t) * D + 32 * cq + 8 * i);
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4 *>(kb + kq_off(crow, 4 * cq + i)) = kw[i];
-      *reinterpret_cast<uint4 *>(vb + v_off(crow, 4 * cq + i)) = vw[i];
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4 *>(dst + (is_v ? v_off(crow, 4 * cq + i) : kq_off(crow, 4 * cq + i))) = w[i];
+  };
+  auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64]) {
+    const int j0 = (t_lo + tile) * 64;
+    const int j = j0 + crow;
+    if (NW == 4 || wave < 4) widen_rows(j, kcs, a.kn, kb, false);
+    if (NW == 4 || wave >= 4) widen_rows(j, vcs, a.vn, vb, true);
     if (tid < 64) {
       const bool cached = j0 + tid < n_occ;
       fac[0][tid] = cached ? f16_to_f32(fcs[0][tid]) * a.sl2 : a.sl2;
@@ -383,13 +383,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   for (int t = 0; t < ntiles; t += 2) {
     wait_dma_and_sync();  // codes(t) in slot 0; everyone done with tile t-1
     if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
-    if (wave < 4) widen_tile(t, kc0, vc0, fc0);  // 256 threads: 4 per key row
+    widen_tile(t, kc0, vc0, fc0);
     lds_barrier();
     compute_tile(t);
     if (t + 1 >= ntiles) break;
     wait_dma_and_sync();  // codes(t+1) in slot 1
     if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
-    if (wave < 4) widen_tile(t + 1, kc1, vc1, fc1);
+    widen_tile(t + 1, kc1, vc1, fc1);
     lds_barrier();
     compute_tile(t + 1);
   }
