@@ -103,16 +103,19 @@ template <int FMT, bool LG, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
   using Q = QTile<FMT>;
-  __shared__ __attribute__((aligned(1024))) char kb[TILE_BYTES];  // bf16 K tile (K/Q swizzle)
-  __shared__ __attribute__((aligned(1024))) char vb[TILE_BYTES];  // bf16 V tile (V swizzle)
+  // bf16 tiles: two with 8 wavefronts (one block per CU), so that tile t+1 is
+  // widened beside the compute of tile t; one with 4 (two blocks per CU)
+  constexpr int NB = NW == 8 ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) char kbs[NB][TILE_BYTES];  // bf16 K tile (K/Q swizzle)
+  __shared__ __attribute__((aligned(1024))) char vbs[NB][TILE_BYTES];  // bf16 V tile (V swizzle)
   __shared__ __attribute__((aligned(1024))) char kc0[Q::CODE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vc0[Q::CODE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kc1[Q::CODE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vc1[Q::CODE_BYTES];
   __shared__ __attribute__((aligned(256))) uint16_t fc0[Q::NFAC][64];  // fp16 factors, slot 0
   __shared__ __attribute__((aligned(256))) uint16_t fc1[Q::NFAC][64];  // fp16 factors, slot 1
-  // factors of the current tile: [0] sl2*s_k, [1] sl2*z_k, [2] s_v, [3] z_v (chunk keys: sl2, 0, 1, 0)
-  __shared__ __attribute__((aligned(256))) float fac[4][64];
+  // factors of a widened tile: [0] sl2*s_k, [1] sl2*z_k, [2] s_v, [3] z_v (chunk keys: sl2, 0, 1, 0)
+  __shared__ __attribute__((aligned(256))) float facs[NB][4][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hl = lane >> 5;
@@ -215,7 +218,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<uint4 *>(dst + (is_v ? v_off(crow, 4 * cq + i) : kq_off(crow, 4 * cq + i))) = w[i];
   };
-  auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64]) {
+  auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64], char *kb,
+                        char *vb, float (*fac)[64]) {
     const int j0 = (t_lo + tile) * 64;
     const int j = j0 + crow;
     if (NW == 4 || wave < 4) widen_rows(j, kcs, a.kn, kb, false);
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   for (int k = 0; k < 4; ++k) o[k] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f, u_run = 0.f;
 
-  auto v_operand = [&](int s) {
+  auto v_operand = [&](const char *vb, int s) {
     const int ks = s >> 2, blk = s & 3;
     const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
     const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
@@ -250,7 +254,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
 
   // One tile from the bf16 tiles: S^T = K Q^T, factors, mask, online softmax,
   // O^T += V^T (P s_v)^T.
-  auto compute_tile = [&](int tile) {
+  auto compute_tile = [&](int tile, const char *kb, const char *vb, const float (*fac)[64]) {
     const int j0 = (t_lo + tile) * 64;
     uint32_t ka = k_lane;
     asm volatile("" : "+v"(ka));
@@ -365,11 +369,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     }
     l_run += ls;
     u_run += us;
-    bf16x8 vc = v_operand(0);
+    bf16x8 vc = v_operand(vb, 0);
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       bf16x8 vn = vc;
-      if (s < 15) vn = v_operand(s + 1);
+      if (s < 15) vn = v_operand(vb, s + 1);
       __builtin_amdgcn_sched_barrier(0);
       o[s & 3] = mfma32(vc, pb[s >> 2], o[s & 3]);
       vc = vn;
@@ -377,21 +381,46 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     }
   };
 
-  // ---- pipeline: codes one tile ahead in two staging slots; per tile:
-  //      [codes(t) landed] barrier, DMA codes(t+1), widen(t), barrier, compute(t)
-  if (ntiles > 0) issue_codes(0, kc0, vc0, fc0);
-  for (int t = 0; t < ntiles; t += 2) {
-    wait_dma_and_sync();  // codes(t) in slot 0; everyone done with tile t-1
-    if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
-    widen_tile(t, kc0, vc0, fc0);
-    lds_barrier();
-    compute_tile(t);
-    if (t + 1 >= ntiles) break;
-    wait_dma_and_sync();  // codes(t+1) in slot 1
-    if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
-    widen_tile(t + 1, kc1, vc1, fc1);
-    lds_barrier();
-    compute_tile(t + 1);
+  if constexpr (NB == 1) {
+    // ---- codes one tile ahead in two staging slots; per tile:
+    //      [codes(t) landed] barrier, DMA codes(t+1), widen(t), barrier, compute(t)
+    char *kb = kbs[0], *vb = vbs[0];
+    float (*fac)[64] = facs[0];
+    if (ntiles > 0) issue_codes(0, kc0, vc0, fc0);
+    for (int t = 0; t < ntiles; t += 2) {
+      wait_dma_and_sync();  // codes(t) in slot 0; everyone done with tile t-1
+      if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
+      widen_tile(t, kc0, vc0, fc0, kb, vb, fac);
+      lds_barrier();
+      compute_tile(t, kb, vb, fac);
+      if (t + 1 >= ntiles) break;
+      wait_dma_and_sync();  // codes(t+1) in slot 1
+      if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
+      widen_tile(t + 1, kc1, vc1, fc1, kb, vb, fac);
+      lds_barrier();
+      compute_tile(t + 1, kb, vb, fac);
+    }
+  } else {
+    // ---- tile t (codes slot and bf16 buffer t & 1), one barrier each:
+    //      [widen(t) done, codes(t+1) landed, compute(t-1) done] barrier,
+    //      DMA codes(t+2) into the slot widen(t) read, widen(t+1), compute(t)
+    if (ntiles > 0) {
+      issue_codes(0, kc0, vc0, fc0);
+      wait_dma_and_sync();
+      if (ntiles > 1) issue_codes(1, kc1, vc1, fc1);
+      widen_tile(0, kc0, vc0, fc0, kbs[0], vbs[0], facs[0]);
+    }
+    for (int t = 0; t < ntiles; t += 2) {
+      wait_dma_and_sync();
+      if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
+      if (t + 1 < ntiles) widen_tile(t + 1, kc1, vc1, fc1, kbs[1], vbs[1], facs[1]);
+      compute_tile(t, kbs[0], vbs[0], facs[0]);
+      if (t + 1 >= ntiles) break;
+      wait_dma_and_sync();
+      if (t + 3 < ntiles) issue_codes(t + 3, kc1, vc1, fc1);
+      if (t + 2 < ntiles) widen_tile(t + 2, kc0, vc0, fc0, kbs[0], vbs[0], facs[0]);
+      compute_tile(t + 1, kbs[1], vbs[1], facs[1]);
+    }
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
