@@ -472,7 +472,7 @@ def main():
         sweep_small_t(args)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the chunk step shards "
+        print(json.dumps({"error": "this library runs on one GPU only; the chunk step shards "
                           "over (batch, KV head) groups with no exchange, but no multi-GPU "
                           "path is built", "n_gpus": args.gpus}))
         sys.exit(2)

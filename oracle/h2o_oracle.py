@@ -23,8 +23,8 @@ KeysAndValues release (cited as [AM]).
 * Replay log of the policy's decisions per chunk ([LF] §3.2).
 * 8-bit and 4-bit cache buffers ([AM]; [LF] §2) -- the pages give no scheme.
 
-Readings where the pages are silent or garbled (each also listed in the design doc)
--------------------------------------------------------------------------------
+Readings where the pages are silent or garbled
+----------------------------------------------
 R1 Step order is attend-then-evict: the chunk attends to the n_occ occupied
    slots (all visible, their tokens are older) plus its own keys causally; the
    eviction then uses scores that already include this chunk's sums.  With this
