@@ -244,6 +244,10 @@ __device__ __forceinline__ void update_scores(const EvictArgs &a, int head, int 
   constexpr int UB = ITEMS < 8 ? ITEMS : 8;
   const int C = a.C, n_keys = a.n_occ + a.T;
   const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+  // ages are pos + T - token_pos; the host checks that pos + T fits in int32
+  // whenever token positions are kept (and h2o_norm needs them), so the age
+  // converts to fp32 with one instruction and the same rounding as from int64
+  const int32_t pos_end = static_cast<int32_t>(a.pos + a.T);
   for (int bb = 0; bb < nb; ++bb) {
     const size_t g = (POL == H2O_POLICY_ORIG) ? static_cast<size_t>(bb) * a.Hkv + head : head;
     float *ph = a.scores + g * C;
@@ -269,7 +273,7 @@ __device__ __forceinline__ void update_scores(const EvictArgs &a, int head, int 
         if constexpr (POL == H2O_POLICY_ORIG) {
           rank[k] = (bb == 0) ? f[u] : rank[k] + f[u];
         } else if constexpr (POL == H2O_POLICY_NORM) {
-          rank[k] = f[u] / static_cast<float>(a.pos + a.T - t0[u]);
+          rank[k] = f[u] / static_cast<float>(pos_end - t0[u]);
         } else {
           rank[k] = f[u];
         }
