@@ -70,6 +70,32 @@ def pairs_visible(B, Hq, T, n_occ):
     return B * Hq * (T * n_occ + T * (T + 1) // 2)
 
 
+def host_description(blas):
+    """CPU model, logical CPUs and the BLAS the oracle's products run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {
+        "cpu_model": model,
+        "logical_cpus": os.cpu_count(),
+        "usable_cpus": usable,
+        "blas": [{"library": p.get("internal_api"), "version": p.get("version"),
+                  "threads": p.get("num_threads"), "arch": p.get("architecture")} for p in blas],
+        "threads_note": "matrix products run on the BLAS threads; exp and the other "
+                        "elementwise numpy work on one thread",
+    }
+
+
 def cpu_baseline(w, max_groups=8):
     """Time the fp64 oracle on up to `max_groups` KV groups of one evicting
     step (about 10 s of host work for the 32K/2048 step, where 8 groups are
@@ -91,12 +117,14 @@ def cpu_baseline(w, max_groups=8):
     O.bottom_t(phi, w.C, w.C, w.T)
     dt = time.perf_counter() - t0
     step_s = dt * (w.B * w.Hkv) / groups
-    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max([p.get("num_threads", 1) for p in blas] or [1])
     return {
         "value": w.B * w.T / step_s,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
+        "host": host_description(blas),
         "sample": f"{groups} of {w.B * w.Hkv} KV groups of one evicting step "
                   f"({w.qg} heads x {w.T} queries x {w.C + w.T} keys each) in {dt:.1f} s"
                   + (f", scaled by {w.B * w.Hkv / groups:g} to the full step" if groups < w.B * w.Hkv else ""),
@@ -113,6 +141,100 @@ def _counter_rows(folder, counter):
                 rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
     rows.sort()
     return rows
+
+
+def _short_kernel_name(name):
+    """Kernel name without the argument list and namespaces."""
+    base = name.replace("(anonymous namespace)::", "").replace("h2o::", "")
+    base = base.split("(")[0].strip()
+    if base.startswith("void "):
+        base = base[5:]
+    return base
+
+
+def _csv_rows(folder, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(folder, "**", "*" + suffix), recursive=True)):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def trace_summary(folder, skip):
+    """Per-kernel durations from a rocprofv3 --kernel-trace folder, leaving
+    out the first `skip` dispatches of every kernel (warm-up)."""
+    per = {}
+    rows = _csv_rows(folder, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        name = _short_kernel_name(r["Kernel_Name"])
+        per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = [f"{'kernel':44s} {'calls':>6s} {'used':>5s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    total = sum(sum(v[skip:]) for v in per.values())
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1][skip:])):
+        used = d[skip:]
+        if not used:
+            continue
+        lines.append(f"{name[:44]:44s} {len(d):6d} {len(used):5d} {sum(used) / len(used):9.1f} "
+                     f"{min(used):9.1f} {max(used):9.1f}   {100 * sum(used) / total:5.1f}%")
+    return "\n".join(lines)
+
+
+def counters_summary(folders, skip, cus=256, xcds=8):
+    """Per-kernel averages of the counters in rocprofv3 --pmc folders (first
+    `skip` dispatches of every kernel left out), with the ratios derived from
+    them.  SQ counters are chip totals; GRBM_GUI_ACTIVE is summed over the
+    XCDs, so GRBM_GUI_ACTIVE / xcds is the kernel's length in GPU cycles."""
+    per = {}
+    for folder in folders:
+        seen = {}
+        for r in _csv_rows(folder, "counter_collection.csv"):
+            name = _short_kernel_name(r["Kernel_Name"])
+            did = int(r["Dispatch_Id"])
+            seen.setdefault(name, set()).add(did)
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append((did, float(r["Counter_Value"]), dur))
+    out = []
+    for name, cnt in sorted(per.items()):
+        avg = {}
+        durs = []
+        for c, vals in cnt.items():
+            vals.sort()
+            used = vals[skip:] or vals
+            avg[c] = sum(v for _, v, _ in used) / len(used)
+            durs += [d for _, _, d in used]
+        out.append(f"## {name}  (dispatches averaged: {len(used)}, mean duration {sum(durs) / len(durs):.1f} us)")
+        for c in sorted(avg):
+            out.append(f"  {c:34s} {avg[c]:18.1f}")
+        cyc = avg.get("GRBM_GUI_ACTIVE")
+        if cyc:
+            cyc /= xcds
+            simd = cyc * cus * 4
+            derived = []
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+                derived.append(("MFMA busy, share of SIMD cycles", avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd))
+            if "SQ_ACTIVE_INST_VALU" in avg:
+                derived.append(("VALU issue, share of SIMD cycles", avg["SQ_ACTIVE_INST_VALU"] / simd))
+            if "SQ_ACTIVE_INST_LDS" in avg:
+                derived.append(("LDS issue, share of SIMD cycles", avg["SQ_ACTIVE_INST_LDS"] / simd))
+            if "SQ_LDS_IDX_ACTIVE" in avg:
+                derived.append(("LDS active, share of CU cycles", avg["SQ_LDS_IDX_ACTIVE"] / (cyc * cus)))
+            if "SQ_LDS_BANK_CONFLICT" in avg:
+                derived.append(("LDS bank-conflict cycles, share of CU cycles",
+                                avg["SQ_LDS_BANK_CONFLICT"] / (cyc * cus)))
+            if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+                derived.append(("waves waiting on an instruction dependency", avg["SQ_WAIT_INST_ANY"] / avg["SQ_WAVE_CYCLES"]))
+            if "SQ_WAIT_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+                derived.append(("waves waiting (any reason)", avg["SQ_WAIT_ANY"] / avg["SQ_WAVE_CYCLES"]))
+            if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg and avg["SQ_INSTS_MFMA"]:
+                derived.append(("VALU instructions per MFMA", avg["SQ_INSTS_VALU"] / avg["SQ_INSTS_MFMA"]))
+            clk = cyc / (sum(durs) / len(durs)) * 1e-3
+            out.append(f"  {'GPU clock over the kernel (GHz)':34s} {clk:18.3f}")
+            for label, v in derived:
+                out.append(f"  {label:50s} {v:8.3f}")
+        out.append("")
+    return "\n".join(out)
 
 
 def traffic_from(workload, fetch_dir, write_dir):
@@ -208,14 +330,14 @@ def sweep_small_t(args):
             out, wsum, slot_log = gc.new_outputs(w.C)
             bufs = gc.bufs()
             stream = torch.cuda.current_stream()
-            reps = 200
+            reps = args.sweep_reps
 
             def step(i):
                 q, kn, vn = chunks[i % N_CHUNKS]
                 api.h2o_chunk_step(gc.dims, bufs, w.C, gc.pos, q, kn, vn, out, wsum, slot_log, gc.ws, stream)
                 gc.pos += T
 
-            for i in range(10):
+            for i in range(min(10, reps)):
                 step(i)
             torch.cuda.synchronize()
             # step time without per-kernel events
@@ -367,8 +489,9 @@ def prefill(args):
 def backward(args):
     """Gradients of the chunk attention (the fine-tuning pass): the evicting
     step of the 32K cache (n_occ = C = 32768, T = 2048) and a 16K prefill
-    square.  Matrix work per visible pair: dq 6*D flops (S, dP, dS K),
-    dk/dv 8*D (S, dP, P^T dO, dS^T Q)."""
+    square.  Matrix work per visible pair: row terms 4*D flops (S, dP),
+    dq 6*D (S, dP, dS K), dk/dv 8*D (S, dP, P^T dO, dS^T Q); the figure of
+    merit counts the 14*D of the gradients themselves."""
     import numpy as np
     import torch
 
@@ -401,7 +524,7 @@ def backward(args):
         reps = 5
 
         def step():
-            api.h2o_sdpa_backward(dims, bufs, n_occ, q, kn, vn, out, lse, dout, dq, dkc, dvc, dkn, dvn, ws, stream)
+            api.h2o_sdpa_backward(dims, bufs, n_occ, q, kn, vn, lse, dout, dq, dkc, dvc, dkn, dvn, ws, stream)
 
         step()
         torch.cuda.synchronize()
@@ -424,6 +547,7 @@ def backward(args):
             "backward": name, "B": B, "Hq": Hq, "Hkv": Hkv, "D": D, "chunk": T, "cache_slots": C, "n_occ": n_occ,
             "ms": ms, "tflops_14d": 14 * D * pairs / (ms * 1e-3) / 1e12,
             "mfma_frac_14d": 14 * D * pairs / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "rowterm_tflops": 4 * D * pairs / (kms["bwd_rows"] * 1e-3) / 1e12,
             "dq_tflops": 6 * D * pairs / (kms["bwd_dq"] * 1e-3) / 1e12,
             "dkdv_tflops": 8 * D * pairs / (kms["bwd_dkdv"] * 1e-3) / 1e12,
             "kernel_ms": kms,
@@ -442,6 +566,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--trace-from", metavar="DIR",
+                    help="summarise a rocprofv3 --kernel-trace folder (no GPU); --skip-first dispatches "
+                         "of every kernel are left out")
+    ap.add_argument("--counters-from", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc folders per kernel (no GPU)")
+    ap.add_argument("--skip-first", type=int, default=0, help="warm-up dispatches per kernel to leave out")
     ap.add_argument("--sweep-small-t", action="store_true",
                     help="chunk lengths 1, 4, 16, 64, 128 on the 32K-slot cache in bf16, int8 and int4; "
                          "one JSON line each (HBM-bound regime)")
@@ -455,9 +585,21 @@ def main():
     ap.add_argument("--replay-workloads", default="3,4,5", help="workloads of --replay")
     ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
     ap.add_argument("--sweep-ts", default="1,4,16,64,128", help="chunk lengths of --sweep-small-t")
+    ap.add_argument("--sweep-reps", type=int, default=200, help="timed steps per --sweep-small-t case")
     args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU only; the chunk step shards "
+                          "over (batch, KV head) groups with no exchange, but no multi-GPU "
+                          "path is built", "n_gpus": args.gpus}))
+        sys.exit(2)
     if args.traffic_from:
         traffic_from(args.workload, *args.traffic_from)
+        return
+    if args.trace_from:
+        print(trace_summary(args.trace_from, args.skip_first))
+        return
+    if args.counters_from:
+        print(counters_summary(args.counters_from, args.skip_first))
         return
     if args.prefill:
         prefill(args)
@@ -471,11 +613,6 @@ def main():
     if args.sweep_small_t:
         sweep_small_t(args)
         return
-    if args.gpus != 1:
-        print(json.dumps({"error": "this library runs on one GPU only; the chunk step shards "
-                          "over (batch, KV head) groups with no exchange, but no multi-GPU "
-                          "path is built", "n_gpus": args.gpus}))
-        sys.exit(2)
 
     import numpy as np
     import torch
@@ -504,9 +641,7 @@ def main():
 
     for i in range(args.warmup):
         step(i)
-    torch.cuda.synchronize()
-    api.profile_reset()
-    api.profile_enable(True)
+    # timed region: the K steps alone, bracketed by two events on the launch stream
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -516,9 +651,17 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    # per-kernel durations: a second run of K steps with the library's event
+    # timers around every launch (they add a few microseconds per kernel, so
+    # they stay out of the timed region above)
+    api.profile_reset()
+    api.profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
     api.profile_enable(False)
     prof = api.profile_read()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
 
     pairs = pairs_visible(B, Hq, T, C)
     flops_a = 4 * D * pairs       # QK^T and PV of pass A

@@ -97,7 +97,7 @@ def lib():
     L.h2o_replay_step.restype = ctypes.c_int
     L.h2o_replay_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, S, P]
     L.h2o_sdpa_backward.restype = ctypes.c_int
-    L.h2o_sdpa_backward.argtypes = [pd, pc, I32] + [P] * 11 + [P, S, P]
+    L.h2o_sdpa_backward.argtypes = [pd, pc, I32] + [P] * 10 + [P, S, P]
     L.h2o_profile_enable.restype = ctypes.c_int
     L.h2o_profile_enable.argtypes = [ctypes.c_int]
     L.h2o_profile_read.restype = ctypes.c_int
@@ -195,10 +195,10 @@ def h2o_replay_step(dims, cache, n_occ, pos, q, k_new, v_new, out, slot_log, ws,
     _check("h2o_replay_step", st)
 
 
-def h2o_sdpa_backward(dims, cache, n_occ, q, k_new, v_new, out, lse, dout, dq, dk_cache, dv_cache,
+def h2o_sdpa_backward(dims, cache, n_occ, q, k_new, v_new, lse, dout, dq, dk_cache, dv_cache,
                       dk_new, dv_new, ws, stream=None):
     st = lib().h2o_sdpa_backward(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), _ptr(q),
-                                 _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq),
+                                 _ptr(k_new), _ptr(v_new), _ptr(lse), _ptr(dout), _ptr(dq),
                                  _ptr(dk_cache), _ptr(dv_cache), _ptr(dk_new), _ptr(dv_new),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _check("h2o_sdpa_backward", st)

@@ -5,15 +5,16 @@
 //
 // With P = softmax(mask(scale Q K^T)) as in the forward, per query row r of a
 // KV group and key j of the group:
-//   dP_rj = <dO_r, v_j>,  D_r = <dO_r, O_r> (= sum_j P_rj dP_rj),
+//   dP_rj = <dO_r, v_j>,  D_r = sum_j P_rj dP_rj (= <dO_r, O_r>),
 //   dS_rj = P_rj (dP_rj - D_r),
 //   dQ_r = scale sum_j dS_rj k_j,  dK_j = scale sum_r dS_rj q_r,  dV_j = sum_r P_rj dO_r.
 // P is recomputed from the forward's row normalisers, exp2(s * scale * log2 e - L2_r).
 //
 // Three kernels, no atomics (every output element has one writer):
-//  * bwd_rows: L2_r and D_r, one 16-lane group per row;
-//  * bwd_dq (attn_bwd_dq.hip): 128 query rows per workgroup, K and V tiles
-//    streamed (its own file: it is compiled with MFMA results in VGPRs);
+//  * bwd_dq<true> (attn_bwd_dq.hip): L2_r and D_r, the latter summed from the
+//    recomputed fp32 P and dP over every visible key of the row;
+//  * bwd_dq<false> (attn_bwd_dq.hip): 128 query rows per workgroup, K and V
+//    tiles streamed (its own file: it is compiled with MFMA results in VGPRs);
 //  * bwd_dkdv: 128 keys per workgroup (4 waves x 32) held in registers as
 //    MFMA operands; 64-row blocks of Q and dO (and L2, D) stream through LDS,
 //    double-buffered.  Q rows enter S = Q K^T in the same permuted order pass A
@@ -28,31 +29,6 @@
 
 namespace h2o {
 namespace {
-
-constexpr float LOG2E = 1.4426950408889634074f;
-
-__global__ __launch_bounds__(256) void bwd_rows(BwdArgs a) {
-  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
-  const size_t r = static_cast<size_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  float acc = 0.f;
-  if (r < rows) {
-    const uint4 o = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.out) + r * D + 8 * c);
-    const uint4 g = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.dout) + r * D + 8 * c);
-    const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, gw[4] = {g.x, g.y, g.z, g.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__uint_as_float(ow[e] << 16), __uint_as_float(gw[e] << 16), acc);
-      acc = fmaf(__uint_as_float(ow[e] & 0xffff0000u), __uint_as_float(gw[e] & 0xffff0000u), acc);
-    }
-  }
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (r < rows && c == 0) {
-    a.dd[r] = acc;
-    a.l2[r] = a.lse[r] * LOG2E;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // dK, dV: 128 keys per block (4 waves x 32), query rows streamed in blocks of 64
@@ -256,11 +232,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
 
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
-  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
-  {
-    KernelTimer timer(H2O_K_BWD_ROWS, s);
-    hipLaunchKernelGGL(bwd_rows, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s, a);
-  }
   {
     const hipError_t e = launch_bwd_dq(a, s);
     if (e != hipSuccess) return e;

@@ -6,6 +6,14 @@
 // dQ^T += K^T dS^T, the K^T operand read from the row-major K tile by
 // ds_read_b64_tr_b16 (as V^T in pass A).
 //
+// The same kernel with ROWTERM = true runs first and forms each row's term
+// D_r = sum_j P_rj dP_rj from the recomputed fp32 P and dP of every visible
+// key (plus L2_r = lse_r log2 e), so that dS = P (dP - D) is taken against
+// the row term of this P and dP.  (D_r also equals <dO_r, O_r>, but the
+// stored output is bf16, and the rounding of O shifts every dS_rj of the
+// row by P_rj times the same error, which becomes visible wherever
+// dP_rj - D_r cancels.)
+//
 // This file is built with the VGPR form of the MFMAs: the kernel runs one
 // wavefront per SIMD with more than 256 registers, and otherwise its S / dP
 // results would sit in accumulation registers and be copied out before every
@@ -18,7 +26,11 @@
 namespace h2o {
 namespace {
 
-// dQ: 128 packed query rows per block (r = i * q_g + h), keys streamed
+constexpr float LOG2E = 1.4426950408889634074f;
+
+// dQ (ROWTERM = false) or the row terms L2, D (ROWTERM = true): 128 packed
+// query rows per block (r = i * q_g + h), keys streamed
+template <bool ROWTERM>
 __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
@@ -62,8 +74,9 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
       gf[st] = __builtin_bit_cast(bf16x8, vg);
     }
   }
-  const float Lr = row_ok ? a.l2[li] : 0.f;
-  const float Dr = row_ok ? a.dd[li] : 0.f;
+  const float Lr = !row_ok ? 0.f : ROWTERM ? a.lse[li] * LOG2E : a.l2[li];
+  const float Dr = (row_ok && !ROWTERM) ? a.dd[li] : 0.f;
+  float d_acc = 0.f;  // ROWTERM: sum of P dP over the keys so far
 
   const int last_row = min(R, row0 + 128) - 1;
   const int key_end = n_occ + last_row / a.qg + 1;
@@ -128,9 +141,21 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // register r: key t*64 + 32*half + 16*(r/8) + 8*hl + r%8 of the lane's row
-      bf16x8 dsb[2];
       // wave-uniform: every row of the wave exists and sees every key of the half
       const bool half_full = wave_rows_ok && t * 64 + 32 * half + 31 - n_occ <= wave_i_min;
+      if constexpr (ROWTERM) {
+        float part = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ja = t * 64 + 32 * half + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
+          const bool vis = half_full || (row_ok && ja <= i_q);
+          const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr)) : 0.f;
+          part = fmaf(pp, p0[r], part);
+        }
+        d_acc += part;
+        continue;
+      }
+      bf16x8 dsb[2];
       if (half_full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -181,6 +206,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
     compute(t + 1, kb1, vb1);
   }
 
+  if constexpr (ROWTERM) {
+    const float d_row = d_acc + __shfl_xor(d_acc, 32);
+    if (row_ok && hl == 0) {
+      a.dd[li] = d_row;
+      a.l2[li] = Lr;
+    }
+    return;
+  }
   if (!row_ok) return;
   float *dst = a.dq + li * D;
 #pragma unroll
@@ -200,8 +233,15 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
   const int R = a.qg * a.T;
+  const dim3 grid(groups * ((R + 127) / 128));
+  {
+    KernelTimer timer(H2O_K_BWD_ROWS, s);
+    hipLaunchKernelGGL(bwd_dq<true>, grid, dim3(256), 0, s, a);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   KernelTimer timer(H2O_K_BWD_DQ, s);
-  hipLaunchKernelGGL(bwd_dq, dim3(groups * ((R + 127) / 128)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(bwd_dq<false>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

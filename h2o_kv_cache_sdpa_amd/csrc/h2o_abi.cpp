@@ -269,14 +269,14 @@ int h2o_evict_topk(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
 }
 
 int h2o_sdpa_backward(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, const void *q,
-                      const void *k_new, const void *v_new, const void *out, const float *lse,
-                      const void *dout, float *dq, float *dk_cache, float *dv_cache, float *dk_new,
-                      float *dv_new, void *ws, size_t ws_bytes, void *stream) {
+                      const void *k_new, const void *v_new, const float *lse, const void *dout,
+                      float *dq, float *dk_cache, float *dv_cache, float *dk_new, float *dv_new,
+                      void *ws, size_t ws_bytes, void *stream) {
   int st = check_dims(d);
   if (st != H2O_OK) return st;
   if (d->dtype != H2O_BF16 || d->cache_fmt != H2O_CACHE_NATIVE || d->D != 128) return H2O_EUNSUPPORTED;
   if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
-  const void *need[] = {q, k_new, v_new, out, lse, dout, dq, dk_new, dv_new};
+  const void *need[] = {q, k_new, v_new, lse, dout, dq, dk_new, dv_new};
   for (const void *p : need)
     if (!p || !aligned16(p)) return H2O_EINVAL;
   if (n_occ > 0) {
@@ -294,7 +294,6 @@ int h2o_sdpa_backward(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ, 
     a.kc = cache->k;
     a.vc = cache->v;
   }
-  a.out = out;
   a.dout = dout;
   a.lse = lse;
   const size_t rows = static_cast<size_t>(d->B) * d->Hq * d->T;

@@ -61,16 +61,16 @@ struct KvWriteArgs {
 
 // Backward of the chunk attention (bf16, native cache, D = 128).
 struct BwdArgs {
-  const void *q, *kn, *vn, *kc, *vc, *out, *dout;
+  const void *q, *kn, *vn, *kc, *vc, *dout;
   const float *lse;  // (B,Hq,T) natural-log row normalisers of the forward
-  float *l2, *dd;    // workspace (B,Hq,T): lse * log2(e), rowsum(dout * out)
+  float *l2, *dd;    // workspace (B,Hq,T): lse * log2(e), sum_j P_rj dP_rj
   float *dq;         // (B,Hq,T,D)
   float *dkc, *dvc;  // (B,Hkv,C,D), rows < n_occ
   float *dkn, *dvn;  // (B,Hkv,T,D)
   int B, Hq, Hkv, C, T, qg, n_occ;
   float scale, sl2;
 };
-hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t s);  // dQ kernel (attn_bwd_dq.hip)
+hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t s);  // row terms, then dQ (attn_bwd_dq.hip)
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t s);
 
 // Brackets one kernel launch with hipEvents on `s` while timing is enabled

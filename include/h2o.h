@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define H2O_ABI_VERSION 3
+#define H2O_ABI_VERSION 4
 
 /* Status codes. */
 enum h2o_status {
@@ -209,14 +209,15 @@ int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t 
  * the attention of h2o_sdpa_scoresum with the same d, cache, n_occ and chunk,
  * and an upstream gradient dout = dL/d(out):
  *   dq = scale dS K,  dk = scale dS^T Q,  dv = P^T dout,
- *   dS = P o (dout V^T - rowsum(dout o out)),
+ *   dS = P o (dP - rowsum(P o dP)),  dP = dout V^T,
  * with P the masked softmax (cache slots visible, chunk keys causal) and the
  * keys K, V = the n_occ cache rows followed by the chunk's.  dk and dv of a KV
  * head are summed over its q_g query heads.  The summed weights carry no
- * gradient.  P is recomputed from lse; P and dS enter the products as bf16,
- * all sums are fp32.
+ * gradient.  P is recomputed from lse; the row term rowsum(P o dP) (which
+ * equals rowsum(dout o out)) is summed in fp32 from the recomputed P and dP,
+ * so the forward's output is not needed.  P and dS enter the products as
+ * bf16, all sums are fp32.
  *   q, k_new, v_new, cache   as for h2o_sdpa_scoresum (read only)
- *   out    (B,Hq,T,D) bf16: the forward's output
  *   lse    (B,Hq,T) fp32: the forward's natural-log row normalisers (the lse
  *          output of h2o_sdpa_scoresum)
  *   dout   (B,Hq,T,D) bf16
@@ -230,7 +231,7 @@ int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t 
  * (no atomics). */
 int h2o_sdpa_backward(const h2o_dims *d, const h2o_cache *cache, int32_t n_occ,
                       const void *q, const void *k_new, const void *v_new,
-                      const void *out, const float *lse, const void *dout,
+                      const float *lse, const void *dout,
                       float *dq, float *dk_cache, float *dv_cache, float *dk_new, float *dv_new,
                       void *ws, size_t ws_bytes, void *stream);
 
@@ -246,7 +247,7 @@ enum h2o_kernel_kind {
   H2O_K_EVICT = 2,    /* score update, selection, replay log */
   H2O_K_KV_WRITE = 3, /* slot overwrite / quantise */
   H2O_K_ATTN_COMBINE = 4, /* merge of key-split partial outputs (small chunks) */
-  H2O_K_BWD_ROWS = 5, /* backward: row normalisers and rowsum(dout o out) */
+  H2O_K_BWD_ROWS = 5, /* backward: row terms rowsum(P o dP) and log2 normalisers */
   H2O_K_BWD_DQ = 6,   /* backward: dq */
   H2O_K_BWD_DKDV = 7, /* backward: dk, dv */
   H2O_K_COUNT = 8

@@ -52,10 +52,7 @@ R11 Policy variants ([LF] §3.1.1).  h2o_orig ranks slot j of KV head h by
 R19 Gradients ([LF] §3.2, §A.10): the backward of the chunk attention is the
    exact derivative of attend_chunk's output with respect to q, the cache
    rows < n_occ and the chunk's keys and values (the summed weights carry no
-   gradient); dK and dV of a KV group are summed over its query heads.  The
-   row term sum_j P_rj dP_rj = <dO_r, O_r> is taken from the forward output
-   the caller passes in (stored in bf16), as a backward that receives the
-   stored output computes it.
+   gradient); dK and dV of a KV group are summed over its query heads.
 R10 Quantisers (fp32 operation sequences, IEEE round-to-nearest-even):
    int8 symmetric per slot:  a = max|x|;  s = fp16(fp32(a / 127));
         c = clamp(rne(fp32(x / fp32(s))), -127, 127);  x_hat = c * s
@@ -145,7 +142,7 @@ def attend_chunk(q, k_cache, v_cache, n_occ, k_new, v_new, scale, row_block=256)
 # Score update and bottom-T selection
 # --------------------------------------------------------------------------
 
-def attend_backward(q, k_cache, v_cache, n_occ, k_new, v_new, scale, dout, out=None):
+def attend_backward(q, k_cache, v_cache, n_occ, k_new, v_new, scale, dout):
     """Gradients of the chunk attention of attend_chunk for an upstream
     gradient dout = dL/d(out).
 
@@ -161,11 +158,8 @@ def attend_backward(q, k_cache, v_cache, n_occ, k_new, v_new, scale, dout, out=N
       dS_rj = P_rj (dP_rj - sum_j' P_rj' dP_rj')
       dQ_r  = scale sum_j dS_rj k_j
       dK_j  = scale sum_r dS_rj q_r           (summed over the group's heads)
-    Masked pairs have P = 0 and contribute nothing.  The row term
-    sum_j' P_rj' dP_rj' equals <dO_r, O_r>; when ``out`` (B, Hq, T, D) is given
-    -- the forward output as the caller stored it, e.g. rounded to bf16 -- the
-    row term is taken as <dO_r, out_r> instead, which is how a backward that
-    receives the stored output defines it (reading R19).
+    Masked pairs have P = 0 and contribute nothing.  (The row term
+    sum_j' P_rj' dP_rj' equals <dO_r, O_r>.)
 
     Returns float64 arrays dq (B, Hq, T, D), dk_cache, dv_cache
     (B, Hkv, n_occ, D), dk_new, dv_new (B, Hkv, T, D).
@@ -191,10 +185,7 @@ def attend_backward(q, k_cache, v_cache, n_occ, k_new, v_new, scale, dout, out=N
                 e = np.exp(logits - logits.max(axis=1, keepdims=True))
                 p = e / e.sum(axis=1, keepdims=True)
                 dp = dout[b, h] @ vals.T
-                if out is None:
-                    row = (p * dp).sum(axis=1, keepdims=True)
-                else:
-                    row = (dout[b, h] * np.asarray(out[b, h], dtype=np.float64)).sum(axis=1, keepdims=True)
+                row = (p * dp).sum(axis=1, keepdims=True)
                 ds = p * (dp - row)
                 dq[b, h] = scale * (ds @ keys)
                 dk[b, g] += scale * (ds.T @ q[b, h])

@@ -65,14 +65,11 @@ def _run(case, seed=70):
     dvc = torch.full((B, Hkv, C, D), sentinel, dtype=torch.float32, device=DEV)
     dkn = torch.empty(B, Hkv, T, D, dtype=torch.float32, device=DEV)
     dvn = torch.empty(B, Hkv, T, D, dtype=torch.float32, device=DEV)
-    api.h2o_sdpa_backward(dims, bufs, n_occ, q, kn, vn, out, lse, dout, dq, dkc, dvc, dkn, dvn, ws)
+    api.h2o_sdpa_backward(dims, bufs, n_occ, q, kn, vn, lse, dout, dq, dkc, dvc, dkn, dvn, ws)
     torch.cuda.synchronize()
     scale = float(np.float32(1.0 / np.sqrt(D)))
-    # the row term uses the forward output as stored: the oracle's own output rounded to bf16
-    out64, _, _ = O.attend_chunk(ch["q"].f64, k.f64, v.f64, n_occ, ch["k"].f64, ch["v"].f64, scale)
-    out_bf16 = W.to_storage(out64, "bf16").f64
-    ref = O.attend_backward(ch["q"].f64, k.f64, v.f64, n_occ, ch["k"].f64, ch["v"].f64, scale, dout_st.f64,
-                            out=out_bf16)
+    # the exact gradient of the chunk attention at the stored (bf16) inputs
+    ref = O.attend_backward(ch["q"].f64, k.f64, v.f64, n_occ, ch["k"].f64, ch["v"].f64, scale, dout_st.f64)
     return (dq, dkc, dvc, dkn, dvn), ref, sentinel
 
 
@@ -121,6 +118,6 @@ def test_backward_rejects_quantised_cache():
     bufs = api.cache_struct(k, k, k_scale=s, v_scale=s)
     lse = torch.zeros(1, 8, 16, dtype=torch.float32, device=DEV)
     with pytest.raises(api.H2OError) as e:
-        api.h2o_sdpa_backward(dims, bufs, 0, t, t[:, :2], t[:, :2], t, lse, t, f, None, None, f[:, :2],
+        api.h2o_sdpa_backward(dims, bufs, 0, t, t[:, :2], t[:, :2], lse, t, f, None, None, f[:, :2],
                               f[:, :2], ws)
     assert e.value.status == api.H2O_EUNSUPPORTED
