@@ -1,8 +1,9 @@
 """Chunk-step streams through h2o_chunk_step against the fp64 oracle, step by
 step, for the five workloads: tiny fp32 stream and the single bf16 step at full
-size, the long bf16 / int8 / int4 streams with their structure (fill then
-evict, heavy hitters, B) at reduced cache and chunk sizes, and one evicting
-step of each big workload at full size checked on whole KV groups.
+size; the long bf16 / int8 / int4 streams with their structure (fill then
+evict, heavy hitters, B) at reduced cache and chunk sizes; and consecutive
+evicting steps of each long stream at full size with every KV group
+recomputed by the oracle.
 
 When the GPU picks a different slot than the oracle inside the tie band, the
 GPU cache is reloaded from the oracle's state (inputs flow oracle -> GPU only)
@@ -170,8 +171,109 @@ def test_replay_stream(cfg):
 
 
 # ---------------------------------------------------------------------------
-# one evicting step at full size, checked on whole KV groups
+# full-size evicting steps, every KV group recomputed by the oracle
 # ---------------------------------------------------------------------------
+
+def _prefilled_pair(w: W.Workload):
+    """A GPU cache and an oracle cache holding the same full cache of the
+    workload's size (seed [cfg, 777]: random contents, 2 % heavy-hitter keys
+    for bf16 caches, prior scores ~ U(0, 50), token_pos[j] = j)."""
+    B, Hq, Hkv, D, C, T = w.B, w.Hq, w.Hkv, w.D, w.C, w.T
+    gc = H2OCache(B, Hq, Hkv, D, C, T, dtype=w.dtype, cache_fmt=w.cache_fmt, device=DEV)
+    oc = O.OracleCache(B, Hq, Hkv, D, C, fmt=w.cache_fmt)
+    seed = [w.cfg_id, 777]
+    if w.cache_fmt == "native":
+        k, v, scores, tp, _ = W.random_cache(seed, B, Hkv, C, D, C, w.dtype, hh_frac=0.02)
+        oc.k[:], oc.v[:] = k.f64, v.f64
+    else:
+        arr = W.random_quant_cache(seed, B, Hkv, C, D, C, w.cache_fmt)
+        scores, tp = arr["scores"], arr["token_pos"]
+        for name in ("k", "v"):
+            getattr(oc, name + "_codes")[:] = arr[name + "_codes"]
+            getattr(oc, name + "_scale")[:] = arr[name + "_scale"]
+            if w.cache_fmt == "int4":
+                getattr(oc, name + "_zero")[:] = arr[name + "_zero"]
+        if w.cache_fmt == "int8":
+            oc.k[:] = O.dequantize_int8(arr["k_codes"], arr["k_scale"])
+            oc.v[:] = O.dequantize_int8(arr["v_codes"], arr["v_scale"])
+        else:
+            oc.k[:] = O.dequantize_int4(arr["k_codes"], arr["k_scale"], arr["k_zero"])
+            oc.v[:] = O.dequantize_int4(arr["v_codes"], arr["v_scale"], arr["v_zero"])
+    oc.phi[:] = scores.astype(np.float64)
+    oc.token_pos[:] = tp
+    oc.n_occ = oc.pos = C
+    _load_gpu_from_oracle(gc, oc)
+    return gc, oc
+
+
+def _near_threshold(phi_gpu, phi_ref, T, window=1e-3):
+    """Per KV group, the oracle's T-th smallest updated score theta; over the
+    slots whose oracle score lies within `window` relative of theta, the
+    largest |phi_gpu - phi_ref| / theta, and the number of slots inside the
+    1e-6 tie band."""
+    worst, in_band = 0.0, 0
+    B, H, C = phi_ref.shape
+    for b in range(B):
+        for g in range(H):
+            ref = phi_ref[b, g]
+            theta = np.partition(ref, T - 1)[T - 1]
+            near = np.abs(ref - theta) <= window * abs(theta)
+            worst = max(worst, float((np.abs(phi_gpu[b, g][near] - ref[near]) / abs(theta)).max()))
+            in_band += int((np.abs(ref - theta) <= 1e-6 * abs(theta)).sum())
+    return worst, in_band
+
+
+def _full_stream(w: W.Workload, n_steps):
+    """Consecutive evicting steps on a full cache of the workload's size,
+    starting at the stream's first evicting chunk.  Every step: the output,
+    the summed weights and the selection of every (b, g) group against the
+    oracle, then the cache state (contents bit for bit, positions, scores).
+    Reports in-band swaps and the worst GPU score error near the threshold."""
+    gc, oc = _prefilled_pair(w)
+    C, T, qg = w.C, w.T, w.qg
+    swaps = resync = 0
+    for s in range(n_steps):
+        ch = W.chunk(w, w.n_fill + s)
+        phi_before = gc.scores.cpu().numpy()
+        print(f"{w.name} full-size step {s}: GPU", flush=True)
+        out, wsum, slots = gc.step(to_dev(ch["q"]), to_dev(ch["k"]), to_dev(ch["v"]))
+        torch.cuda.synchronize()
+        print(f"{w.name} full-size step {s}: oracle, {w.B * w.Hkv} groups", flush=True)
+        ref = oc.step(ch["q"].f64, ch["k"].f64, ch["v"].f64)
+        err = check_out(out, ref["out"], w.dtype, f"step {s} out")
+        wsum_np = wsum.cpu().numpy()
+        werr = check_rel(wsum_np, ref["w"], T, qg, f"step {s} wsum")
+        differ = check_selection(slots.cpu().numpy(), ref["slots"], ref["rank_key"], C, C, T)
+        # the selection kernel adds the sums to the scores in fp32
+        phi_gpu = (phi_before + wsum_np[:, :, :C]).astype(np.float32).astype(np.float64)
+        near_err, in_band = _near_threshold(phi_gpu, ref["phi_updated"], T)
+        swaps += differ
+        print(f"{w.name} full-size step {s}: out err {err:.2e} wsum rel {werr:.2e} "
+              f"groups with in-band swaps {differ} slots in the tie band {in_band} "
+              f"worst near-threshold score error / theta {near_err:.2e}", flush=True)
+        assert near_err < 5e-7, "score error near the threshold reaches the tie band"
+        if differ:
+            resync += 1
+            _load_gpu_from_oracle(gc, oc)
+        else:
+            _check_state(gc, oc, T, qg)
+    print(f"{w.name}: {n_steps} full-size evicting steps, in-band swaps {swaps}, resyncs {resync}", flush=True)
+
+
+@pytest.mark.timeout(900)
+def test_full_stream_cfg3():
+    _full_stream(W.WORKLOADS[3], 3)
+
+
+@pytest.mark.timeout(900)
+def test_full_stream_cfg4():
+    _full_stream(W.WORKLOADS[4], 3)
+
+
+@pytest.mark.timeout(900)
+def test_full_stream_cfg5():
+    _full_stream(W.WORKLOADS[5], 2)
+
 
 def _full_step(w: W.Workload, groups_checked):
     """Prefilled full cache of the workload's size; one evicting step; the
@@ -221,22 +323,6 @@ def _full_step(w: W.Workload, groups_checked):
         ref_slots = O.bottom_t(phi_upd, C, C, T)
         differ = check_selection(slots_np[b:b + 1, g:g + 1], ref_slots, phi_upd, C, C, T)
         print(f"group ({b},{g}) in-band differ {differ}", flush=True)
-
-
-def test_full_step_cfg2():
-    _full_step(W.WORKLOADS[2], [(0, 0), (0, 7)])
-
-
-def test_full_step_cfg3():
-    _full_step(W.WORKLOADS[3], [(0, 0), (0, 5)])
-
-
-def test_full_step_cfg4():
-    _full_step(W.WORKLOADS[4], [(0, 3)])
-
-
-def test_full_step_cfg5():
-    _full_step(W.WORKLOADS[5], [(0, 0), (3, 7)])
 
 
 # short chunks on the full 32K-slot cache, in the launch configuration the
