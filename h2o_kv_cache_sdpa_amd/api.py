@@ -26,7 +26,8 @@ FORMATS = {"native": H2O_CACHE_NATIVE, "int8": H2O_CACHE_INT8, "int4": H2O_CACHE
 EXPORTS = (
     "h2o_abi_version", "h2o_status_str", "h2o_last_hip_error", "h2o_workspace_bytes",
     "h2o_sdpa_scoresum", "h2o_evict_topk", "kv_scatter", "kv_quant_pack",
-    "kv_dequant_unpack", "h2o_chunk_step", "h2o_replay_step", "h2o_sdpa_backward",
+    "kv_dequant_unpack", "h2o_chunk_step", "h2o_chunk_step_noalloc", "h2o_replay_step",
+    "h2o_sdpa_backward",
     "h2o_profile_enable", "h2o_profile_read",
     "h2o_profile_reset",
 )
@@ -94,6 +95,8 @@ def lib():
     L.kv_dequant_unpack.argtypes = [pd, pc, I32, P, P, P]
     L.h2o_chunk_step.restype = ctypes.c_int
     L.h2o_chunk_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, P, S, P]
+    L.h2o_chunk_step_noalloc.restype = ctypes.c_int
+    L.h2o_chunk_step_noalloc.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, P]
     L.h2o_replay_step.restype = ctypes.c_int
     L.h2o_replay_step.argtypes = [pd, pc, I32, I64, P, P, P, P, P, P, S, P]
     L.h2o_sdpa_backward.restype = ctypes.c_int
@@ -186,6 +189,13 @@ def h2o_chunk_step(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log
                               _ptr(slot_log), _ptr(ws), ws.numel() * ws.element_size(),
                               _stream(stream))
     _check("h2o_chunk_step", st)
+
+
+def h2o_chunk_step_noalloc(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, stream=None):
+    st = lib().h2o_chunk_step_noalloc(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
+                                      _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(wsum),
+                                      _ptr(slot_log), _stream(stream))
+    _check("h2o_chunk_step_noalloc", st)
 
 
 def h2o_replay_step(dims, cache, n_occ, pos, q, k_new, v_new, out, slot_log, ws, stream=None):

@@ -7,9 +7,16 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/h2o.h"
 #include "h2o_internal.hpp"
+
+// Workspace of h2o_chunk_step_noalloc: one array per GPU, reserved when the
+// code object is loaded on that GPU and held until the process ends.  Host
+// code never uses this name as a device address: the address comes from
+// hipGetSymbolAddress (scratch_address below), once per device.
+static __device__ __align__(256) unsigned char scratch[H2O_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -345,9 +352,13 @@ int kv_dequant_unpack(const h2o_dims *d, const h2o_cache *cache, int32_t n_slots
   return from_hip(h2o::launch_dequant(w, n_slots, k_out, v_out, static_cast<hipStream_t>(stream)));
 }
 
-int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,
-                   const void *k_new, const void *v_new, void *out, float *wsum,
-                   int32_t *slot_log, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,
+               const void *k_new, const void *v_new, void *out, float *wsum, int32_t *slot_log, void *ws,
+               size_t ws_bytes, void *stream) {
   int st = check_dims(d);
   if (st != H2O_OK) return st;
   if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
@@ -372,6 +383,54 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
                                   static_cast<char *>(ws) + used, ws_bytes - used, s, &kv, &kv_done));
   if (st != H2O_OK || kv_done) return st;
   return from_hip(h2o::launch_kv_write(kv, s));
+}
+
+// Device address of `scratch` on the current device, looked up on the first
+// call per device and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices] = {};
+
+int scratch_address(void **addr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e);
+  if (dev < 0 || dev >= kMaxDevices) return H2O_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return from_hip(e);
+    if (!p) return H2O_EHIP;
+    g_scratch_addr[dev] = p;
+  }
+  *addr = g_scratch_addr[dev];
+  return H2O_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,
+                   const void *k_new, const void *v_new, void *out, float *wsum,
+                   int32_t *slot_log, void *ws, size_t ws_bytes, void *stream) {
+  return chunk_step(d, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, ws, ws_bytes, stream);
+}
+
+int h2o_chunk_step_noalloc(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                           const void *q, const void *k_new, const void *v_new, void *out,
+                           float *wsum, int32_t *slot_log, void *stream) {
+  int st = check_dims(d);
+  if (st != H2O_OK) return st;
+  if (n_occ < 0 || n_occ > d->C) return H2O_EINVAL;
+  const size_t need = attn_ws_bytes(d, n_occ) + (wsum ? 0 : wsum_bytes(d, n_occ));
+  if (need > H2O_NOALLOC_SCRATCH_BYTES) return H2O_EWORKSPACE;
+  void *ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != H2O_OK) return st;
+  return chunk_step(d, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, ws,
+                    H2O_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int h2o_replay_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, const void *q,

@@ -187,6 +187,25 @@ int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t p
                    void *out, float *wsum, int32_t *slot_log,
                    void *ws, size_t ws_bytes, void *stream);
 
+/* h2o_chunk_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same work, with the workspace taken from a device-resident array of
+ * H2O_NOALLOC_SCRATCH_BYTES that the library reserves on each GPU it runs on
+ * and holds until the process ends.  The call allocates and frees nothing.
+ *   Arguments, results and return codes are those of h2o_chunk_step without
+ *   ws / ws_bytes; wsum may be NULL (the sums then live in the array).
+ *   H2O_EWORKSPACE: the workspace this call needs (row normalisers, key-split
+ *   partials, stored logits, and the sums when wsum is NULL) exceeds
+ *   H2O_NOALLOC_SCRATCH_BYTES.  The array is per GPU: `stream` must belong to
+ *   the current device.  Every call on a GPU uses that GPU's one array, and
+ *   no kernel reads a byte of it the same call has not written, so it is
+ *   never cleared; calls that overlap in time on one GPU (several streams,
+ *   or host threads without ordering) race on it. */
+#define H2O_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int h2o_chunk_step_noalloc(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
+                           const void *q, const void *k_new, const void *v_new, void *out,
+                           float *wsum, int32_t *slot_log, void *stream);
+
 /* Replay step ("Learning how to Forget", §3.2: replay caches act like normal
  * KV caches except that eviction decisions are replayed from the log): the
  * attention of h2o_sdpa_scoresum without the summed weights (no scoring, no
