@@ -13,7 +13,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libh2o.so")
+# H2O_DEBUG_LIB=1 selects the debug build (device index checks on).
+LIB_PATH = os.path.join(PKG, "libh2o_debug.so" if os.environ.get("H2O_DEBUG_LIB") == "1" else "libh2o.so")
 
 H2O_OK, H2O_EINVAL, H2O_EUNSUPPORTED, H2O_EWORKSPACE, H2O_EHIP = 0, -1, -2, -3, -4
 H2O_F32, H2O_BF16 = 0, 1
@@ -139,8 +140,65 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _torch():
+    import torch
+    return torch
+
+
+def _need(t, what, numel, dtypes, required=True):
+    """A tensor handed to the library must live on the GPU, be contiguous and
+    have the element type and element count the dimensions call for: the
+    library only sees its address."""
+    if t is None:
+        if required:
+            raise ValueError(f"{what} is required")
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{what} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() != numel:
+        raise ValueError(f"{what} has {t.numel()} elements, expected {numel}")
+
+
+def _io_dtype(dims):
+    torch = _torch()
+    return (torch.float32,) if dims.dtype == H2O_F32 else (torch.bfloat16,)
+
+
+def _check_chunk(dims, q, k_new, v_new, out=None, need_out=True):
+    torch = _torch()
+    dt = _io_dtype(dims)
+    B, Hq, Hkv, D, T = dims.B, dims.Hq, dims.Hkv, dims.D, dims.T
+    _need(q, "q", B * Hq * T * D, dt)
+    _need(k_new, "k_new", B * Hkv * T * D, dt)
+    _need(v_new, "v_new", B * Hkv * T * D, dt)
+    if need_out:
+        _need(out, "out", B * Hq * T * D, dt)
+    return torch
+
+
 def cache_struct(k, v, scores=None, token_pos=None, k_scale=None, v_scale=None, k_zero=None,
-                 v_zero=None):
+                 v_zero=None, dims=None):
+    """Pointers of one cache's state tensors; with `dims`, each tensor given
+    is checked against the cache layout first."""
+    if dims is not None:
+        torch = _torch()
+        B, Hkv, C, D = dims.B, dims.Hkv, dims.C, dims.D
+        if dims.cache_fmt == H2O_CACHE_NATIVE:
+            kv_n, kv_dt = B * Hkv * C * D, _io_dtype(dims)
+        elif dims.cache_fmt == H2O_CACHE_INT8:
+            kv_n, kv_dt = B * Hkv * C * D, (torch.int8,)
+        else:
+            kv_n, kv_dt = B * Hkv * C * D // 2, (torch.uint8,)
+        _need(k, "cache k", kv_n, kv_dt)
+        _need(v, "cache v", kv_n, kv_dt)
+        for name, t in (("k_scale", k_scale), ("v_scale", v_scale), ("k_zero", k_zero), ("v_zero", v_zero)):
+            _need(t, name, B * Hkv * C, (torch.float16,), required=False)
+        _need(scores, "scores", B * Hkv * C, (torch.float32,), required=False)
+        _need(token_pos, "token_pos", B * Hkv * C, (torch.int32,), required=False)
     f = lambda t: None if t is None else t.data_ptr()
     return H2OCacheBufs(f(k), f(v), f(k_scale), f(v_scale), f(k_zero), f(v_zero), f(scores),
                         f(token_pos))
@@ -151,7 +209,16 @@ def _check(fn, st):
         raise H2OError(fn, st)
 
 
+def _check_ws(ws):
+    torch = _torch()
+    _need(ws, "ws", ws.numel() if ws is not None else 0, (torch.uint8,))
+
+
 def h2o_sdpa_scoresum(dims, cache, n_occ, q, k_new, v_new, out, wsum, lse, ws, stream=None):
+    torch = _check_chunk(dims, q, k_new, v_new, out)
+    _need(wsum, "wsum", dims.B * dims.Hkv * (int(n_occ) + dims.T), (torch.float32,))
+    _need(lse, "lse", dims.B * dims.Hq * dims.T, (torch.float32,), required=False)
+    _check_ws(ws)
     st = lib().h2o_sdpa_scoresum(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), _ptr(q),
                                  _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(wsum), _ptr(lse),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
@@ -159,6 +226,11 @@ def h2o_sdpa_scoresum(dims, cache, n_occ, q, k_new, v_new, out, wsum, lse, ws, s
 
 
 def h2o_evict_topk(dims, cache, n_occ, pos, wsum, slot_log, ws=None, stream=None):
+    torch = _torch()
+    _need(wsum, "wsum", dims.B * dims.Hkv * (int(n_occ) + dims.T), (torch.float32,))
+    _need(slot_log, "slot_log", dims.B * dims.Hkv * dims.T, (torch.int32,))
+    if ws is not None:
+        _check_ws(ws)
     nb = 0 if ws is None else ws.numel() * ws.element_size()
     st = lib().h2o_evict_topk(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
                               _ptr(wsum), _ptr(slot_log), _ptr(ws), nb, _stream(stream))
@@ -166,24 +238,45 @@ def h2o_evict_topk(dims, cache, n_occ, pos, wsum, slot_log, ws=None, stream=None
 
 
 def kv_scatter(dims, cache, k_new, v_new, slot_log, stream=None):
+    torch = _torch()
+    dt = _io_dtype(dims)
+    _need(k_new, "k_new", dims.B * dims.Hkv * dims.T * dims.D, dt)
+    _need(v_new, "v_new", dims.B * dims.Hkv * dims.T * dims.D, dt)
+    _need(slot_log, "slot_log", dims.B * dims.Hkv * dims.T, (torch.int32,))
     st = lib().kv_scatter(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
                           _ptr(slot_log), _stream(stream))
     _check("kv_scatter", st)
 
 
 def kv_quant_pack(dims, cache, k_new, v_new, slot_log, stream=None):
+    torch = _torch()
+    dt = _io_dtype(dims)
+    _need(k_new, "k_new", dims.B * dims.Hkv * dims.T * dims.D, dt)
+    _need(v_new, "v_new", dims.B * dims.Hkv * dims.T * dims.D, dt)
+    _need(slot_log, "slot_log", dims.B * dims.Hkv * dims.T, (torch.int32,))
     st = lib().kv_quant_pack(ctypes.byref(dims), ctypes.byref(cache), _ptr(k_new), _ptr(v_new),
                              _ptr(slot_log), _stream(stream))
     _check("kv_quant_pack", st)
 
 
 def kv_dequant_unpack(dims, cache, n_slots, k_out, v_out, stream=None):
+    torch = _torch()
+    for name, t in (("k_out", k_out), ("v_out", v_out)):
+        _need(t, name, dims.B * dims.Hkv * int(n_slots) * dims.D, (torch.float32,))
     st = lib().kv_dequant_unpack(ctypes.byref(dims), ctypes.byref(cache), int(n_slots),
                                  _ptr(k_out), _ptr(v_out), _stream(stream))
     _check("kv_dequant_unpack", st)
 
 
-def h2o_chunk_step(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, ws, stream=None):
+def h2o_chunk_step(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, ws, stream=None,
+                   check=True):
+    """check=False skips the tensor checks (for a timing loop whose tensors
+    have already been checked once)."""
+    if check:
+        torch = _check_chunk(dims, q, k_new, v_new, out)
+        _need(wsum, "wsum", dims.B * dims.Hkv * (int(n_occ) + dims.T), (torch.float32,), required=False)
+        _need(slot_log, "slot_log", dims.B * dims.Hkv * dims.T, (torch.int32,))
+        _check_ws(ws)
     st = lib().h2o_chunk_step(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
                               _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(wsum),
                               _ptr(slot_log), _ptr(ws), ws.numel() * ws.element_size(),
@@ -192,13 +285,20 @@ def h2o_chunk_step(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log
 
 
 def h2o_chunk_step_noalloc(dims, cache, n_occ, pos, q, k_new, v_new, out, wsum, slot_log, stream=None):
+    torch = _check_chunk(dims, q, k_new, v_new, out)
+    _need(wsum, "wsum", dims.B * dims.Hkv * (int(n_occ) + dims.T), (torch.float32,), required=False)
+    _need(slot_log, "slot_log", dims.B * dims.Hkv * dims.T, (torch.int32,))
     st = lib().h2o_chunk_step_noalloc(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
                                       _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(wsum),
                                       _ptr(slot_log), _stream(stream))
     _check("h2o_chunk_step_noalloc", st)
 
 
-def h2o_replay_step(dims, cache, n_occ, pos, q, k_new, v_new, out, slot_log, ws, stream=None):
+def h2o_replay_step(dims, cache, n_occ, pos, q, k_new, v_new, out, slot_log, ws, stream=None, check=True):
+    if check:
+        torch = _check_chunk(dims, q, k_new, v_new, out)
+        _need(slot_log, "slot_log", dims.B * dims.Hkv * dims.T, (torch.int32,))
+        _check_ws(ws)
     st = lib().h2o_replay_step(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), int(pos),
                                _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(out), _ptr(slot_log),
                                _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
@@ -207,6 +307,16 @@ def h2o_replay_step(dims, cache, n_occ, pos, q, k_new, v_new, out, slot_log, ws,
 
 def h2o_sdpa_backward(dims, cache, n_occ, q, k_new, v_new, lse, dout, dq, dk_cache, dv_cache,
                       dk_new, dv_new, ws, stream=None):
+    torch = _check_chunk(dims, q, k_new, v_new, need_out=False)
+    B, Hq, Hkv, D, C, T = dims.B, dims.Hq, dims.Hkv, dims.D, dims.C, dims.T
+    _need(lse, "lse", B * Hq * T, (torch.float32,))
+    _need(dout, "dout", B * Hq * T * D, _io_dtype(dims))
+    _need(dq, "dq", B * Hq * T * D, (torch.float32,))
+    for name, t in (("dk_cache", dk_cache), ("dv_cache", dv_cache)):
+        _need(t, name, B * Hkv * C * D, (torch.float32,), required=int(n_occ) > 0)
+    for name, t in (("dk_new", dk_new), ("dv_new", dv_new)):
+        _need(t, name, B * Hkv * T * D, (torch.float32,))
+    _check_ws(ws)
     st = lib().h2o_sdpa_backward(ctypes.byref(dims), ctypes.byref(cache), int(n_occ), _ptr(q),
                                  _ptr(k_new), _ptr(v_new), _ptr(lse), _ptr(dout), _ptr(dq),
                                  _ptr(dk_cache), _ptr(dv_cache), _ptr(dk_new), _ptr(dv_new),

@@ -51,7 +51,7 @@ class H2OCache:
 
     def bufs(self):
         return api.cache_struct(self.k, self.v, self.scores, self.token_pos, self.k_scale,
-                                self.v_scale, self.k_zero, self.v_zero)
+                                self.v_scale, self.k_zero, self.v_zero, dims=self.dims)
 
     def new_outputs(self, n_occ=None):
         n = self.n_occ if n_occ is None else n_occ

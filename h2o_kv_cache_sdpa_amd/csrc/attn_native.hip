@@ -350,6 +350,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     return;
   }
   const float inv = 1.f / l_tot;
+  H2O_DEVICE_CHECK(i_q < a.T && h_q < a.Hq && b < a.B);
   uint16_t *orow = static_cast<uint16_t *>(a.out) + li * D;
 #pragma unroll
   for (int blk = 0; blk < 4; ++blk) {
@@ -1171,6 +1172,7 @@ __global__ __launch_bounds__(256, 2) void attn_b_native(AttnArgs a) {
     const float other0 = __shfl_xor(mine0, 32), other1 = __shfl_xor(mine1, 32);
     if (hl == 0) {
       float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
+      H2O_DEVICE_CHECK(grp < a.B * a.Hkv && key0 >= 0 && key1 >= 0);
       if (key0 < n_keys) w[key0] = mine0 + other0;
       if (key1 < n_keys) w[key1] = mine1 + other1;
     }

@@ -289,6 +289,7 @@ template <int POL>
 __device__ __forceinline__ void take_slot(const EvictArgs &a, int head, int j, int out, float seed0) {
   const int C = a.C, T = a.T, n_keys = a.n_occ + T;
   const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+  H2O_DEVICE_CHECK(j >= 0 && j < C && out >= 0 && out < T);
   for (int bb = 0; bb < nb; ++bb) {
     const size_t g = (POL == H2O_POLICY_ORIG) ? static_cast<size_t>(bb) * a.Hkv + head : head;
     const float seed = (bb == 0) ? seed0 : a.wsum[g * n_keys + C + out];
@@ -323,6 +324,7 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
     const float *w = a.wsum + grp0 * n_keys;
     for (int t = tid; t < T; t += NT) {
       const int slot = n_occ + t;
+      H2O_DEVICE_CHECK(slot < C);
       a.slot_log[grp0 * T + t] = slot;
       a.scores[grp0 * C + slot] = w[n_occ + t];
       if (a.token_pos) a.token_pos[grp0 * C + slot] = static_cast<int32_t>(a.pos + t);

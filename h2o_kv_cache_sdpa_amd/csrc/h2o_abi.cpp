@@ -38,11 +38,15 @@ int check_dims(const h2o_dims *d) {
   if (!(std::isfinite(d->scale) && d->scale >= 0.f)) return H2O_EINVAL;
   if (d->policy < H2O_POLICY_H2O || d->policy > H2O_POLICY_ORIG) return H2O_EUNSUPPORTED;
   if (d->D != 64 && d->D != 128) return H2O_EUNSUPPORTED;
-  // index arithmetic inside the kernels uses 32-bit row counts
+  // Index arithmetic inside the kernels uses 32-bit integers: byte offsets
+  // of up to 2^22 rows of 256 bytes, score / position / sum indices of up to
+  // B*Hkv*(C+T) elements, and query-row indices of up to B*Hq*T.
   const int64_t rows = static_cast<int64_t>(d->Hq / d->Hkv) * d->T;
   const int64_t keys = static_cast<int64_t>(d->C) + d->T;
   const int64_t groups = static_cast<int64_t>(d->B) * d->Hkv;
-  if (rows > (1 << 26) || keys > (1 << 26) || groups > (1 << 20)) return H2O_EUNSUPPORTED;
+  if (rows > (1 << 22) || keys > (1 << 22)) return H2O_EUNSUPPORTED;
+  if (groups * keys > INT32_MAX) return H2O_EUNSUPPORTED;
+  if (static_cast<int64_t>(d->B) * d->Hq * d->T * d->D > INT32_MAX) return H2O_EUNSUPPORTED;
   return H2O_OK;
 }
 

@@ -6,6 +6,19 @@
 
 #include "../../include/h2o.h"
 
+// Device-side index checks of the debug build (H2O_DEBUG): a failed check
+// ends the kernel with a trap, so a write that would land outside its
+// buffer becomes a launch error instead of silent corruption.  The release
+// build compiles them away.
+#ifdef H2O_DEBUG
+#define H2O_DEVICE_CHECK(cond) \
+  do {                         \
+    if (!(cond)) __builtin_trap(); \
+  } while (0)
+#else
+#define H2O_DEVICE_CHECK(cond) ((void)0)
+#endif
+
 namespace h2o {
 
 enum : int { DT_F32 = 0, DT_BF16 = 1 };

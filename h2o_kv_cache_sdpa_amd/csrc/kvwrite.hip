@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256) void scatter_native(KvWriteArgs a, int row_byt
   if (slot < 0 || slot >= a.C) return;  // caller-supplied log: never write outside the cache
   if (a.token_pos && chunk == 0 && isv == 0)
     a.token_pos[static_cast<size_t>(grp) * a.C + slot] = static_cast<int32_t>(a.pos + static_cast<int>(r % a.T));
+  H2O_DEVICE_CHECK(grp < a.groups && chunk < cpr);
   const char *src = static_cast<const char *>(isv ? a.vn : a.kn) + r * row_bytes + chunk * 16;
   char *dst = static_cast<char *>(isv ? a.vc : a.kc) +
               (static_cast<size_t>(grp) * a.C + slot) * row_bytes + chunk * 16;

@@ -50,7 +50,9 @@ extern "C" {
 enum h2o_status {
   H2O_OK = 0,
   H2O_EINVAL = -1,       /* null / misaligned pointer, bad sizes, n_occ out of range */
-  H2O_EUNSUPPORTED = -2, /* valid but not implemented: D not in {64,128}, chunk straddling capacity, ... */
+  H2O_EUNSUPPORTED = -2, /* valid but not implemented: D not in {64,128}, chunk straddling capacity,
+                            sizes past the 32-bit index range (q_g*T or C+T above 2^22,
+                            B*Hkv*(C+T) or B*Hq*T*D above 2^31 - 1), ... */
   H2O_EWORKSPACE = -3,   /* ws_bytes smaller than h2o_workspace_bytes() or ws NULL */
   H2O_EHIP = -4          /* a HIP launch failed; see h2o_last_hip_error() */
 };
@@ -163,8 +165,11 @@ int kv_scatter(const h2o_dims *d, h2o_cache *cache, const void *k_new, const voi
 
 /* Quantise the chunk's keys and values per row and write codes, scales (and
  * zero points) into the slots of slot_log.  INT8 or INT4 caches only
- * (H2O_EINVAL for NATIVE).  The pages name 8-bit and 4-bit buffers without a
- * scheme; this library uses, per slot and KV head, with IEEE fp32 operations:
+ * (H2O_EINVAL for NATIVE).  The aimodeling.com article on the KeysAndValues
+ * release names 8-bit and 4-bit cache buffers (4-bit: a quarter of the cache
+ * memory), and "Learning how to Forget" §2 lists quantised caches among the
+ * library's buffers; neither gives a scheme.  This library uses, per slot
+ * and KV head, with IEEE fp32 operations:
  *   INT8: a = max|x|; s = fp16(a/127); c = clamp(rne(x/s), -127, 127)
  *   INT4: z = fp16(min x); s = fp16((max x - min x)/15);
  *         c = clamp(rne((x - z)/s), 0, 15)
@@ -178,10 +183,14 @@ int kv_quant_pack(const h2o_dims *d, h2o_cache *cache, const void *k_new, const 
 int kv_dequant_unpack(const h2o_dims *d, const h2o_cache *cache, int32_t n_slots,
                       float *k_out, float *v_out, void *stream);
 
-/* The whole chunk step: h2o_sdpa_scoresum, then h2o_evict_topk, then
- * kv_scatter (NATIVE) or kv_quant_pack (INT8/INT4), enqueued on `stream`.
- * wsum may be NULL (the sums then live in the workspace).  After the call the
- * caller's occupancy is min(n_occ + T, C) and its position pos + T. */
+/* The whole chunk step ("Learning how to Forget", §3.1: a chunk of T tokens
+ * attends to the cache plus itself, and B*Hkv*T slots are then overwritten
+ * by its keys and values; §3.1.1: the H2O score of a slot is its cumulative
+ * summed attention weight; §3.2: the decisions go to a replay log):
+ * h2o_sdpa_scoresum, then h2o_evict_topk, then kv_scatter (NATIVE) or
+ * kv_quant_pack (INT8/INT4), enqueued on `stream`.  wsum may be NULL (the
+ * sums then live in the workspace).  After the call the caller's occupancy
+ * is min(n_occ + T, C) and its position pos + T. */
 int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
                    const void *q, const void *k_new, const void *v_new,
                    void *out, float *wsum, int32_t *slot_log,

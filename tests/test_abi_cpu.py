@@ -138,3 +138,86 @@ def test_chunk_step_validation_enqueues_nothing():
     need_lse = 2 * 4 * 8 * 64
     assert step(0, ws_bytes=need_lse, wsum=None) == api.H2O_EWORKSPACE
     assert L.h2o_last_hip_error() == 0
+
+
+def test_sizes_past_32bit_index_limits_are_rejected():
+    # 2^22 + 1 keys, or B*Hkv*(C+T) past 2^31, or B*Hq*T*D past 2^31
+    assert api.workspace_bytes(api.make_dims(1, 8, 8, 128, (1 << 22) - 63, 64)) == 0
+    assert api.workspace_bytes(api.make_dims(1, 8, 8, 128, (1 << 22) - 64, 64)) > 0
+    assert api.workspace_bytes(api.make_dims(1024, 8, 8, 128, 1 << 18, 64)) == 0
+    assert api.workspace_bytes(api.make_dims(1, 4096, 1, 128, 256, 8192)) == 0
+    d = api.make_dims(1024, 8, 8, 128, 1 << 18, 64)
+    assert _sdpa(d) == api.H2O_EUNSUPPORTED
+
+
+def _noalloc(d, n_occ, wsum=FAKE):
+    c = _cache()
+    return api.lib().h2o_chunk_step_noalloc(ctypes.byref(d), ctypes.byref(c), n_occ, 0, FAKE, FAKE, FAKE,
+                                            FAKE, wsum, FAKE, None)
+
+
+def test_noalloc_validation():
+    d = api.make_dims(1, 8, 2, 128, 256, 64)
+    assert _noalloc(d, 257) == api.H2O_EINVAL
+    assert _noalloc(d, -1) == api.H2O_EINVAL
+    # stored logits of 4-token chunks over a 1M-slot cache exceed the 64 MiB array
+    big = api.make_dims(1, 32, 8, 128, 1 << 20, 4)
+    assert _noalloc(big, 1 << 20, wsum=None) == api.H2O_EWORKSPACE
+
+
+class _FakeTensor:
+    """Just enough of a tensor for the binding's checks."""
+
+    def __init__(self, numel, dtype, cuda=True, contiguous=True):
+        self._n, self.dtype, self.is_cuda, self._c = numel, dtype, cuda, contiguous
+
+    def numel(self):
+        return self._n
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        return FAKE
+
+
+def test_binding_checks_tensors_against_dims():
+    import torch
+    d = api.make_dims(1, 8, 2, 128, 256, 64)
+    q_n = 8 * 64 * 128
+    ok = _FakeTensor(q_n, torch.bfloat16)
+    kv = _FakeTensor(2 * 64 * 128, torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        api.h2o_sdpa_scoresum(d, _cache(), 0, torch.zeros(q_n, dtype=torch.bfloat16), kv, kv, ok, None, None, None)
+    with pytest.raises(ValueError, match="contiguous"):
+        api.h2o_sdpa_scoresum(d, _cache(), 0, _FakeTensor(q_n, torch.bfloat16, contiguous=False), kv, kv, ok,
+                              None, None, None)
+    with pytest.raises(ValueError, match="dtype"):
+        api.h2o_sdpa_scoresum(d, _cache(), 0, _FakeTensor(q_n, torch.float32), kv, kv, ok, None, None, None)
+    with pytest.raises(ValueError, match="elements"):
+        api.h2o_sdpa_scoresum(d, _cache(), 0, _FakeTensor(q_n - 1, torch.bfloat16), kv, kv, ok, None, None, None)
+    wsum_short = _FakeTensor(2 * (10 + 64) - 1, torch.float32)
+    with pytest.raises(ValueError, match="wsum"):
+        api.h2o_sdpa_scoresum(d, _cache(), 10, ok, kv, kv, ok, wsum_short, None, None)
+    with pytest.raises(ValueError, match="slot_log"):
+        api.h2o_evict_topk(d, _cache(), 0, 0, _FakeTensor(2 * 64, torch.float32), _FakeTensor(2 * 64, torch.int64))
+    with pytest.raises(ValueError, match="cache k"):
+        api.cache_struct(_FakeTensor(2 * 256 * 128 - 8, torch.bfloat16), kv, dims=d)
+
+
+def test_debug_build_host_asan():
+    """The debug build's host checker: the ABI layer's host code under
+    AddressSanitizer, every entry point driven through its validation paths
+    (built here if missing; it runs only where no GPU is visible)."""
+    import subprocess
+    from h2o_kv_cache_sdpa_amd import build as B
+    if not os.path.exists(B.ASAN_EXE):
+        B.build_debug()
+    libs = subprocess.run(["ldd", B.ASAN_EXE], capture_output=True, text=True).stdout
+    assert "libasan" in libs, "checker is not linked with AddressSanitizer"
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    r = subprocess.run([B.ASAN_EXE], capture_output=True, text=True, env=env, timeout=300)
+    if r.returncode == 2 and "GPU is visible" in r.stdout:
+        pytest.skip("the host checker runs on hosts without a GPU")
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi checks ok" in r.stdout

@@ -112,12 +112,13 @@ def test_backward_rejects_quantised_cache():
     dims = api.make_dims(1, 8, 2, 128, 256, 16, "bf16", "int8")
     ws = torch.empty(api.workspace_bytes(dims), dtype=torch.uint8, device=DEV)
     t = torch.zeros(1, 8, 16, 128, dtype=torch.bfloat16, device=DEV)
+    t2 = torch.zeros(1, 2, 16, 128, dtype=torch.bfloat16, device=DEV)
     f = torch.zeros(1, 8, 16, 128, dtype=torch.float32, device=DEV)
+    f2 = torch.zeros(1, 2, 16, 128, dtype=torch.float32, device=DEV)
     k = torch.zeros(1, 2, 256, 128, dtype=torch.int8, device=DEV)
     s = torch.zeros(1, 2, 256, dtype=torch.float16, device=DEV)
     bufs = api.cache_struct(k, k, k_scale=s, v_scale=s)
     lse = torch.zeros(1, 8, 16, dtype=torch.float32, device=DEV)
     with pytest.raises(api.H2OError) as e:
-        api.h2o_sdpa_backward(dims, bufs, 0, t, t[:, :2], t[:, :2], lse, t, f, None, None, f[:, :2],
-                              f[:, :2], ws)
+        api.h2o_sdpa_backward(dims, bufs, 0, t, t2, t2, lse, t, f, None, None, f2, f2, ws)
     assert e.value.status == api.H2O_EUNSUPPORTED

@@ -68,10 +68,13 @@ def test_noalloc_matches_chunk_step_twice_second_smaller():
 
 
 def test_noalloc_rejects_workspace_beyond_the_array():
-    # stored logits of a 4-token chunk on a 1M-slot cache need more than the array
+    # stored logits of a 4-token chunk on a 1M-slot cache need more than the
+    # array; the call is rejected before any buffer is touched
+    import ctypes
     dims = api.make_dims(1, 32, 8, 128, 1 << 20, 4)
     t = torch.zeros(16, dtype=torch.bfloat16, device=DEV)
-    bufs = api.cache_struct(t, t, scores=t, token_pos=t)
-    with pytest.raises(api.H2OError) as e:
-        api.h2o_chunk_step_noalloc(dims, bufs, 1 << 20, 1 << 20, t, t, t, t, None, t)
-    assert e.value.status == api.H2O_EWORKSPACE
+    p = ctypes.c_void_p(t.data_ptr())
+    bufs = api.H2OCacheBufs(p.value, p.value, None, None, None, None, p.value, p.value)
+    st = api.lib().h2o_chunk_step_noalloc(ctypes.byref(dims), ctypes.byref(bufs), 1 << 20, 1 << 20, p, p, p, p,
+                                          None, p, None)
+    assert st == api.H2O_EWORKSPACE
