@@ -70,6 +70,31 @@ def pairs_visible(B, Hq, T, n_occ):
     return B * Hq * (T * n_occ + T * (T + 1) // 2)
 
 
+def gemm_ceiling(dev, n=8192, reps=10):
+    """The matrix rate this GPU sustains on a plain library GEMM (torch.matmul
+    in bf16, n x n x n, hipBLASLt), for context beside the nominal peak: under
+    a full matrix-core load the clock settles well below its maximum."""
+    import torch
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"achieved": tf, "unit": "TFLOP/s", "frac_of_peak": tf / PEAK_BF16_TFLOPS,
+            "how": f"torch.matmul bf16 {n}x{n}x{n}, mean of {reps} after 3 warm-up calls"}
+
+
 def host_description(blas):
     """CPU model, logical CPUs and the BLAS the oracle's products run on."""
     model = None
@@ -586,6 +611,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, choices=[2, 3, 4, 5])
     ap.add_argument("--policy", default="h2o", choices=["h2o", "h2o_norm", "h2o_orig"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-ceiling", action="store_true",
+                    help="skip the library-GEMM rate printed beside the headline for context")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--trace-from", metavar="DIR",
@@ -735,6 +762,10 @@ def main():
         "attn_b_tflops": flops_b / (b_ms * 1e-3) / 1e12,
         "wall_s_timed": wall,
     }
+    if not args.no_gemm_ceiling:
+        line["gemm_ceiling"] = gemm_ceiling(dev)
+        line["step_frac_of_gemm_ceiling_6d"] = (6 * D * pairs / (ms_step * 1e-3) / 1e12
+                                                / line["gemm_ceiling"]["achieved"])
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)

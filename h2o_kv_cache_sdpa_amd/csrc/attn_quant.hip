@@ -57,7 +57,8 @@ struct QTile {
 };
 
 // 32 codes starting at element 32*q of a key row -> 32 bf16 (4 x 16 bytes).
-template <int FMT>
+// OFF16 (4-bit keys): code n widens to 16 + n, see below.
+template <int FMT, bool OFF16 = false>
 __device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4]) {
   if constexpr (FMT == FMT_INT8) {
     const uint4 a = *reinterpret_cast<const uint4 *>(codes);
@@ -74,6 +75,29 @@ __device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4]) {
         const float f2 = static_cast<float>((x << 8) >> 24), f3 = static_cast<float>(x >> 24);
         r[2 * h] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
         r[2 * h + 1] = __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u);
+      }
+      out[i] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+  } else if constexpr (OFF16) {
+    // A 4-bit key code n widens to 16 + n, whose bf16 pattern is
+    // 0x4180 | n << 3 (exponent of 16, n in the top 4 of the 7 mantissa
+    // bits): no conversion instruction, and 16 + n is still an integer exact
+    // in bf16.  The logits take the offset back out through the zero point:
+    // s n + z = s (16 + n) + (z - 16 s).  (Values keep their codes: there
+    // the offset would pass through the bf16-rounded P s_v and cost accuracy.)
+    const uint4 a = *reinterpret_cast<const uint4 *>(codes);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // even elements are the low nibbles, odd ones the high nibbles
+      const uint32_t ev = w[i] & 0x0f0f0f0fu, od = (w[i] >> 4) & 0x0f0f0f0fu;
+      uint32_t r[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // bytes [ev_q, 0, od_q, 0] (selector 0x0c yields a zero byte)
+        const uint32_t sel = 0x0c000c00u | ((4u + q) << 16) | static_cast<uint32_t>(q);
+        const uint32_t y = __builtin_amdgcn_perm(od, ev, sel);
+        r[q] = (y << 3) | 0x41804180u;
       }
       out[i] = make_uint4(r[0], r[1], r[2], r[3]);
     }
@@ -204,7 +228,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   auto widen_rows = [&](int j, const char *cs, const void *nsrc, char *dst, bool is_v) {
     uint4 w[4];
     if (j < n_occ) {
-      widen32<FMT>(cs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), w);
+      if (is_v) {
+        widen32<FMT>(cs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), w);
+      } else {
+        widen32<FMT, true>(cs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), w);
+      }
     } else {
       const int t = j - n_occ;
 #pragma unroll
@@ -229,7 +257,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
       fac[0][tid] = cached ? f16_to_f32(fcs[0][tid]) * a.sl2 : a.sl2;
       fac[2][tid] = cached ? f16_to_f32(fcs[1][tid]) : 1.f;
       if constexpr (FMT == FMT_INT4) {
-        fac[1][tid] = cached ? f16_to_f32(fcs[2][tid]) * a.sl2 : 0.f;
+        // the widened key codes are 16 + n: k = s n + z = s (16 + n) + (z - 16 s)
+        fac[1][tid] = cached ? (f16_to_f32(fcs[2][tid]) - 16.f * f16_to_f32(fcs[0][tid])) * a.sl2 : 0.f;
         fac[3][tid] = cached ? f16_to_f32(fcs[3][tid]) : 0.f;
       }
     }
@@ -322,10 +351,14 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
         c1[r] = (row_ok && ja + 32 <= i_q) ? c1[r] : -INFINITY;
       }
     }
-    float mx = fmaxf(c0[0], c1[0]);
+    float mx = __builtin_fmaxf(__builtin_fmaxf(c0[0], c1[0]), c0[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(c0[r], c1[r]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int r = 1; r < 15; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, c1[r]), c0[r + 1]);
+    mx = __builtin_fmaxf(mx, c1[15]);
+    {  // the other half-wave holds the other 32 keys of the lane's row
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     if (__ballot(mx > m_run + RESCALE_SLACK)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -574,15 +607,15 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   auto store_fac = [&](float (*fac)[64], bool cached, const uint16_t *f) {
     fac[0][fkey] = cached ? f16_to_f32(f[0]) * a.sl2 : a.sl2;
     fac[2][fkey] = cached ? f16_to_f32(f[1]) : 1.f;
-    if constexpr (FMT == FMT_INT4) {
-      fac[1][fkey] = cached ? f16_to_f32(f[2]) * a.sl2 : 0.f;
+    if constexpr (FMT == FMT_INT4) {  // widened key codes are 16 + n: key zero point z - 16 s
+      fac[1][fkey] = cached ? (f16_to_f32(f[2]) - 16.f * f16_to_f32(f[0])) * a.sl2 : 0.f;
       fac[3][fkey] = cached ? f16_to_f32(f[3]) : 0.f;
     }
   };
   // a tile wholly in the cache, from the prefetched registers
   auto widen_full = [&](const Codes &c, char *kb, char *vb, float (*fac)[64]) {
     uint4 kw[4], vw[4];
-    widen32<FMT>(reinterpret_cast<const char *>(c.k), kw);
+    widen32<FMT, true>(reinterpret_cast<const char *>(c.k), kw);
     widen32<FMT>(reinterpret_cast<const char *>(c.v), vw);
     store(kb, vb, kw, vw);
     if (lane < 16) store_fac(fac, true, c.f);
@@ -595,7 +628,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     uint4 kw[4], vw[4];
     if (j < n_occ) {
       const size_t off = (cache_row0 + j) * Q::CODE_ROW + cq * (Q::CODE_ROW / 4);
-      widen32<FMT>(static_cast<const char *>(a.kc) + off, kw);
+      widen32<FMT, true>(static_cast<const char *>(a.kc) + off, kw);
       widen32<FMT>(static_cast<const char *>(a.vc) + off, vw);
     } else {
       const int t = j - n_occ;
