@@ -208,56 +208,82 @@ def trace_summary(folder, skip):
 
 def counters_summary(folders, skip, cus=256, xcds=8):
     """Per-kernel averages of the counters in rocprofv3 --pmc folders (first
-    `skip` dispatches of every kernel left out), with the ratios derived from
-    them.  SQ counters are chip totals; GRBM_GUI_ACTIVE is summed over the
-    XCDs, so GRBM_GUI_ACTIVE / xcds is the kernel's length in GPU cycles."""
+    `skip` dispatches of every kernel left out; the library's kernels only),
+    with ratios derived from them.  SQ counters are chip totals.
+    GRBM_GUI_ACTIVE is summed over the XCDs, so GRBM_GUI_ACTIVE / xcds is the
+    kernel's length in GPU cycles (cyc), and a SIMD-cycle share divides by
+    cyc * 4 * cus.  SQ_VALU_MFMA_BUSY_CYCLES counts 32 cycles per
+    32x32x16 MFMA; SQ_ACTIVE_INST_VALU counts one 4-cycle issue slot per
+    vector instruction (MFMAs included) and one more per transcendental, so
+    4 * (SQ_ACTIVE_INST_VALU - SQ_INSTS_MFMA) estimates the SIMD cycles the
+    vector ALU is busy.  SQ_WAVE_CYCLES and the SQ_WAIT counters are in the
+    same (4-cycle) units, so their ratios are shares of wave time."""
     per = {}
     for folder in folders:
-        seen = {}
         for r in _csv_rows(folder, "counter_collection.csv"):
             name = _short_kernel_name(r["Kernel_Name"])
+            if name.startswith("at::"):
+                continue
             did = int(r["Dispatch_Id"])
-            seen.setdefault(name, set()).add(did)
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
             per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append((did, float(r["Counter_Value"]), dur))
     out = []
     for name, cnt in sorted(per.items()):
         avg = {}
         durs = []
+        nd = 0
         for c, vals in cnt.items():
             vals.sort()
             used = vals[skip:] or vals
+            nd = len(used)
             avg[c] = sum(v for _, v, _ in used) / len(used)
             durs += [d for _, _, d in used]
-        out.append(f"## {name}  (dispatches averaged: {len(used)}, mean duration {sum(durs) / len(durs):.1f} us)")
+        out.append(f"## {name}  (dispatches averaged: {nd}, mean duration {sum(durs) / len(durs):.1f} us)")
         for c in sorted(avg):
             out.append(f"  {c:34s} {avg[c]:18.1f}")
+        derived = []
         cyc = avg.get("GRBM_GUI_ACTIVE")
+        if cyc and sum(durs) / len(durs) < 100.0:
+            out.append("  (shorter than 100 us: launch overhead dominates GRBM_GUI_ACTIVE, so no cycle shares)")
+            cyc = None
         if cyc:
             cyc /= xcds
             simd = cyc * cus * 4
-            derived = []
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-                derived.append(("MFMA busy, share of SIMD cycles", avg["SQ_VALU_MFMA_BUSY_CYCLES"] / simd))
-            if "SQ_ACTIVE_INST_VALU" in avg:
-                derived.append(("VALU issue, share of SIMD cycles", avg["SQ_ACTIVE_INST_VALU"] / simd))
-            if "SQ_ACTIVE_INST_LDS" in avg:
-                derived.append(("LDS issue, share of SIMD cycles", avg["SQ_ACTIVE_INST_LDS"] / simd))
+            derived.append(("GPU clock over the kernel (GHz)", cyc / (sum(durs) / len(durs)) * 1e-3))
+            mfma = avg.get("SQ_VALU_MFMA_BUSY_CYCLES")
+            if mfma is not None:
+                derived.append(("MFMA busy, share of SIMD cycles", mfma / simd))
+            valu = None
+            if "SQ_ACTIVE_INST_VALU" in avg and "SQ_INSTS_MFMA" in avg:
+                valu = 4 * (avg["SQ_ACTIVE_INST_VALU"] - avg["SQ_INSTS_MFMA"]) / simd
+                derived.append(("vector ALU busy (estimate), share of SIMD cycles", valu))
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in avg:
+                co = avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / simd
+                derived.append(("MFMA and vector ALU both busy, share", co))
+                if mfma is not None and valu is not None:
+                    derived.append(("neither busy, share", 1 - mfma / simd - valu + co))
             if "SQ_LDS_IDX_ACTIVE" in avg:
                 derived.append(("LDS active, share of CU cycles", avg["SQ_LDS_IDX_ACTIVE"] / (cyc * cus)))
             if "SQ_LDS_BANK_CONFLICT" in avg:
                 derived.append(("LDS bank-conflict cycles, share of CU cycles",
                                 avg["SQ_LDS_BANK_CONFLICT"] / (cyc * cus)))
-            if "SQ_WAIT_INST_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
-                derived.append(("waves waiting on an instruction dependency", avg["SQ_WAIT_INST_ANY"] / avg["SQ_WAVE_CYCLES"]))
-            if "SQ_WAIT_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
-                derived.append(("waves waiting (any reason)", avg["SQ_WAIT_ANY"] / avg["SQ_WAVE_CYCLES"]))
-            if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg and avg["SQ_INSTS_MFMA"]:
-                derived.append(("VALU instructions per MFMA", avg["SQ_INSTS_VALU"] / avg["SQ_INSTS_MFMA"]))
-            clk = cyc / (sum(durs) / len(durs)) * 1e-3
-            out.append(f"  {'GPU clock over the kernel (GHz)':34s} {clk:18.3f}")
-            for label, v in derived:
-                out.append(f"  {label:50s} {v:8.3f}")
+        if "SQ_WAVE_CYCLES" in avg:
+            for c, label in (("SQ_WAIT_INST_ANY", "waiting on a dependency, share of wave time"),
+                             ("SQ_WAIT_ANY", "waiting (any reason), share of wave time"),
+                             ("SQ_WAIT_INST_LDS", "waiting on LDS, share of wave time")):
+                if c in avg:
+                    derived.append((label, avg[c] / avg["SQ_WAVE_CYCLES"]))
+        if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
+            m = avg["SQ_INSTS_MFMA"]
+            derived.append(("vector instructions per MFMA", (avg["SQ_INSTS_VALU"] - m) / m))
+            for c, label in (("SQ_INSTS_VALU_TRANS_F32", "  of them transcendental"),
+                             ("SQ_INSTS_VALU_FMA_F32", "  of them FMA"), ("SQ_INSTS_VALU_ADD_F32", "  of them add"),
+                             ("SQ_INSTS_VALU_MUL_F32", "  of them multiply"), ("SQ_INSTS_VALU_CVT", "  of them conversion"),
+                             ("SQ_INSTS_LDS", "LDS instructions per MFMA"), ("SQ_INSTS_SALU", "scalar instructions per MFMA")):
+                if c in avg:
+                    derived.append((label, avg[c] / m))
+        for label, v in derived:
+            out.append(f"  {label:52s} {v:8.3f}")
         out.append("")
     return "\n".join(out)
 

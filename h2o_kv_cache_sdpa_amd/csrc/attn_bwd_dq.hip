@@ -1,6 +1,6 @@
 // Backward of the chunk attention, dQ ("Learning how to Forget", §3.2): see
 // attn_bwd.hip for the formulas.  bwd_dq: 128 query rows per workgroup
-// (4 waves x 32), K and V tiles of 64 keys moved HBM -> LDS by buffer-load
+// (4 waves x 32; 256 rows, 8 waves, for the row terms), K and V tiles of 64 keys moved HBM -> LDS by buffer-load
 // DMA, double-buffered.  S^T = K Q^T and dP^T = V dO^T on the matrix cores
 // with Q and dO held in registers; dS in registers becomes the B operand of
 // dQ^T += K^T dS^T, the K^T operand read from the row-major K tile by
@@ -27,11 +27,15 @@ namespace h2o {
 namespace {
 
 constexpr float LOG2E = 1.4426950408889634074f;
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008;  // __builtin_amdgcn_sched_group_barrier masks
 
-// dQ (ROWTERM = false) or the row terms L2, D (ROWTERM = true): 128 packed
-// query rows per block (r = i * q_g + h), keys streamed
-template <bool ROWTERM>
-__global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
+// dQ (ROWTERM = false) or the row terms L2, D (ROWTERM = true): 32 packed
+// query rows (r = i * q_g + h) per wavefront, NW wavefronts per block, keys
+// streamed.  dQ needs more than 256 registers (4 wavefronts, one per SIMD);
+// the row terms fit two per SIMD, so 8 wavefronts share each K / V tile.
+template <bool ROWTERM, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void bwd_dq(BwdArgs a) {
+  constexpr int ROWS = 32 * NW, SPW = 16 / NW;  // rows per block, 1 KB tile segments per wavefront
   __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
@@ -40,13 +44,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 31, hl = lane >> 5;
   const int R = a.qg * a.T;
-  const int tiles_per_grp = (R + 127) / 128;
+  const int tiles_per_grp = (R + ROWS - 1) / ROWS;
   const int wi = xcd_remap(blockIdx.x, gridDim.x);
   // Row blocks go out last first: under the causal mask the last rows see the
   // most keys, and starting the longest blocks first evens out the tail.
   const int grp = wi / tiles_per_grp, rt = tiles_per_grp - 1 - wi % tiles_per_grp;
   const int g = grp % a.Hkv, b = grp / a.Hkv;
-  const int row0 = rt * 128;
+  const int row0 = rt * ROWS;
   const int my_row = row0 + wave * 32 + n;
   const bool row_ok = my_row < R;
   const int i_q = row_ok ? my_row / a.qg : 0;
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
   const float Dr = (row_ok && !ROWTERM) ? a.dd[li] : 0.f;
   float d_acc = 0.f;  // ROWTERM: sum of P dP over the keys so far
 
-  const int last_row = min(R, row0 + 128) - 1;
+  const int last_row = min(R, row0 + ROWS) - 1;
   const int key_end = n_occ + last_row / a.qg + 1;
   const int ntiles = (key_end + 63) / 64;
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
@@ -89,24 +93,24 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
   const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
   // both tiles in the K/Q swizzle: read row-wise for S^T / dP^T and (K) transposed for dQ
   auto lane_off = [&](int q) -> uint32_t {
-    const int row = (wave * 4 + q) * 4 + (lane >> 4);
+    const int row = (wave * SPW + q) * 4 + (lane >> 4);
     return static_cast<uint32_t>(row * ROW_BYTES + 16 * kq_chunk_at(row, lane & 15));
   };
   auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs) {
     const int j0 = tile * 64;
     if (j0 + 64 <= n_occ) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
+      for (int q = 0; q < SPW; ++q) dma16(crs, lane_off(q), j0 * ROW_BYTES, dst + (wave * SPW + q) * 1024);
     } else {
       const int dt = j0 - n_occ;  // chunk index of the tile's first row, may be < 0
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = (wave * 4 + q) * 4 + (lane >> 4);
+      for (int q = 0; q < SPW; ++q) {
+        const int row = (wave * SPW + q) * 4 + (lane >> 4);
         const uint32_t lo = lane_off(q);
         if (dt + row >= 0) {
-          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * SPW + q) * 1024);
         } else {
-          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
+          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * SPW + q) * 1024);
         }
       }
     }
@@ -117,8 +121,60 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
 #pragma unroll
   for (int k = 0; k < 4; ++k) dq[k] = f32x16{};
 
+  // Row terms of one 64-key tile: the S / dP MFMAs of the second 32-key half
+  // run beside the exponentials of the first (the terms need no dQ product,
+  // so both halves' results fit in registers at once).
+  auto rowterm_tile = [&](int t, const char *kb, const char *vb) __attribute__((always_inline)) {
+    f32x16 s0 = f32x16{}, p0 = f32x16{}, s1 = f32x16{}, p1 = f32x16{};
+    float part = 0.f;
+    // wave-uniform: every row of the wave exists and sees every key of the half
+    const bool full0 = wave_rows_ok && t * 64 + 31 - n_occ <= wave_i_min;
+    const bool full1 = wave_rows_ok && t * 64 + 63 - n_occ <= wave_i_min;
+    auto term = [&](bool full, int k0, float sv, float dpv, int r) {
+      const int ja = t * 64 + k0 + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
+      const bool vis = full || (row_ok && ja <= i_q);
+      const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(sv, sl2, -Lr)) : 0.f;
+      part = fmaf(pp, dpv, part);
+    };
+    auto chain = [&](int k0, f32x16 &sacc, f32x16 &pacc, bool overlap) {
+      const int kr = k0 + prow;
+      bf16x8 ka = lds16(kb + kq_off(kr, hl)), va = lds16(vb + kq_off(kr, hl));
+#pragma unroll
+      for (int st = 0; st < 8; ++st) {
+        bf16x8 nk = ka, nv = va;
+        if (st < 7) {
+          nk = lds16(kb + kq_off(kr, 2 * st + 2 + hl));
+          nv = lds16(vb + kq_off(kr, 2 * st + 2 + hl));
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sacc = mfma32(ka, qf[st], sacc);
+        pacc = mfma32(va, gf[st], pacc);
+        ka = nk;
+        va = nv;
+        if (overlap) {  // two of the first half's 16 terms per step
+          term(full0, 0, s0[2 * st], p0[2 * st], 2 * st);
+          term(full0, 0, s0[2 * st + 1], p0[2 * st + 1], 2 * st + 1);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    chain(0, s0, p0, false);
+    chain(32, s1, p1, true);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) term(full1, 32, s1[r], p1[r], r);
+    d_acc += part;
+  };
+
   // One 64-key tile in two halves of 32 keys (keeps one S / dP pair live).
-  auto compute = [&](int t, const char *kb, const char *vb) {
+  auto compute = [&](int t, const char *kb, const char *vb) __attribute__((always_inline)) {
+    if constexpr (ROWTERM) {
+      rowterm_tile(t, kb, vb);
+      return;
+    }
 #pragma unroll 1
     for (int half = 0; half < 2; ++half) {
       const int kr = 32 * half + prow;  // K / V row of the lane's operand
@@ -143,18 +199,6 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
       // register r: key t*64 + 32*half + 16*(r/8) + 8*hl + r%8 of the lane's row
       // wave-uniform: every row of the wave exists and sees every key of the half
       const bool half_full = wave_rows_ok && t * 64 + 32 * half + 31 - n_occ <= wave_i_min;
-      if constexpr (ROWTERM) {
-        float part = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ja = t * 64 + 32 * half + 16 * (r >> 3) + 8 * hl + (r & 7) - n_occ;  // chunk index
-          const bool vis = half_full || (row_ok && ja <= i_q);
-          const float pp = vis ? __builtin_amdgcn_exp2f(fmaf(s0[r], sl2, -Lr)) : 0.f;
-          part = fmaf(pp, p0[r], part);
-        }
-        d_acc += part;
-        continue;
-      }
       bf16x8 dsb[2];
       if (half_full) {
 #pragma unroll
@@ -233,15 +277,14 @@ __global__ __launch_bounds__(256, 1) void bwd_dq(BwdArgs a) {
 hipError_t launch_bwd_dq(const BwdArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
   const int R = a.qg * a.T;
-  const dim3 grid(groups * ((R + 127) / 128));
   {
     KernelTimer timer(H2O_K_BWD_ROWS, s);
-    hipLaunchKernelGGL(bwd_dq<true>, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((bwd_dq<true, 8>), dim3(groups * ((R + 255) / 256)), dim3(512), 0, s, a);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   KernelTimer timer(H2O_K_BWD_DQ, s);
-  hipLaunchKernelGGL(bwd_dq<false>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bwd_dq<false, 4>), dim3(groups * ((R + 127) / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
