@@ -208,8 +208,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
     mx = __builtin_fmaxf(mx, c0[15]);
 #pragma unroll
     for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(__builtin_fmaxf(mx, c1[r]), c1[r + 1]);
-    mx *= sl2;
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(mx * sl2);  // the other half-wave holds the row's other 32 keys
     if (__ballot(mx > m_run + RESCALE_SLACK)) {
       const float m_new = __builtin_fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -480,8 +479,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_dec(AttnArgs a) {
       c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 16));
-    mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
+    mx = max_xor32(max_xor16(mx));
     mx *= sl2;
     if (mx > m_run + RESCALE_SLACK) {  // uniform across the row's four lanes
       const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mx);

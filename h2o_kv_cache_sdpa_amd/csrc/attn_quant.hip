@@ -355,10 +355,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
 #pragma unroll
     for (int r = 1; r < 15; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, c1[r]), c0[r + 1]);
     mx = __builtin_fmaxf(mx, c1[15]);
-    {  // the other half-wave holds the other 32 keys of the lane's row
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
+    mx = max_xor32(mx);  // the other half-wave holds the other 32 keys of the lane's row
     if (__ballot(mx > m_run + RESCALE_SLACK)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -562,17 +559,16 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
-  // Codes move HBM -> registers with plain vector loads, PD tiles ahead of
+  // Codes move HBM -> registers with plain vector loads, one tile ahead of
   // their use: thread tid holds the 32 codes of key row tid / 4, quarter
   // tid % 4, of K and of V (int8: 2 x 16 bytes each, int4: 16 bytes), and
-  // lane l < 16 of wavefront w the fp16 factors of key 16w + l.  Loads into
-  // registers keep their order in the vector-memory counter, so each tile
-  // waits only for its own loads; an LDS-DMA pipeline this deep would wait
-  // for all.  Wavefront w widens, stores and reads back only the rows of its
-  // own keys 16w .. 16w + 15, so the wavefronts never wait for each other
-  // inside the tile loop.
+  // every lane of wavefront w the fp16 factors of key 16w + lane % 16.
+  // (Prefetching two or three tiles ahead measured slower: the per-tile
+  // chain of widening, LDS round trip and products sets the pace, not the
+  // loads in flight.)  Wavefront w widens, stores and reads back only the
+  // rows of its own keys 16w .. 16w + 15, so the wavefronts never wait for
+  // each other inside the tile loop.
   constexpr int CW = Q::CODE_ROW / 4 / 16;  // 16-byte words of one thread's share
-  constexpr int PD = (FMT == FMT_INT8) ? 2 : 3;
   struct Codes {
     uint4 k[CW], v[CW];
     uint16_t f[Q::NFAC];
@@ -618,7 +614,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     widen32<FMT, true>(reinterpret_cast<const char *>(c.k), kw);
     widen32<FMT>(reinterpret_cast<const char *>(c.v), vw);
     store(kb, vb, kw, vw);
-    if (lane < 16) store_fac(fac, true, c.f);
+    store_fac(fac, true, c.f);  // four lanes per key write the same values
   };
   // any other tile, loading as it goes: codes of rows below n_occ, new keys
   // (bf16) above, zeros past the chunk
@@ -690,9 +686,8 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
       const int ja = j0 + kk0 + i - n_occ;
       c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
     }
-    float mx = fmaxf(fmaxf(c[0], c[1]), fmaxf(c[2], c[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    float mx = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
+    mx = max_xor32(max_xor16(mx));
     if (mx > m_run + RESCALE_SLACK) {
       const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mx);
       l_run *= alpha;
@@ -723,33 +718,31 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     }
   };
 
-  // Tile t: widen into buffer t & 1, refill its registers with tile t + PD,
+  // Tile t: widen into buffer t & 1, refill the registers with tile t + 1,
   // compute.  Lanes read rows that other lanes of their wavefront wrote;
   // wave_lds_sync keeps the reads of tile t after its writes, and (one tile
   // on) the reads of tile t - 1 before the writes of tile t + 1 into the
-  // same buffer.
-  // Groups of G tiles are unrolled straight-line: the compiler counts the
-  // loads in flight exactly there, while across a loop back-edge it waits
-  // for all of them (so it drains once per group, not once per tile).
+  // same buffer.  Tiles go in pairs (buffers 0, 1) with no branch inside a
+  // pair, so the compiler may overlap one tile's widening with the other's
+  // products.
   if (nfull > 0) {
-    constexpr int G = 3 * PD;
-    Codes cr[PD];
-#pragma unroll
-    for (int p = 0; p < PD; ++p) load_codes(p, cr[p]);
-    for (int t0 = 0; t0 < nfull; t0 += G) {
-#pragma unroll
-      for (int p = 0; p < G; ++p) {
-        const int t = t0 + p;
-        char *kb = (p & 1) ? kb1 : kb0;  // t0 is even: t & 1 == p & 1
-        char *vb = (p & 1) ? vb1 : vb0;
-        float (*fac)[64] = (p & 1) ? fac1 : fac0;
-        if (t < nfull) widen_full(cr[p % PD], kb, vb, fac);
-        load_codes(t + PD, cr[p % PD]);
-        if (t < nfull) {
-          wave_lds_sync();
-          compute(t, kb, vb, fac);
-        }
-      }
+    Codes cr;
+    load_codes(0, cr);
+    int t = 0;
+    for (; t + 2 <= nfull; t += 2) {
+      widen_full(cr, kb0, vb0, fac0);
+      load_codes(t + 1, cr);
+      wave_lds_sync();
+      compute(t, kb0, vb0, fac0);
+      widen_full(cr, kb1, vb1, fac1);
+      load_codes(t + 2, cr);
+      wave_lds_sync();
+      compute(t + 1, kb1, vb1, fac1);
+    }
+    if (t < nfull) {
+      widen_full(cr, kb0, vb0, fac0);
+      wave_lds_sync();
+      compute(t, kb0, vb0, fac0);
     }
   }
   for (int t = nfull; t < ntiles; ++t) {

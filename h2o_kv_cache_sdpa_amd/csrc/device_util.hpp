@@ -52,6 +52,23 @@ __device__ __forceinline__ float cache_elem(const void *buf, const uint16_t *sca
   }
 }
 
+// Maximum of x over lanes l and l ^ 32.  v_permlane32_swap exchanges the
+// wavefront's halves on the VALU; __shfl_xor would go through the LDS
+// crossbar (ds_bpermute) and wait for every LDS access in flight.  With both
+// operands x, the two results at lane l are x[l % 32] and x[32 + l % 32].
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
+// Maximum of x over lanes l and l ^ 16 (v_permlane16_swap: rows of 16 lanes,
+// odd rows of the first operand trade with even rows of the second; at lane
+// l the two results are x of rows 2k and 2k + 1, k = l / 32).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   // Blocks are dispatched round-robin over the 8 XCDs of an MI355X.  Remap so
   // that each XCD receives a contiguous range of work items (shared L2 lines).
