@@ -30,6 +30,7 @@
 
 #include "device_util.hpp"
 #include "h2o_internal.hpp"
+#include "kv_quant.hpp"
 
 namespace h2o {
 namespace {
@@ -487,9 +488,11 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
 // as slot order does.  ncand: list length per head (the last slice may fill
 // fewer than T entries: nreal counts the filled ones, which come first).
 //
-// KV: also copy the chunk's K and V rows (native cache) into the slots this
-// head took, replacing the separate write kernel for short chunks: the slots
-// stay in LDS, and the rows of T <= KV_FUSE_T tokens are a few KB per head.
+// KV: also write the chunk's K and V rows into the slots this head took,
+// replacing the separate write kernel for short chunks: the slots stay in
+// LDS, and the rows of T <= KV_FUSE_T tokens are a few KB per head.  Native
+// caches copy the rows; 8/4-bit caches (one token) quantise them, one
+// wavefront per row, with the write kernel's own row quantiser.
 template <int NTH, int ITEMS, int POL, bool KV>
 __global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand, int ncand, int nreal,
                                                  KvWriteArgs kv) {
@@ -501,6 +504,20 @@ __global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand
   auto write_rows = [&]() {
     __syncthreads();  // chosen[] complete
     const int nb = (POL == H2O_POLICY_ORIG) ? a.B : 1;
+    if (kv.cache_fmt != FMT_NATIVE) {  // bf16 rows: one wavefront per (batch row, token, K or V)
+      const int lane = tid & 63;
+      for (int r = tid >> 6; r < nb * T * 2; r += NTH / 64) {
+        const int isv = r & 1, t = (r >> 1) % T, bb = (r >> 1) / T;
+        const size_t g = (POL == H2O_POLICY_ORIG) ? static_cast<size_t>(bb) * a.Hkv + head : head;
+        const size_t dst_row = g * C + chosen[t];
+        if (kv.cache_fmt == FMT_INT8) {
+          quantize_row<DT_BF16, FMT_INT8>(kv, g * T + t, dst_row, isv, lane);
+        } else {
+          quantize_row<DT_BF16, FMT_INT4>(kv, g * T + t, dst_row, isv, lane);
+        }
+      }
+      return;
+    }
     const int row_bytes = kv.D * (kv.dtype == DT_F32 ? 4 : 2);
     const int cpr = row_bytes / 16;
     const int total = nb * T * 2 * cpr;
@@ -636,8 +653,11 @@ bool two_pass_fits(int C, int T) { return 2LL * n_slices(C) * T <= C; }
 template <int POL, bool KV>
 void launch_pick(const EvictArgs &a, const uint2 *cand, int ncand, int nreal, const KvWriteArgs &kv,
                  int heads, hipStream_t s) {
-  // short lists: one wavefront; longer ones: 256 or 1024 threads
-  if (nreal <= 64) {
+  // short lists: one wavefront (two when the pick quantises a K and a V
+  // row per head); longer ones: 256 or 1024 threads
+  if (KV && kv.cache_fmt != FMT_NATIVE && nreal <= 128) {
+    hipLaunchKernelGGL((evict_pick<128, 1, POL, KV>), dim3(heads), dim3(128), 0, s, a, cand, ncand, nreal, kv);
+  } else if (nreal <= 64) {
     hipLaunchKernelGGL((evict_pick<64, 1, POL, KV>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal, kv);
   } else if (nreal <= 256) {
     hipLaunchKernelGGL((evict_pick<64, 4, POL, KV>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal, kv);
@@ -683,8 +703,13 @@ hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream
   const size_t need = evict_workspace_bytes(a.groups, a.C, a.T);
   if (a.n_occ == a.C && need && ws && ws_bytes >= need) {
     uint2 *cand = static_cast<uint2 *>(ws);
-    // fuse the K/V write into the pick: native cache, short chunk, evict-only bookkeeping
-    const bool fuse = kv && kv_done && kv->cache_fmt == FMT_NATIVE && a.T <= KV_FUSE_T && !kv->token_pos;
+    // fuse the K/V write into the pick (evict-only bookkeeping): native
+    // caches up to KV_FUSE_T tokens; 8/4-bit caches for one token, where the
+    // two quantised rows per head cost less than a launch (from four tokens
+    // on, the write kernel's one wavefront per row is faster)
+    const bool fuse = kv && kv_done && !kv->token_pos &&
+                      ((kv->cache_fmt == FMT_NATIVE && a.T <= KV_FUSE_T) ||
+                       (kv->dtype == DT_BF16 && a.T == 1 && kv->D <= 128));
     const KvWriteArgs *kvp = fuse ? kv : nullptr;
     if (fuse) *kv_done = true;
     if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, kvp, s);

@@ -135,6 +135,17 @@ def test_stream_policies_short_chunks_batch(policy):
     _run_stream(W.WORKLOADS[3].scaled(B=2, C=256, T=4, n_fill=64, n_evict=6), policy=policy)
 
 
+@pytest.mark.parametrize("fmt,T,policy", [("int8", 1, "h2o"), ("int4", 1, "h2o_orig"),
+                                           ("int8", 4, "h2o_orig"), ("int4", 4, "h2o")])
+def test_stream_short_chunks_quant(fmt, T, policy):
+    """One- and four-token chunks into 8/4-bit caches, B = 2: the pick
+    kernel quantises the chunk's K/V rows into the slots it took (for every
+    batch row under h2o_orig); codes, scales and zero points bit for bit."""
+    base = W.WORKLOADS[4] if fmt == "int8" else W.WORKLOADS[5]
+    C = 128 if T == 1 else 256
+    _run_stream(base.scaled(B=2, C=C, T=T, n_fill=C // T, n_evict=8, cache_fmt=fmt), policy=policy)
+
+
 @pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
 def test_stream_policies_int4_batch(policy):
     _run_stream(W.WORKLOADS[5].scaled(C=512, T=32, n_fill=16, n_evict=8), policy=policy)
