@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+STEP_TARGET_FRAC = 0.60     # target for the whole evicting step, 6*D flops per visible pair
 PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector / matrix peak
 PEAK_HBM_GBS = 8000.0
 N_CHUNKS = 4                # distinct chunks rotated through the timed steps
@@ -782,7 +783,11 @@ def main():
             "frac": achieved_a / PEAK_BF16_TFLOPS,
             "traffic": traffic,
         },
+        # the whole step against the bf16 peak (the headline fraction), and the
+        # step time that STEP_TARGET_FRAC of the peak would take
         "step_mfma_frac_6d": 6 * D * pairs / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "step_target_frac_6d": STEP_TARGET_FRAC,
+        "ms_per_step_at_target": 6 * D * pairs / (STEP_TARGET_FRAC * PEAK_BF16_TFLOPS * 1e12) * 1e3,
         "step_mfma_frac_4d": 4 * D * pairs / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()},
         "attn_b_tflops": flops_b / (b_ms * 1e-3) / 1e12,
