@@ -170,9 +170,8 @@ __global__ __launch_bounds__(256, 2) void attn_a_mfma(AttnArgs a) {
   const int key_end = n_occ + last_row / a.qg + 1;  // keys any row of the block can see
   // key tiles t_lo .. t_lo + ntiles - 1 (all of them when unsplit)
   const int ntiles_all = (key_end + A_KT - 1) / A_KT;
-  const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
-  const int t_lo = split * per_split;
-  const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;  // <= 0: empty split
+  int t_lo, ntiles;  // key tiles t_lo .. t_lo + ntiles - 1 of this split (ntiles 0: none)
+  split_tiles(ntiles_all, a.nsplit, split, t_lo, ntiles);
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
 

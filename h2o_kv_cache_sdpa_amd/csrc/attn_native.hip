@@ -106,9 +106,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
   const int key_end = n_occ + last_row / a.qg + 1;
   // key tiles t_lo .. t_lo + ntiles - 1 of the block's range (all of it when unsplit)
   const int ntiles_all = (key_end + 63) / 64;
-  const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
-  const int t_lo = split * per_split;
-  const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;  // <= 0: empty split
+  int t_lo, ntiles;  // key tiles t_lo .. t_lo + ntiles - 1 of this split (ntiles 0: none)
+  split_tiles(ntiles_all, a.nsplit, split, t_lo, ntiles);
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
 
@@ -417,9 +416,8 @@ __global__ __launch_bounds__(256, 2) void attn_a_dec(AttnArgs a) {
 
   const int key_end = n_occ + (R - 1) / a.qg + 1;
   const int ntiles_all = (key_end + 63) / 64;
-  const int per_split = (ntiles_all + a.nsplit - 1) / a.nsplit;
-  const int t_lo = split * per_split;
-  const int ntiles = min(ntiles_all, t_lo + per_split) - t_lo;  // <= 0: empty split
+  int t_lo, ntiles;  // key tiles t_lo .. t_lo + ntiles - 1 of this split (ntiles 0: none)
+  split_tiles(ntiles_all, a.nsplit, split, t_lo, ntiles);
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
   const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);

@@ -69,6 +69,15 @@ __device__ __forceinline__ float max_xor16(float x) {
   return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
+// Key tiles t_lo .. t_lo + count - 1 of split `split` of `nsplit` over
+// `ntiles` tiles: the first ntiles % nsplit splits take one tile more, so no
+// split holds more than one tile above another (count 0: an empty split).
+__device__ __forceinline__ void split_tiles(int ntiles, int nsplit, int split, int &t_lo, int &count) {
+  const int base = ntiles / nsplit, rem = ntiles % nsplit;
+  t_lo = split * base + (split < rem ? split : rem);
+  count = base + (split < rem ? 1 : 0);
+}
+
 __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
   // Blocks are dispatched round-robin over the 8 XCDs of an MI355X.  Remap so
   // that each XCD receives a contiguous range of work items (shared L2 lines).
