@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
       const int seg = wave * 4 + q;
       const int rib = seg * 4 + (lane >> 4);
       const uint32_t voff =
-          static_cast<uint32_t>(src_row(rb + rib) * ROW_BYTES + 16 * kq_chunk_at(rib, lane & 15));
+          static_cast<uint32_t>(src_row(rb + rib) * ROW_BYTES + 16 * bt_chunk_at(rib, lane & 15));
       dma16(q_rs, voff, 0, qdst + seg * 1024);
       dma16(g_rs, voff, 0, gdst + seg * 1024);
     }
@@ -127,13 +127,13 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv(BwdArgs a) {
       const char *qs = qb + sub * 32 * ROW_BYTES;
       const char *gs = gb + sub * 32 * ROW_BYTES;
       f32x16 c = f32x16{}, dp = f32x16{};
-      bf16x8 qa = lds16(qs + kq_off(prow, hl)), ga = lds16(gs + kq_off(prow, hl));
+      bf16x8 qa = lds16(qs + bt_off(prow, hl)), ga = lds16(gs + bt_off(prow, hl));
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         bf16x8 nqa = qa, nga = ga;
         if (st < 7) {
-          nqa = lds16(qs + kq_off(prow, 2 * st + 2 + hl));
-          nga = lds16(gs + kq_off(prow, 2 * st + 2 + hl));
+          nqa = lds16(qs + bt_off(prow, 2 * st + 2 + hl));
+          nga = lds16(gs + bt_off(prow, 2 * st + 2 + hl));
         }
         __builtin_amdgcn_sched_barrier(0);
         c = mfma32(qa, kf[st], c);

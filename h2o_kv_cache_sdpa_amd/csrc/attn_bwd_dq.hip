@@ -91,10 +91,10 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq(BwdArgs a) {
   const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
   const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
   const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
-  // both tiles in the K/Q swizzle: read row-wise for S^T / dP^T and (K) transposed for dQ
+  // both tiles in the bt swizzle: read row-wise for S^T / dP^T and (K) transposed for dQ
   auto lane_off = [&](int q) -> uint32_t {
     const int row = (wave * SPW + q) * 4 + (lane >> 4);
-    return static_cast<uint32_t>(row * ROW_BYTES + 16 * kq_chunk_at(row, lane & 15));
+    return static_cast<uint32_t>(row * ROW_BYTES + 16 * bt_chunk_at(row, lane & 15));
   };
   auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs) {
     const int j0 = tile * 64;
@@ -138,13 +138,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq(BwdArgs a) {
     };
     auto chain = [&](int k0, f32x16 &sacc, f32x16 &pacc, bool overlap) {
       const int kr = k0 + prow;
-      bf16x8 ka = lds16(kb + kq_off(kr, hl)), va = lds16(vb + kq_off(kr, hl));
+      bf16x8 ka = lds16(kb + bt_off(kr, hl)), va = lds16(vb + bt_off(kr, hl));
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         bf16x8 nk = ka, nv = va;
         if (st < 7) {
-          nk = lds16(kb + kq_off(kr, 2 * st + 2 + hl));
-          nv = lds16(vb + kq_off(kr, 2 * st + 2 + hl));
+          nk = lds16(kb + bt_off(kr, 2 * st + 2 + hl));
+          nv = lds16(vb + bt_off(kr, 2 * st + 2 + hl));
         }
         __builtin_amdgcn_sched_barrier(0);
         sacc = mfma32(ka, qf[st], sacc);
@@ -181,13 +181,13 @@ __global__ __launch_bounds__(64 * NW, 1) void bwd_dq(BwdArgs a) {
       f32x16 s0 = f32x16{}, p0 = f32x16{};
       // operands one step ahead of their MFMAs; the barriers keep the compiler
       // from hoisting every step's reads (and their registers) to the top
-      bf16x8 k0 = lds16(kb + kq_off(kr, hl)), v0 = lds16(vb + kq_off(kr, hl));
+      bf16x8 k0 = lds16(kb + bt_off(kr, hl)), v0 = lds16(vb + bt_off(kr, hl));
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         bf16x8 nk0 = k0, nv0 = v0;
         if (st < 7) {
-          nk0 = lds16(kb + kq_off(kr, 2 * st + 2 + hl));
-          nv0 = lds16(vb + kq_off(kr, 2 * st + 2 + hl));
+          nk0 = lds16(kb + bt_off(kr, 2 * st + 2 + hl));
+          nv0 = lds16(vb + bt_off(kr, 2 * st + 2 + hl));
         }
         __builtin_amdgcn_sched_barrier(0);
         s0 = mfma32(k0, qf[st], s0);

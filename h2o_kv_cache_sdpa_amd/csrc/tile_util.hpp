@@ -71,15 +71,27 @@ __device__ __forceinline__ i16x4 lds_tr(const char *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p));
 }
 
-// Transpose read of a K/Q-swizzled tile: for lane l the 8 rows
+// Tiles the backward reads both row-wise (16 rows at one chunk index) and
+// transposed (4 aligned rows x 4 aligned chunks per half-wave): chunk c of
+// row r at r*256 + 16*(c ^ g(r)), g(r) = 4*(r & 3) + ((r >> 2) & 3).  g is a
+// bijection of r & 15, so a row-wise read meets 16 distinct 16-byte groups;
+// over 4 aligned rows (r >> 2) & 3 is fixed and 4*(r & 3) moves the 4
+// aligned chunks to 4 distinct quarters, so a transpose read meets all 16
+// groups too (the K/Q swizzle put those 4 x 4 chunks on 4 groups: a 4-way
+// bank conflict).
+__device__ __forceinline__ int bt_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+__device__ __forceinline__ int bt_off(int row, int chunk) { return row * ROW_BYTES + ((chunk ^ bt_swz(row)) << 4); }
+__device__ __forceinline__ int bt_chunk_at(int row, int pos) { return pos ^ bt_swz(row); }
+
+// Transpose read of a bt-swizzled tile: for lane l the 8 rows
 // 16*ks + 8*(l/32) + 0..7 at column 32*blk + l%32 (the A operand of a product
 // whose K dimension runs along the tile's rows).
 __device__ __forceinline__ bf16x8 tr_operand(const char *tb, int ks, int blk, int lane) {
   const int grp16 = lane >> 4, i16 = lane & 15;
   const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
   const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
-  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row, col >> 3) + 2 * (col & 7)));
-  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(tb + kq_off(row + 4, col >> 3) + 2 * (col & 7)));
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(tb + bt_off(row, col >> 3) + 2 * (col & 7)));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(tb + bt_off(row + 4, col >> 3) + 2 * (col & 7)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
