@@ -57,12 +57,13 @@ struct QTile {
 };
 
 // 32 codes starting at element 32*q of a key row -> 32 bf16 (4 x 16 bytes).
-// OFF16 (4-bit keys): code n widens to 16 + n, see below.
+// OFF16 (4-bit keys): code n widens to 16 + n, see below.  8-bit codes: the
+// second 16 bytes at `hi` (default codes + 16).
 template <int FMT, bool OFF16 = false>
-__device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4]) {
+__device__ __forceinline__ void widen32(const char *codes, uint4 (&out)[4], const char *hi = nullptr) {
   if constexpr (FMT == FMT_INT8) {
     const uint4 a = *reinterpret_cast<const uint4 *>(codes);
-    const uint4 b = *reinterpret_cast<const uint4 *>(codes + 16);
+    const uint4 b = *reinterpret_cast<const uint4 *>(hi ? hi : codes + 16);
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -210,7 +211,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
                                         rows_left * Q::CODE_ROW);
     const uint32_t soff = whole ? static_cast<uint32_t>(j0 * Q::CODE_ROW) : 0u;
     for (int sgm = wave; sgm < Q::SEGS; sgm += NW) {
-      const uint32_t off = static_cast<uint32_t>(sgm * 1024 + 16 * lane);
+      uint32_t off = static_cast<uint32_t>(sgm * 1024 + 16 * lane);
+      if constexpr (FMT == FMT_INT8) {  // 16-byte chunk c of code row r lands at c ^ ((r >> 1) & 1)
+        const int row = sgm * 8 + (lane >> 3);
+        off = static_cast<uint32_t>(row * Q::CODE_ROW + 16 * ((lane & 7) ^ ((row >> 1) & 1)));
+      }
       dma16(kr, off, soff, kdst + sgm * 1024);
       dma16(vr, off, soff, vdst + sgm * 1024);
     }
@@ -224,13 +229,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   // Thread tid widens the 32-element quarter tid % 4 of key row (tid % 256) / 4:
   // of K and V with 4 wavefronts, of K (wavefronts 0-3) or V (4-7) with 8.
   const int crow = (tid & 255) >> 2, cq = tid & 3;
+  // 8-bit code rows sit in the staging slot with 16-byte chunk c at position
+  // c ^ ((r >> 1) & 1): the 4 rows x 4 quarters that 16 lanes read at once
+  // then meet 16 distinct bank groups (in order, rows r and r + 2 met the
+  // same 8); 4-bit rows (64 bytes) already do.
   auto widen_rows = [&](int j, const char *cs, const void *nsrc, char *dst, bool is_v) {
     uint4 w[4];
     if (j < n_occ) {
+      const char *row = cs + crow * Q::CODE_ROW;
+      const char *lo = row + cq * (Q::CODE_ROW / 4), *hi = nullptr;
+      if constexpr (FMT == FMT_INT8) {
+        const int sw = (crow >> 1) & 1;
+        lo = row + 16 * ((2 * cq) ^ sw);
+        hi = row + 16 * ((2 * cq + 1) ^ sw);
+      }
       if (is_v) {
-        widen32<FMT>(cs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), w);
+        widen32<FMT>(lo, w, hi);
       } else {
-        widen32<FMT, true>(cs + crow * Q::CODE_ROW + cq * (Q::CODE_ROW / 4), w);
+        widen32<FMT, true>(lo, w, hi);
       }
     } else {
       const int t = j - n_occ;
