@@ -259,7 +259,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4 *>(dst + (is_v ? v_off(crow, 4 * cq + i) : kq_off(crow, 4 * cq + i))) = w[i];
+      *reinterpret_cast<uint4 *>(dst + (is_v ? vq_off(crow, 4 * cq + i) : kq_off(crow, 4 * cq + i))) = w[i];
   };
   auto widen_tile = [&](int tile, const char *kcs, const char *vcs, const uint16_t (*fcs)[64], char *kb,
                         char *vb, float (*fac)[64]) {
@@ -291,8 +291,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     const int ks = s >> 2, blk = s & 3;
     const int row = 16 * ks + 8 * (grp16 >> 1) + (i16 >> 2);
     const int col = 32 * blk + 16 * (grp16 & 1) + 4 * (i16 & 3);
-    const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(vb + v_off(row, col >> 3) + 2 * (col & 7)));
-    const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(vb + v_off(row + 4, col >> 3) + 2 * (col & 7)));
+    const bf16x4 lo = __builtin_bit_cast(bf16x4, lds_tr(vb + vq_off(row, col >> 3) + 2 * (col & 7)));
+    const bf16x4 hi = __builtin_bit_cast(bf16x4, lds_tr(vb + vq_off(row + 4, col >> 3) + 2 * (col & 7)));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       *reinterpret_cast<uint4 *>(kb + kq_off(crow, 4 * cq + i)) = kw[i];
-      *reinterpret_cast<uint4 *>(vb + v_off(crow, 4 * cq + i)) = vw[i];
+      *reinterpret_cast<uint4 *>(vb + vq_off(crow, 4 * cq + i)) = vw[i];
     }
   };
   auto store_fac = [&](float (*fac)[64], bool cached, const uint16_t *f) {
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
 #pragma unroll
     for (int dblk = 0; dblk < 8; ++dblk) {
       const int col = 16 * dblk + 4 * (n & 3);
-      const i16x4 va = lds_tr(vb + v_off(vrow, col >> 3) + 2 * (col & 7));
+      const i16x4 va = lds_tr(vb + vq_off(vrow, col >> 3) + 2 * (col & 7));
       o[dblk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dblk], 0, 0, 0);
     }
   };

@@ -56,18 +56,23 @@ __device__ __forceinline__ int kq_off(int row, int chunk) {
 }
 __device__ __forceinline__ int kq_chunk_at(int row, int pos) { return pos ^ (row & 15); }
 
-// V tile: chunk c of row r at r*256 + 16*(c ^ h(r)), h(r) = 5*(r & 3).  Over
-// 4 aligned rows (j = r & 3) a chunk 4b + i lands at 4(b ^ j) + (i ^ j), so
-// both the 128-row passes' transpose reads (4 aligned rows x 4 aligned
-// chunks per half-wave) and the 8/4-bit passes' stores of widened rows (4
-// aligned rows x chunks 4q + i, q = 0..3) meet 16 distinct 16-byte bank
-// groups.  4*(r & 3) served the reads only (the stores met 4 lanes per
-// bank).  The short-chunk passes' transpose reads (8 rows x 2 chunks) meet 2
-// lanes per bank; adding 2*((r >> 2) & 1) to h would spread those too, but
-// the 4-bit pass A then spilled registers and ran slower.
-__device__ __forceinline__ int v_swz(int row) { return 5 * (row & 3); }
-__device__ __forceinline__ int v_off(int row, int chunk) { return row * ROW_BYTES + ((chunk ^ v_swz(row)) << 4); }
-__device__ __forceinline__ int v_chunk_at(int row, int pos) { return pos ^ v_swz(row); }
+// V tile: chunk c of row r at r*256 + 16*(c ^ 4*(r & 3)) -- the 4 rows x 4
+// chunks a transpose read touches per half-wave land on 16 distinct groups.
+// (The short-chunk passes' transpose reads of 8 rows x 2 chunks meet 2 lanes
+// per bank: spreading those too cost the 128-row kernels registers.)
+__device__ __forceinline__ int v_off(int row, int chunk) {
+  return row * ROW_BYTES + ((chunk ^ ((row & 3) << 2)) << 4);
+}
+__device__ __forceinline__ int v_chunk_at(int row, int pos) { return pos ^ ((row & 3) << 2); }
+
+// V tile the 8/4-bit passes widen into: chunk c of row r at
+// r*256 + 16*(c ^ 5*(r & 3)).  Over 4 aligned rows (j = r & 3) a chunk
+// 4b + i lands at 4(b ^ j) + (i ^ j), so the same transpose reads and also
+// the stores of widened rows (4 aligned rows x chunks 4q + i, q = 0..3) meet
+// 16 distinct groups; with 4*(r & 3) those stores met 4 lanes per bank.
+__device__ __forceinline__ int vq_off(int row, int chunk) {
+  return row * ROW_BYTES + ((chunk ^ (5 * (row & 3))) << 4);
+}
 
 __device__ __forceinline__ bf16x8 lds16(const char *p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(p));
