@@ -135,7 +135,7 @@ def test_stream_policies_short_chunks_batch(policy):
     _run_stream(W.WORKLOADS[3].scaled(B=2, C=256, T=4, n_fill=64, n_evict=6), policy=policy)
 
 
-@pytest.mark.parametrize("fmt,T,policy", [("int8", 1, "h2o"), ("int4", 1, "h2o_orig"),
+@pytest.mark.parametrize("fmt,T,policy", [("int8", 1, "h2o"), ("int4", 1, "h2o_orig"), ("int8", 1, "h2o_norm"),
                                            ("int8", 4, "h2o_orig"), ("int4", 4, "h2o")])
 def test_stream_short_chunks_quant(fmt, T, policy):
     """One- and four-token chunks into 8/4-bit caches, B = 2: the pick
