@@ -1244,7 +1244,7 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
     e = launch_attn_combine(a, s);
     if (e != hipSuccess) return e;
   }
-  if (!a.wsum) return hipSuccess;
+  if (!a.wsum || (a.lg && a.defer_b)) return hipSuccess;
   if (a.lg) return launch_attn_b_logits(a, s);
   return launch_attn_b_native(a, s);
 }

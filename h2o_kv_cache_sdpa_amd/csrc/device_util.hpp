@@ -69,6 +69,45 @@ __device__ __forceinline__ float max_xor16(float x) {
   return __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
 }
 
+// v = min(v, u) for the 64-bit u made of the 32-bit halves lo, hi.
+__device__ __forceinline__ void min_u64_halves(uint64_t &v, uint32_t lo, uint32_t hi) {
+  const uint64_t u = (static_cast<uint64_t>(hi) << 32) | lo;
+  v = u < v ? u : v;
+}
+
+// One DPP step of wave_min_u64: both halves take the lane move CTRL.
+template <int CTRL>
+__device__ __forceinline__ void dpp_min_u64(uint64_t &v) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(v));
+  const int hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+  min_u64_halves(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xf, 0xf, false)),
+                 static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xf, 0xf, false)));
+}
+
+// Minimum of v over the wavefront, in every lane, without the LDS crossbar:
+// DPP within rows of 16 lanes (neighbours in a quad, then the mirrored
+// half-row and row, each pairing two groups that already agree), then
+// v_permlane16_swap and v_permlane32_swap across rows.  Both 32-bit halves
+// take the same lane moves, so every step compares whole 64-bit values.
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  dpp_min_u64<0xb1>(v);   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_min_u64<0x4e>(v);   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_min_u64<0x141>(v);  // row_half_mirror: quads 0 and 1 of each 8 lanes
+  dpp_min_u64<0x140>(v);  // row_mirror: the two 8-lane halves of each row
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  const auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  min_u64_halves(v, l16[0], h16[0]);
+  min_u64_halves(v, l16[1], h16[1]);
+  lo = static_cast<uint32_t>(v);
+  hi = static_cast<uint32_t>(v >> 32);
+  const auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  min_u64_halves(v, l32[0], h32[0]);
+  min_u64_halves(v, l32[1], h32[1]);
+  return v;
+}
+
 // Key tiles t_lo .. t_lo + count - 1 of split `split` of `nsplit` over
 // `ntiles` tiles: the first ntiles % nsplit splits take one tile more, so no
 // split holds more than one tile above another (count 0: an empty split).

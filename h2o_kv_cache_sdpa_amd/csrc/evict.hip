@@ -52,8 +52,9 @@ struct SelShared {
   uint32_t hist[256];
   uint32_t sel, k;
   uint32_t a[16], b[16];
-  uint64_t m64[32];  // two banks of up to 16 wavefronts (alternate rounds)
-  uint32_t ps[SMALL_T];
+  uint64_t m64[16];                 // one entry per wavefront (up to 16)
+  uint64_t lst[16 * SMALL_T];       // each wavefront's SMALL_T smallest
+  uint64_t win[SMALL_T];            // the block's SMALL_T smallest, ascending
 };
 
 // Block-wide exclusive scan of two counters; returns the prefixes for this thread.
@@ -204,20 +205,49 @@ __device__ __forceinline__ void select_smallest(uint32_t (&key)[ITEMS], int nval
 template <int NTH>
 __device__ __forceinline__ uint64_t block_min_u64(uint64_t v, uint64_t *sh64) {
   constexpr int NW = NTH / 64;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    const uint64_t u = static_cast<uint64_t>(__shfl_xor(static_cast<unsigned long long>(v), o));
-    v = u < v ? u : v;
-  }
+  v = wave_min_u64(v);
   if constexpr (NW == 1) {
     return v;
   } else {
-    if ((threadIdx.x & 63) == 0) sh64[threadIdx.x >> 6] = v;
+    const int lane = threadIdx.x & 63;
+    if (lane == 0) sh64[threadIdx.x >> 6] = v;
     __syncthreads();
-    v = sh64[0];
-    for (int w = 1; w < NW; ++w) v = sh64[w] < v ? sh64[w] : v;
-    return v;
+    return wave_min_u64(lane < NW ? sh64[lane] : ~0ull);
   }
+}
+
+// The T <= SMALL_T smallest of the block's (key << 32 | slot) values u[k]
+// (~0ull: no value), ascending, in sh.win[0 .. T) on return (every thread
+// calls; the slice or candidate list holds at least T values).  Each
+// wavefront lists its own T smallest (T rounds of the wavefront minimum, no
+// barrier between them); wavefront 0 then takes the T smallest of the lists.
+// The values are distinct, so a round's minimum leaves exactly one entry.
+template <int NTH, int ITEMS>
+__device__ __forceinline__ void block_smallest(uint64_t (&u)[ITEMS], int T, SelShared &sh) {
+  constexpr int NW = NTH / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = 0; r < T; ++r) {
+    uint64_t m = u[0];
+#pragma unroll
+    for (int k = 1; k < ITEMS; ++k) m = u[k] < m ? u[k] : m;
+    m = wave_min_u64(m);
+    if (lane == 0) (NW == 1 ? sh.win[r] : sh.lst[wave * T + r]) = m;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) u[k] = u[k] == m ? ~0ull : u[k];
+  }
+  __syncthreads();
+  if (NW > 1 && wave == 0) {
+    // NW * T <= 128 listed values: two per lane
+    uint64_t c0 = lane < NW * T ? sh.lst[lane] : ~0ull;
+    uint64_t c1 = lane + 64 < NW * T ? sh.lst[lane + 64] : ~0ull;
+    for (int r = 0; r < T; ++r) {
+      const uint64_t m = wave_min_u64(c0 < c1 ? c0 : c1);
+      if (lane == 0) sh.win[r] = m;
+      c0 = c0 == m ? ~0ull : c0;
+      c1 = c1 == m ? ~0ull : c1;
+    }
+  }
+  if constexpr (NW > 1) __syncthreads();
 }
 
 // Position in the selection (-1: not taken) of a thread's next valid key, in
@@ -409,6 +439,63 @@ __global__ __launch_bounds__(NT) void evict_kernel(EvictArgs a) {
 // smallest (every slot of a slice that holds at most T) as (key, slot) pairs
 // in slot order at cand[(head * nslice + slice) * T ..].
 // ---------------------------------------------------------------------------
+// The slice's candidates from its ranking keys (ITEMS per thread, slots
+// base .. base + ITEMS - 1, nvalid of them real), written to dst.
+template <int NTH, int ITEMS>
+__device__ __forceinline__ void slice_candidates(const uint32_t (&key)[ITEMS], int base, int nvalid, int s0,
+                                                 int len, int T, uint2 *dst, SelShared &sh) {
+  const int tid = threadIdx.x;
+  if (T == 1) {  // the slice's smallest (key, slot)
+    uint64_t v = ~0ull;
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k) {
+      const uint64_t u = (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(base + k);
+      if (k < nvalid && u < v) v = u;
+    }
+    v = block_min_u64<NTH>(v, sh.m64);
+    if (tid == 0) dst[0] = make_uint2(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v));
+    return;
+  }
+  if (len <= T) {  // the whole slice (only the last one can be this short)
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      if (k < nvalid) dst[base + k - s0] = make_uint2(key[k], static_cast<uint32_t>(base + k));
+    return;
+  }
+  if (T <= SMALL_T) {
+    // the slice's T smallest (key, slot), listed in increasing order (the
+    // pick compares (key, slot) pairs, so list order carries no tie-break)
+    uint64_t u[ITEMS];
+#pragma unroll
+    for (int k = 0; k < ITEMS; ++k)
+      u[k] = k < nvalid ? (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(base + k) : ~0ull;
+    block_smallest<NTH, ITEMS>(u, T, sh);
+    if (tid < T) dst[tid] = make_uint2(static_cast<uint32_t>(sh.win[tid] >> 32), static_cast<uint32_t>(sh.win[tid]));
+    return;
+  }
+  uint32_t rel[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) rel[k] = key[k];
+  uint32_t theta, take_eq;
+  select_smallest<NTH, ITEMS>(rel, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
+  uint32_t nl = 0, ne = 0;
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    if (k < nvalid) {
+      nl += rel[k] < theta;
+      ne += rel[k] == theta;
+    }
+  }
+  uint32_t less_before, eq_before;
+  block_scan2<NTH>(nl, ne, less_before, eq_before, sh);
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) {
+    if (k >= nvalid) continue;
+    const int out = rank_in_selection(rel[k], theta, take_eq, less_before, eq_before);
+    if (out >= 0) dst[out] = make_uint2(key[k], static_cast<uint32_t>(base + k));
+  }
+}
+
 template <int POL>
 __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
   constexpr int ITEMS = SLICE / NT_C;
@@ -422,65 +509,212 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
   const int nvalid = s0 + len - base;
   float f[ITEMS];
   update_scores<POL, ITEMS>(a, head, base, 1, s0 + len, f);
-  uint32_t key[ITEMS], rel[ITEMS];
+  uint32_t key[ITEMS];
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) rel[k] = key[k] = ordered_key(f[k]);
-  uint2 *dst = cand + (static_cast<size_t>(head) * nslice + slice) * T;
+  for (int k = 0; k < ITEMS; ++k) key[k] = ordered_key(f[k]);
+  slice_candidates<NT_C, ITEMS>(key, base, nvalid, s0, len, T,
+                               cand + (static_cast<size_t>(head) * nslice + slice) * T, sh);
+}
 
-  if (T == 1) {  // the slice's smallest (key, slot)
-    uint64_t v = ~0ull;
+// Pass 1 for short chunks whose pass A stored its logits (a.lg, at most
+// LOGIT_ROWS_MAX rows per group): the workgroup first forms its slice's
+// summed weights from the logits -- the sum attn_b_logits forms, in the same
+// order -- and writes them, so the step needs no separate weight-sum launch;
+// then it updates, ranks and selects as evict_cand does.  One slot per thread
+// (NT_LG threads), so the sums keep the parallelism of a kernel of their own.
+// Workgroups with slice index x also merge output rows x, x + nslice, ...
+// of their groups from the key splits (and write their normalisers), and
+// slice 0 sums the chunk's own keys.
+constexpr int NT_LG = SLICE;
+template <int POL>
+__global__ __launch_bounds__(NT_LG) void evict_cand_lg(EvictArgs e, AttnArgs a, float xs, uint2 *cand) {
+  constexpr int ITEMS = 1;
+  constexpr int HD = 128;  // head dimension of the short-chunk logit path
+  __shared__ SelShared sh;
+  __shared__ float Ls[LOGIT_ROWS_MAX], Ms[LOGIT_ROWS_MAX], Ws[LOGIT_ROWS_MAX];
+  __shared__ float4 red_o[8][32];
+  const int tid = threadIdx.x;
+  const int C = e.C, T = e.T;
+  const int slice = blockIdx.x, head = blockIdx.y, nslice = gridDim.x;
+  const int s0 = slice * SLICE;
+  const int len = min(SLICE, C - s0);
+  const int base = s0 + tid;
+  const int nvalid = s0 + len - base;
+  const int R = a.qg * a.T;
+  const int n_keys = C + T;  // evicting: every slot is occupied
+  const int nb = (POL == H2O_POLICY_ORIG) ? e.B : 1;
+  const int32_t pos_end = static_cast<int32_t>(e.pos + T);
+  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+  const bool merger = a.nsplit > 1 && tid < 256;  // 8 groups of 32 lanes merge output rows
+  const int grp8 = (tid >> 5) & 7, c4 = tid & 31;
+  float rank[ITEMS];
+  for (int bb = 0; bb < nb; ++bb) {
+    const int grp = (POL == H2O_POLICY_ORIG) ? bb * e.Hkv + head : head;
+    const int g = grp % a.Hkv, b = grp / a.Hkv;
+    auto row_index = [&](int r) {
+      return (static_cast<size_t>(b) * a.Hq + g * a.qg + r % a.qg) * a.T + r / a.qg;
+    };
+    // Every load of the group is issued first (none depends on another):
+    // the split maxima / sums, the first output row's split partials, the
+    // slice's logits, scores and token positions.
+    // normalisers: 16 lanes per row, lane s takes splits s, s + 16, s + 32, s + 48
+    const int rn = tid >> 4, sl = tid & 15;
+    const size_t li_n = rn < R ? row_index(rn) : 0;
+    float2 ml[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int sp = sl + 16 * k;
+      ml[k] = (a.nsplit > 1 && rn < R && sp < a.nsplit)
+                  ? *reinterpret_cast<const float2 *>(a.part_ml + 2 * (sp * rows + li_n))
+                  : make_float2(-INFINITY, 0.f);
+    }
+    const float lse_own = (a.nsplit == 1 && tid < R) ? a.lse2[row_index(tid)] : 0.f;
+    // output row r: group k takes splits k, k + 8, ... (at most 64 splits)
+    float ms[8];
+    float4 po[8];
+    auto load_row = [&](int r) {
+      const size_t li = row_index(r);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int sp = grp8 + 8 * k;
+        ms[k] = -INFINITY;
+        po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (merger && sp < a.nsplit) {
+          const size_t pr = sp * rows + li;
+          ms[k] = a.part_ml[2 * pr];
+          po[k] = *reinterpret_cast<const float4 *>(a.part + pr * HD + 4 * c4);
+        }
+      }
+    };
+    // (h2o_orig, which loops over the batch rows, loads it later: registers)
+    constexpr bool kEarlyRow = POL != H2O_POLICY_ORIG;
+    if (kEarlyRow && slice < R) load_row(slice);
+    const float *lgp = a.lg + static_cast<size_t>(grp) * R * a.lg_stride;
+    float x[LOGIT_ROWS_MAX][ITEMS];
+#pragma unroll
+    for (int r = 0; r < LOGIT_ROWS_MAX; ++r)
+#pragma unroll
+      for (int k = 0; k < ITEMS; ++k)
+        x[r][k] = (r < R && k < nvalid) ? lgp[static_cast<size_t>(r) * a.lg_stride + base + k] : 0.f;
+    float *ph = e.scores + static_cast<size_t>(grp) * C;
+    const int32_t *tp = e.token_pos ? e.token_pos + static_cast<size_t>(grp) * C : nullptr;
+    float f[ITEMS];
+    int32_t t0[ITEMS] = {};
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k) {
-      const uint64_t u = (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(base + k);
-      if (k < nvalid && u < v) v = u;
+      f[k] = k < nvalid ? ph[base + k] : 0.f;
+      if constexpr (POL == H2O_POLICY_NORM) t0[k] = k < nvalid ? tp[base + k] : 0;
     }
-    v = block_min_u64<NT_C>(v, sh.m64);
-    if (tid == 0) dst[0] = make_uint2(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v));
-    return;
-  }
-  if (len <= T) {  // the whole slice (only the last one can be this short)
+
+    // row normalisers of the group: merged from the key splits, or pass A's own
+    if (a.nsplit > 1) {
+      float m = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
 #pragma unroll
-    for (int k = 0; k < ITEMS; ++k)
-      if (k < nvalid) dst[base + k - s0] = make_uint2(key[k], static_cast<uint32_t>(base + k));
-    return;
-  }
-  if (T <= SMALL_T) {
-    // T rounds of the slice's smallest (key, slot), listed in that order (the
-    // pick compares (key, slot) pairs, so list order carries no tie-break).
-    // Consecutive rounds use alternate LDS slots of the block minimum.
-    uint64_t u[ITEMS];
+      for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      float l = 0.f;
 #pragma unroll
-    for (int k = 0; k < ITEMS; ++k)
-      u[k] = k < nvalid ? (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(base + k) : ~0ull;
-    for (int r = 0; r < T; ++r) {
-      uint64_t m = u[0];
+      for (int k = 0; k < 4; ++k)
+        if (ml[k].x != -INFINITY) l = fmaf(ml[k].y, __builtin_amdgcn_exp2f(ml[k].x - m), l);
 #pragma unroll
-      for (int k = 1; k < ITEMS; ++k) m = u[k] < m ? u[k] : m;
-      m = block_min_u64<NT_C>(m, sh.m64 + 16 * (r & 1));
-      if (tid == 0) dst[r] = make_uint2(static_cast<uint32_t>(m >> 32), static_cast<uint32_t>(m));
-#pragma unroll
-      for (int k = 0; k < ITEMS; ++k) u[k] = u[k] == m ? ~0ull : u[k];
+      for (int o = 8; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+      if (rn < R && sl == 0) {
+        Ms[rn] = m;
+        Ws[rn] = l;
+        Ls[rn] = m + log2f(l);
+      }
+    } else if (tid < R) {
+      Ls[tid] = lse_own;
     }
-    return;
-  }
-  uint32_t theta, take_eq;
-  select_smallest<NT_C, ITEMS>(rel, nvalid, static_cast<uint32_t>(T), sh, theta, take_eq);
-  uint32_t nl = 0, ne = 0;
+    __syncthreads();
+    // output rows slice, slice + nslice, ...: sum_s 2^(m_s - M) O_s / l,
+    // the 8 groups added in order
+    for (int r = slice; a.nsplit > 1 && r < R; r += nslice) {
+      if (!kEarlyRow || r != slice) load_row(r);
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    if (k < nvalid) {
-      nl += rel[k] < theta;
-      ne += rel[k] == theta;
+      for (int k = 0; k < 8; ++k) {
+        if (ms[k] == -INFINITY) continue;
+        const float w = __builtin_amdgcn_exp2f(ms[k] - Ms[r]);
+        acc.x = fmaf(po[k].x, w, acc.x);
+        acc.y = fmaf(po[k].y, w, acc.y);
+        acc.z = fmaf(po[k].z, w, acc.z);
+        acc.w = fmaf(po[k].w, w, acc.w);
+      }
+      if (merger) red_o[grp8][c4] = acc;
+      __syncthreads();
+      if (tid < 32) {
+        float4 t = red_o[0][c4];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+          const float4 u = red_o[k][c4];
+          t.x += u.x;
+          t.y += u.y;
+          t.z += u.z;
+          t.w += u.w;
+        }
+        const size_t li = row_index(r);
+        const float inv = 1.f / Ws[r];
+        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(t.x * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(t.y * inv)) << 16);
+        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(t.z * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(t.w * inv)) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + li * HD + 4 * c4) = make_uint2(lo, hi);
+        if (c4 == 0) {
+          a.lse2[li] = Ls[r];
+          if (a.lse_nat) a.lse_nat[li] = Ls[r] * 0.69314718055994530942f;
+        }
+      }
+      __syncthreads();  // red_o is reused by the next row
     }
-  }
-  uint32_t less_before, eq_before;
-  block_scan2<NT_C>(nl, ne, less_before, eq_before, sh);
+    // summed weights: Kahan-compensated over the rows in order; every row
+    // sees the cache slots, row r sees chunk key t iff t * q_g <= r - r % q_g
+    float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
+    if (slice == 0 && tid < T) {
+      float acc = 0.f, comp = 0.f;
+      for (int r = 0; r < R; ++r) {
+        if (tid * a.qg <= r - r % a.qg) {
+          const float p =
+              __builtin_amdgcn_exp2f(fmaf(lgp[static_cast<size_t>(r) * a.lg_stride + C + tid], xs, -Ls[r]));
+          const float y = p - comp;
+          const float s2 = acc + y;
+          comp = (s2 - acc) - y;
+          acc = s2;
+        }
+      }
+      w[C + tid] = acc;
+    }
 #pragma unroll
-  for (int k = 0; k < ITEMS; ++k) {
-    if (k >= nvalid) continue;
-    const int out = rank_in_selection(rel[k], theta, take_eq, less_before, eq_before);
-    if (out >= 0) dst[out] = make_uint2(key[k], static_cast<uint32_t>(base + k));
+    for (int k = 0; k < ITEMS; ++k) {
+      float acc = 0.f, comp = 0.f;
+#pragma unroll
+      for (int r = 0; r < LOGIT_ROWS_MAX; ++r) {
+        if (r < R) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(x[r][k], xs, -Ls[r]));
+          const float y = p - comp;
+          const float s2 = acc + y;
+          comp = (s2 - acc) - y;
+          acc = s2;
+        }
+      }
+      if (k >= nvalid) continue;
+      w[base + k] = acc;
+      f[k] += acc;
+      ph[base + k] = f[k];
+      if constexpr (POL == H2O_POLICY_ORIG) {
+        rank[k] = (bb == 0) ? f[k] : rank[k] + f[k];
+      } else if constexpr (POL == H2O_POLICY_NORM) {
+        rank[k] = f[k] / static_cast<float>(pos_end - t0[k]);
+      } else {
+        rank[k] = f[k];
+      }
+    }
+    __syncthreads();  // Ls / Ms / Ws are rewritten for the next batch row
   }
+  uint32_t key[ITEMS];
+#pragma unroll
+  for (int k = 0; k < ITEMS; ++k) key[k] = k < nvalid ? ordered_key(rank[k]) : 0xffffffffu;
+  slice_candidates<NT_LG, ITEMS>(key, base, nvalid, s0, len, T,
+                                cand + (static_cast<size_t>(head) * nslice + slice) * T, sh);
 }
 
 // Short chunks, pass 2: the T smallest candidates of each head.  The lists
@@ -561,26 +795,17 @@ __global__ __launch_bounds__(NTH) void evict_pick(EvictArgs a, const uint2 *cand
     return;
   }
   if (T <= SMALL_T) {
-    // T rounds of the smallest (key, slot); then each winner's place in slot
-    // order is the number of winners with a lower slot.
+    // the T smallest (key, slot); each winner's place in slot order is the
+    // number of winners with a lower slot
     uint64_t u[ITEMS];
 #pragma unroll
     for (int k = 0; k < ITEMS; ++k)
       u[k] = k < nvalid ? (static_cast<uint64_t>(key[k]) << 32) | static_cast<uint32_t>(slot[k]) : ~0ull;
-    for (int r = 0; r < T; ++r) {
-      uint64_t m = u[0];
-#pragma unroll
-      for (int k = 1; k < ITEMS; ++k) m = u[k] < m ? u[k] : m;
-      m = block_min_u64<NTH>(m, sh.m64 + 16 * (r & 1));
-      if (tid == 0) sh.ps[r] = static_cast<uint32_t>(m);
-#pragma unroll
-      for (int k = 0; k < ITEMS; ++k) u[k] = u[k] == m ? ~0ull : u[k];
-    }
-    __syncthreads();
+    block_smallest<NTH, ITEMS>(u, T, sh);
     if (tid < T) {
-      const uint32_t j = sh.ps[tid];
+      const uint32_t j = static_cast<uint32_t>(sh.win[tid]);
       int out = 0;
-      for (int r = 0; r < T; ++r) out += sh.ps[r] < j;
+      for (int r = 0; r < T; ++r) out += static_cast<uint32_t>(sh.win[r]) < j;
       take_slot<POL>(a, head, static_cast<int>(j), out, a.wsum[static_cast<size_t>(head) * n_keys + C + out]);
       if constexpr (KV) chosen[out] = static_cast<int>(j);
     }
@@ -672,16 +897,23 @@ void launch_pick(const EvictArgs &a, const uint2 *cand, int ncand, int nreal, co
   }
 }
 
-// kv: when set, the pick also writes the chunk's K/V rows (native cache).
+// kv: when set, the pick also writes the chunk's K/V rows.  lg: when set,
+// the candidate pass also forms the summed weights from the stored logits.
 template <int POL>
-hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, const KvWriteArgs *kv, hipStream_t s) {
+hipError_t launch_two_pass(const EvictArgs &a, uint2 *cand, const KvWriteArgs *kv, const AttnArgs *lg,
+                           hipStream_t s) {
   const int heads = (POL == H2O_POLICY_ORIG) ? a.Hkv : a.groups;
   const int ns = n_slices(a.C);
   const int ncand = ns * a.T;
   const int last = a.C - (ns - 1) * SLICE;  // slots of the last slice
   const int nreal = (ns - 1) * a.T + (last < a.T ? last : a.T);
   KernelTimer timer(H2O_K_EVICT, s);
-  hipLaunchKernelGGL(evict_cand<POL>, dim3(ns, heads), dim3(NT_C), 0, s, a, cand);
+  if (lg) {
+    const float xs = lg->cache_fmt == FMT_NATIVE ? lg->sl2 : 1.f;
+    hipLaunchKernelGGL(evict_cand_lg<POL>, dim3(ns, heads), dim3(NT_LG), 0, s, a, *lg, xs, cand);
+  } else {
+    hipLaunchKernelGGL(evict_cand<POL>, dim3(ns, heads), dim3(NT_C), 0, s, a, cand);
+  }
   if (kv) {
     launch_pick<POL, true>(a, cand, ncand, nreal, *kv, heads, s);
   } else {
@@ -697,12 +929,21 @@ size_t evict_workspace_bytes(int groups, int C, int T) {
   return sizeof(uint2) * static_cast<size_t>(groups) * n_slices(C) * T;
 }
 
-hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s, const KvWriteArgs *kv,
-                        bool *kv_done) {
-  if (kv_done) *kv_done = false;
+bool evict_two_pass(const EvictArgs &a, size_t ws_bytes) {
   const size_t need = evict_workspace_bytes(a.groups, a.C, a.T);
-  if (a.n_occ == a.C && need && ws && ws_bytes >= need) {
+  return a.n_occ == a.C && need && ws_bytes >= need;
+}
+
+hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s, const KvWriteArgs *kv,
+                        bool *kv_done, const AttnArgs *lg) {
+  if (kv_done) *kv_done = false;
+  if (ws && evict_two_pass(a, ws_bytes)) {
     uint2 *cand = static_cast<uint2 *>(ws);
+    // stored logits: short chunks (at most LOGIT_ROWS_MAX query rows per
+    // group), bf16 queries, D = 128, buffers matching the selection's
+    if (lg && (!lg->lg || !lg->wsum || lg->D != 128 || lg->qg * lg->T > LOGIT_ROWS_MAX ||
+               lg->B * lg->Hkv != a.groups || lg->T != a.T || lg->n_occ != a.n_occ || lg->nsplit > 64))
+      return hipErrorInvalidValue;
     // fuse the K/V write into the pick (evict-only bookkeeping): native
     // caches up to KV_FUSE_T tokens; 8/4-bit caches for one token, where the
     // two quantised rows per head cost less than a launch (from four tokens
@@ -712,10 +953,11 @@ hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream
                        (kv->dtype == DT_BF16 && a.T == 1 && kv->D <= 128));
     const KvWriteArgs *kvp = fuse ? kv : nullptr;
     if (fuse) *kv_done = true;
-    if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, kvp, s);
-    if (a.policy == H2O_POLICY_ORIG) return launch_two_pass<H2O_POLICY_ORIG>(a, cand, kvp, s);
-    return launch_two_pass<H2O_POLICY_H2O>(a, cand, kvp, s);
+    if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, kvp, lg, s);
+    if (a.policy == H2O_POLICY_ORIG) return launch_two_pass<H2O_POLICY_ORIG>(a, cand, kvp, lg, s);
+    return launch_two_pass<H2O_POLICY_H2O>(a, cand, kvp, lg, s);
   }
+  if (lg) return hipErrorInvalidValue;  // only the candidate pass sums stored logits
   const int per = (a.C + NT - 1) / NT;
   if (per <= 1) return launch_items<1>(a, s);
   if (per <= 2) return launch_items<2>(a, s);

@@ -377,14 +377,20 @@ int chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos, 
   if (st != H2O_OK) return st;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  st = launch_sdpa(attn_args(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws), s);
-  if (st != H2O_OK) return st;
   // the rest of the workspace, if any, holds the selection's candidate lists
   const size_t used = need;
+  const h2o::EvictArgs ea = evict_args(d, cache, n_occ, pos, w, slot_log);
+  h2o::AttnArgs aa = attn_args(d, cache, n_occ, q, k_new, v_new, out, w, nullptr, ws);
+  // short chunks whose logits pass A stores: when the selection takes the
+  // candidate shape, its first kernel forms the summed weights (and merges
+  // the key splits) instead of a launch of its own
+  aa.defer_b = aa.lg && h2o::evict_two_pass(ea, ws_bytes - used);
+  st = launch_sdpa(aa, s);
+  if (st != H2O_OK) return st;
   const h2o::KvWriteArgs kv = write_args(d, cache, k_new, v_new, slot_log);
   bool kv_done = false;
-  st = from_hip(h2o::launch_evict(evict_args(d, cache, n_occ, pos, w, slot_log),
-                                  static_cast<char *>(ws) + used, ws_bytes - used, s, &kv, &kv_done));
+  st = from_hip(h2o::launch_evict(ea, static_cast<char *>(ws) + used, ws_bytes - used, s, &kv, &kv_done,
+                                  aa.defer_b ? &aa : nullptr));
   if (st != H2O_OK || kv_done) return st;
   return from_hip(h2o::launch_kv_write(kv, s));
 }

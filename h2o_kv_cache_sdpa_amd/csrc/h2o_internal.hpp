@@ -46,6 +46,10 @@ struct AttnArgs {
   // instead of a second pass over K.  Null otherwise.
   float *lg;
   int lg_stride;
+  // With lg set, defer_b leaves the summed weights (and the merge of the key
+  // splits) to the selection's first kernel, which forms them from the
+  // stored logits (launch_evict with these arguments).
+  int defer_b;
   int B, Hq, Hkv, D, C, T, qg, n_occ;
   int dtype, cache_fmt;
   float sl2;  // softmax scale * log2(e)
@@ -122,9 +126,15 @@ size_t attn_split_floats(int B, int Hq, int D, int T, int nsplit);
 // kv (optional): the chunk's K/V write.  When the selection can do it in the
 // same launch (two-pass shape, native cache, short chunk) it does and sets
 // *kv_done; otherwise the caller launches launch_kv_write afterwards.
+// lg (optional): attention arguments whose stored logits the selection sums
+// itself (a.defer_b was set for pass A); requires the two-pass shape
+// (evict_two_pass), otherwise hipErrorInvalidValue.
 hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream_t s,
-                        const KvWriteArgs *kv = nullptr, bool *kv_done = nullptr);
+                        const KvWriteArgs *kv = nullptr, bool *kv_done = nullptr,
+                        const AttnArgs *lg = nullptr);
 size_t evict_workspace_bytes(int groups, int C, int T);
+// True when launch_evict takes the two-pass shape (slice candidates + pick).
+bool evict_two_pass(const EvictArgs &a, size_t ws_bytes);
 hipError_t launch_kv_write(const KvWriteArgs &a, hipStream_t s);
 hipError_t launch_dequant(const KvWriteArgs &a, int n_slots, float *kout, float *vout, hipStream_t s);
 

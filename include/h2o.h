@@ -188,10 +188,11 @@ int kv_dequant_unpack(const h2o_dims *d, const h2o_cache *cache, int32_t n_slots
  * by its keys and values; §3.1.1: the H2O score of a slot is its cumulative
  * summed attention weight; §3.2: the decisions go to a replay log):
  * h2o_sdpa_scoresum, then h2o_evict_topk, then kv_scatter (NATIVE) or
- * kv_quant_pack (INT8/INT4), enqueued on `stream` (for short chunks the
- * selection's last kernel writes the rows itself, with the same result).
- * wsum may be NULL (the
- * sums then live in the workspace).  After the call the caller's occupancy
+ * kv_quant_pack (INT8/INT4), enqueued on `stream`.  For short chunks the
+ * kernels are merged with the same results: the selection's first kernel
+ * forms the summed weights from the logits the attention stored, and its
+ * last kernel writes the rows.  wsum may be NULL (the sums then live in the
+ * workspace).  After the call the caller's occupancy
  * is min(n_occ + T, C) and its position pos + T. */
 int h2o_chunk_step(const h2o_dims *d, h2o_cache *cache, int32_t n_occ, int64_t pos,
                    const void *q, const void *k_new, const void *v_new,
