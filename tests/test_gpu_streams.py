@@ -146,6 +146,16 @@ def test_stream_short_chunks_quant(fmt, T, policy):
     _run_stream(base.scaled(B=2, C=C, T=T, n_fill=C // T, n_evict=8, cache_fmt=fmt), policy=policy)
 
 
+@pytest.mark.parametrize("T,policy", [(1, "h2o"), (4, "h2o"), (4, "h2o_orig"), (1, "h2o_norm")])
+def test_stream_short_chunks_split_merge(T, policy):
+    """Evicting one- and four-token steps on a prefilled 2048-slot cache, B = 2:
+    pass A splits the keys (8 splits), and the selection's two slices each
+    merge several output rows of every group from the split partials while
+    summing the stored logits (both batch rows of a head under h2o_orig)."""
+    w = W.WORKLOADS[2].scaled(B=2, C=2048, T=T, n_fill=0, n_evict=4, name=f"split_merge_t{T}")
+    _run_stream(w, policy=policy)
+
+
 @pytest.mark.parametrize("policy", ["h2o_norm", "h2o_orig"])
 def test_stream_policies_int4_batch(policy):
     _run_stream(W.WORKLOADS[5].scaled(C=512, T=32, n_fill=16, n_evict=8), policy=policy)
