@@ -35,6 +35,7 @@
 
 #include "device_util.hpp"
 #include "h2o_internal.hpp"
+#include "split_merge.hpp"
 #include "tile_util.hpp"
 
 namespace h2o {
@@ -690,90 +691,32 @@ __global__ __launch_bounds__(256) void attn_b_logits(AttnArgs a, float xs) {
   const int grp = blockIdx.y, g = grp % a.Hkv, b = grp / a.Hkv;
   const int R = a.qg * a.T;
   const int tid = threadIdx.x;
+  const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
   auto row_index = [&](int r) {
     return (static_cast<size_t>(b) * a.Hq + g * a.qg + r % a.qg) * a.T + r / a.qg;
   };
-  if (a.nsplit > 1) {
-    // 16 lanes per row, lane s takes splits s, s + 16, s + 32, s + 48 (nsplit
-    // <= 64), all loads issued before use; max, then the rescaled sum
-    const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
+  if (a.nsplit > 1) {  // 16 lanes per row, all loads issued before use
     const int r = tid >> 4, sl = tid & 15;
     float2 ml[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int sp = sl + 16 * k;
-      ml[k] = (r < R && sp < a.nsplit)
-                  ? *reinterpret_cast<const float2 *>(a.part_ml + 2 * (sp * rows + row_index(r)))
-                  : make_float2(-INFINITY, 0.f);
-    }
-    float m = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    float l = 0.f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (ml[k].x != -INFINITY) l = fmaf(ml[k].y, __builtin_amdgcn_exp2f(ml[k].x - m), l);
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    load_split_ml(a, rows, r < R ? row_index(r) : 0, sl, r < R, ml);
+    float M, W;
+    reduce_split_ml(ml, M, W);
     if (r < R && sl == 0) {
-      Ms[r] = m;
-      Ws[r] = l;
-      Ls[r] = m + log2f(l);
+      Ms[r] = M;
+      Ws[r] = W;
+      Ls[r] = M + log2f(W);
     }
   } else if (tid < R) {
     Ls[tid] = a.lse2[row_index(tid)];
   }
   __syncthreads();
-  if (a.nsplit > 1 && static_cast<int>(blockIdx.x) < R) {
-    // output row x: sum_s 2^(m_s - M) O_s / l; 8 groups of 32 lanes (4
-    // components each), group k takes splits k, k + 8, ... (at most 8 each),
-    // loads first, groups added in order
-    const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
-    const int r = blockIdx.x, grp8 = tid >> 5, c4 = tid & 31;
+  if (a.nsplit > 1 && static_cast<int>(blockIdx.x) < R) {  // output row x
+    const int r = blockIdx.x, q = tid >> 5, c4 = tid & 31;
     const size_t li = row_index(r);
     float ms[8];
     float4 po[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int sp = grp8 + 8 * k;
-      ms[k] = -INFINITY;
-      po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (sp < a.nsplit) {
-        const size_t pr = sp * rows + li;
-        ms[k] = a.part_ml[2 * pr];
-        po[k] = *reinterpret_cast<const float4 *>(a.part + pr * D + 4 * c4);
-      }
-    }
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (ms[k] == -INFINITY) continue;
-      const float w = __builtin_amdgcn_exp2f(ms[k] - Ms[r]);
-      acc.x = fmaf(po[k].x, w, acc.x);
-      acc.y = fmaf(po[k].y, w, acc.y);
-      acc.z = fmaf(po[k].z, w, acc.z);
-      acc.w = fmaf(po[k].w, w, acc.w);
-    }
-    red_o[grp8][c4] = acc;
-    __syncthreads();
-    if (grp8 == 0) {
-      float4 t = red_o[0][c4];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) {
-        const float4 u = red_o[k][c4];
-        t.x += u.x;
-        t.y += u.y;
-        t.z += u.z;
-        t.w += u.w;
-      }
-      const float inv = 1.f / Ws[r];
-      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + li * D + 4 * c4) =
-          make_uint2(pack_bf16_rne(t.x * inv, t.y * inv), pack_bf16_rne(t.z * inv, t.w * inv));
-      if (c4 == 0) {
-        a.lse2[li] = Ls[r];
-        if (a.lse_nat) a.lse_nat[li] = Ls[r] * 0.69314718055994530942f;
-      }
-    }
+    load_split_row(a, rows, li, q, c4, true, ms, po);
+    merge_split_row(a, li, Ms[r], Ws[r], Ls[r], q, c4, true, ms, po, red_o);
   }
   const int n_keys = a.n_occ + a.T;
   const int j = blockIdx.x * 256 + threadIdx.x;
@@ -783,18 +726,8 @@ __global__ __launch_bounds__(256) void attn_b_logits(AttnArgs a, float xs) {
   float x[LOGIT_ROWS_MAX];
 #pragma unroll
   for (int r = 0; r < LOGIT_ROWS_MAX; ++r) x[r] = r < R ? src[static_cast<size_t>(r) * a.lg_stride] : 0.f;
-  float acc = 0.f, comp = 0.f;
-#pragma unroll
-  for (int r = 0; r < LOGIT_ROWS_MAX; ++r) {
-    if (r < R && t * a.qg <= r - r % a.qg) {  // t <= r / qg
-      const float p = __builtin_amdgcn_exp2f(fmaf(x[r], xs, -Ls[r]));
-      const float y = p - comp;
-      const float s2 = acc + y;
-      comp = (s2 - acc) - y;
-      acc = s2;
-    }
-  }
-  a.wsum[static_cast<size_t>(grp) * n_keys + j] = acc;
+  a.wsum[static_cast<size_t>(grp) * n_keys + j] = key_weight_sum(
+      R, [&](int r) { return x[r]; }, [&](int r) { return t * a.qg <= r - r % a.qg; }, xs, Ls);  // t <= r / qg
 }
 
 // ---------------------------------------------------------------------------

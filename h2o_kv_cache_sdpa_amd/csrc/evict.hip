@@ -31,6 +31,7 @@
 #include "device_util.hpp"
 #include "h2o_internal.hpp"
 #include "kv_quant.hpp"
+#include "split_merge.hpp"
 
 namespace h2o {
 namespace {
@@ -520,16 +521,14 @@ __global__ __launch_bounds__(NT_C) void evict_cand(EvictArgs a, uint2 *cand) {
 // LOGIT_ROWS_MAX rows per group): the workgroup first forms its slice's
 // summed weights from the logits -- the sum attn_b_logits forms, in the same
 // order -- and writes them, so the step needs no separate weight-sum launch;
-// then it updates, ranks and selects as evict_cand does.  One slot per thread
-// (NT_LG threads), so the sums keep the parallelism of a kernel of their own.
-// Workgroups with slice index x also merge output rows x, x + nslice, ...
-// of their groups from the key splits (and write their normalisers), and
-// slice 0 sums the chunk's own keys.
+// then it updates, ranks and lists candidates as evict_cand does.  One slot
+// per thread (NT_LG threads), so the sums keep the parallelism of a kernel of
+// their own.  Workgroups with slice index x also merge output rows x,
+// x + nslice, ... of their groups from the key splits (and write their
+// normalisers), and slice 0 sums the chunk's own keys.
 constexpr int NT_LG = SLICE;
 template <int POL>
 __global__ __launch_bounds__(NT_LG) void evict_cand_lg(EvictArgs e, AttnArgs a, float xs, uint2 *cand) {
-  constexpr int ITEMS = 1;
-  constexpr int HD = 128;  // head dimension of the short-chunk logit path
   __shared__ SelShared sh;
   __shared__ float Ls[LOGIT_ROWS_MAX], Ms[LOGIT_ROWS_MAX], Ws[LOGIT_ROWS_MAX];
   __shared__ float4 red_o[8][32];
@@ -538,183 +537,90 @@ __global__ __launch_bounds__(NT_LG) void evict_cand_lg(EvictArgs e, AttnArgs a, 
   const int slice = blockIdx.x, head = blockIdx.y, nslice = gridDim.x;
   const int s0 = slice * SLICE;
   const int len = min(SLICE, C - s0);
-  const int base = s0 + tid;
-  const int nvalid = s0 + len - base;
+  const int j = s0 + tid;  // this thread's slot
+  const bool own = tid < len;
   const int R = a.qg * a.T;
   const int n_keys = C + T;  // evicting: every slot is occupied
   const int nb = (POL == H2O_POLICY_ORIG) ? e.B : 1;
   const int32_t pos_end = static_cast<int32_t>(e.pos + T);
   const size_t rows = static_cast<size_t>(a.B) * a.Hq * a.T;
   const bool merger = a.nsplit > 1 && tid < 256;  // 8 groups of 32 lanes merge output rows
-  const int grp8 = (tid >> 5) & 7, c4 = tid & 31;
-  float rank[ITEMS];
+  const int q8 = (tid >> 5) & 7, c4 = tid & 31;
+  const int rn = tid >> 4, sl = tid & 15;  // normalisers: 16 lanes per row
+  // h2o_orig, which loops over the batch rows, loads a merged row's partials
+  // only when it merges it (registers)
+  constexpr bool kEarlyRow = POL != H2O_POLICY_ORIG;
+  float rank = 0.f;
   for (int bb = 0; bb < nb; ++bb) {
     const int grp = (POL == H2O_POLICY_ORIG) ? bb * e.Hkv + head : head;
     const int g = grp % a.Hkv, b = grp / a.Hkv;
     auto row_index = [&](int r) {
       return (static_cast<size_t>(b) * a.Hq + g * a.qg + r % a.qg) * a.T + r / a.qg;
     };
-    // Every load of the group is issued first (none depends on another):
-    // the split maxima / sums, the first output row's split partials, the
-    // slice's logits, scores and token positions.
-    // normalisers: 16 lanes per row, lane s takes splits s, s + 16, s + 32, s + 48
-    const int rn = tid >> 4, sl = tid & 15;
-    const size_t li_n = rn < R ? row_index(rn) : 0;
+    // Every load of the group first (none depends on another): split (m, l)
+    // pairs, the first merged row's partials, the slot's logits, score and
+    // token position.
     float2 ml[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int sp = sl + 16 * k;
-      ml[k] = (a.nsplit > 1 && rn < R && sp < a.nsplit)
-                  ? *reinterpret_cast<const float2 *>(a.part_ml + 2 * (sp * rows + li_n))
-                  : make_float2(-INFINITY, 0.f);
-    }
+    load_split_ml(a, rows, rn < R ? row_index(rn) : 0, sl, a.nsplit > 1 && rn < R, ml);
     const float lse_own = (a.nsplit == 1 && tid < R) ? a.lse2[row_index(tid)] : 0.f;
-    // output row r: group k takes splits k, k + 8, ... (at most 64 splits)
     float ms[8];
     float4 po[8];
-    auto load_row = [&](int r) {
-      const size_t li = row_index(r);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int sp = grp8 + 8 * k;
-        ms[k] = -INFINITY;
-        po[k] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (merger && sp < a.nsplit) {
-          const size_t pr = sp * rows + li;
-          ms[k] = a.part_ml[2 * pr];
-          po[k] = *reinterpret_cast<const float4 *>(a.part + pr * HD + 4 * c4);
-        }
-      }
-    };
-    // (h2o_orig, which loops over the batch rows, loads it later: registers)
-    constexpr bool kEarlyRow = POL != H2O_POLICY_ORIG;
-    if (kEarlyRow && slice < R) load_row(slice);
+    if (kEarlyRow && slice < R) load_split_row(a, rows, row_index(slice), q8, c4, merger, ms, po);
     const float *lgp = a.lg + static_cast<size_t>(grp) * R * a.lg_stride;
-    float x[LOGIT_ROWS_MAX][ITEMS];
+    float x[LOGIT_ROWS_MAX];
 #pragma unroll
-    for (int r = 0; r < LOGIT_ROWS_MAX; ++r)
-#pragma unroll
-      for (int k = 0; k < ITEMS; ++k)
-        x[r][k] = (r < R && k < nvalid) ? lgp[static_cast<size_t>(r) * a.lg_stride + base + k] : 0.f;
+    for (int r = 0; r < LOGIT_ROWS_MAX; ++r) x[r] = (r < R && own) ? lgp[static_cast<size_t>(r) * a.lg_stride + j] : 0.f;
     float *ph = e.scores + static_cast<size_t>(grp) * C;
-    const int32_t *tp = e.token_pos ? e.token_pos + static_cast<size_t>(grp) * C : nullptr;
-    float f[ITEMS];
-    int32_t t0[ITEMS] = {};
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      f[k] = k < nvalid ? ph[base + k] : 0.f;
-      if constexpr (POL == H2O_POLICY_NORM) t0[k] = k < nvalid ? tp[base + k] : 0;
-    }
+    float f = own ? ph[j] : 0.f;
+    int32_t t0 = 0;
+    if constexpr (POL == H2O_POLICY_NORM) t0 = own ? e.token_pos[static_cast<size_t>(grp) * C + j] : 0;
 
     // row normalisers of the group: merged from the key splits, or pass A's own
     if (a.nsplit > 1) {
-      float m = fmaxf(fmaxf(ml[0].x, ml[1].x), fmaxf(ml[2].x, ml[3].x));
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      float l = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (ml[k].x != -INFINITY) l = fmaf(ml[k].y, __builtin_amdgcn_exp2f(ml[k].x - m), l);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+      float M, W;
+      reduce_split_ml(ml, M, W);
       if (rn < R && sl == 0) {
-        Ms[rn] = m;
-        Ws[rn] = l;
-        Ls[rn] = m + log2f(l);
+        Ms[rn] = M;
+        Ws[rn] = W;
+        Ls[rn] = M + log2f(W);
       }
     } else if (tid < R) {
       Ls[tid] = lse_own;
     }
     __syncthreads();
-    // output rows slice, slice + nslice, ...: sum_s 2^(m_s - M) O_s / l,
-    // the 8 groups added in order
     for (int r = slice; a.nsplit > 1 && r < R; r += nslice) {
-      if (!kEarlyRow || r != slice) load_row(r);
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (ms[k] == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(ms[k] - Ms[r]);
-        acc.x = fmaf(po[k].x, w, acc.x);
-        acc.y = fmaf(po[k].y, w, acc.y);
-        acc.z = fmaf(po[k].z, w, acc.z);
-        acc.w = fmaf(po[k].w, w, acc.w);
-      }
-      if (merger) red_o[grp8][c4] = acc;
-      __syncthreads();
-      if (tid < 32) {
-        float4 t = red_o[0][c4];
-#pragma unroll
-        for (int k = 1; k < 8; ++k) {
-          const float4 u = red_o[k][c4];
-          t.x += u.x;
-          t.y += u.y;
-          t.z += u.z;
-          t.w += u.w;
-        }
-        const size_t li = row_index(r);
-        const float inv = 1.f / Ws[r];
-        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(t.x * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16(t.y * inv)) << 16);
-        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(t.z * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16(t.w * inv)) << 16);
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + li * HD + 4 * c4) = make_uint2(lo, hi);
-        if (c4 == 0) {
-          a.lse2[li] = Ls[r];
-          if (a.lse_nat) a.lse_nat[li] = Ls[r] * 0.69314718055994530942f;
-        }
-      }
+      const size_t li = row_index(r);
+      if (!kEarlyRow || r != slice) load_split_row(a, rows, li, q8, c4, merger, ms, po);
+      merge_split_row(a, li, Ms[r], Ws[r], Ls[r], q8, c4, merger, ms, po, red_o);
       __syncthreads();  // red_o is reused by the next row
     }
-    // summed weights: Kahan-compensated over the rows in order; every row
-    // sees the cache slots, row r sees chunk key t iff t * q_g <= r - r % q_g
+    // summed weights: every row sees the cache slots, row r sees chunk key t
+    // iff t * q_g <= r - r % q_g
     float *w = a.wsum + static_cast<size_t>(grp) * n_keys;
-    if (slice == 0 && tid < T) {
-      float acc = 0.f, comp = 0.f;
-      for (int r = 0; r < R; ++r) {
-        if (tid * a.qg <= r - r % a.qg) {
-          const float p =
-              __builtin_amdgcn_exp2f(fmaf(lgp[static_cast<size_t>(r) * a.lg_stride + C + tid], xs, -Ls[r]));
-          const float y = p - comp;
-          const float s2 = acc + y;
-          comp = (s2 - acc) - y;
-          acc = s2;
-        }
-      }
-      w[C + tid] = acc;
+    const float d = key_weight_sum(R, [&](int r) { return x[r]; }, [](int) { return true; }, xs, Ls);
+    if (slice == 0 && tid < T) {  // chunk key tid: its logits into x, all loads first
+#pragma unroll
+      for (int r = 0; r < LOGIT_ROWS_MAX; ++r) x[r] = r < R ? lgp[static_cast<size_t>(r) * a.lg_stride + C + tid] : 0.f;
+      w[C + tid] = key_weight_sum(
+          R, [&](int r) { return x[r]; }, [&](int r) { return tid * a.qg <= r - r % a.qg; }, xs, Ls);
     }
-#pragma unroll
-    for (int k = 0; k < ITEMS; ++k) {
-      float acc = 0.f, comp = 0.f;
-#pragma unroll
-      for (int r = 0; r < LOGIT_ROWS_MAX; ++r) {
-        if (r < R) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(x[r][k], xs, -Ls[r]));
-          const float y = p - comp;
-          const float s2 = acc + y;
-          comp = (s2 - acc) - y;
-          acc = s2;
-        }
-      }
-      if (k >= nvalid) continue;
-      w[base + k] = acc;
-      f[k] += acc;
-      ph[base + k] = f[k];
+    if (own) {
+      w[j] = d;
+      f += d;
+      ph[j] = f;
       if constexpr (POL == H2O_POLICY_ORIG) {
-        rank[k] = (bb == 0) ? f[k] : rank[k] + f[k];
+        rank = (bb == 0) ? f : rank + f;
       } else if constexpr (POL == H2O_POLICY_NORM) {
-        rank[k] = f[k] / static_cast<float>(pos_end - t0[k]);
+        rank = f / static_cast<float>(pos_end - t0);
       } else {
-        rank[k] = f[k];
+        rank = f;
       }
     }
     __syncthreads();  // Ls / Ms / Ws are rewritten for the next batch row
   }
-  uint32_t key[ITEMS];
-#pragma unroll
-  for (int k = 0; k < ITEMS; ++k) key[k] = k < nvalid ? ordered_key(rank[k]) : 0xffffffffu;
-  slice_candidates<NT_LG, ITEMS>(key, base, nvalid, s0, len, T,
-                                cand + (static_cast<size_t>(head) * nslice + slice) * T, sh);
+  const uint32_t key[1] = {own ? ordered_key(rank) : 0xffffffffu};
+  slice_candidates<NT_LG, 1>(key, j, own ? 1 : 0, s0, len, T, cand + (static_cast<size_t>(head) * nslice + slice) * T,
+                             sh);
 }
 
 // Short chunks, pass 2: the T smallest candidates of each head.  The lists
