@@ -40,6 +40,7 @@ constexpr int NT = 1024;     // threads of the per-head workgroups
 constexpr int SLICE = 1024;  // slots per candidate workgroup
 constexpr int NT_C = 256;    // threads of the candidate workgroups (4 slots each)
 constexpr int KV_FUSE_T = 64;  // chunks up to this length: the pick writes the K/V rows
+constexpr int QKV_FUSE_T = 4;  // 8/4-bit caches: the pick quantises the rows of chunks up to this length
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -786,8 +787,10 @@ void launch_pick(const EvictArgs &a, const uint2 *cand, int ncand, int nreal, co
                  int heads, hipStream_t s) {
   // short lists: one wavefront (two when the pick quantises a K and a V
   // row per head); longer ones: 256 or 1024 threads
-  if (KV && kv.cache_fmt != FMT_NATIVE && nreal <= 128) {
+  if (KV && kv.cache_fmt != FMT_NATIVE && a.T == 1 && nreal <= 128) {
     hipLaunchKernelGGL((evict_pick<128, 1, POL, KV>), dim3(heads), dim3(128), 0, s, a, cand, ncand, nreal, kv);
+  } else if (KV && kv.cache_fmt != FMT_NATIVE && nreal <= 512) {  // a wavefront per quantised row
+    hipLaunchKernelGGL((evict_pick<512, 1, POL, KV>), dim3(heads), dim3(512), 0, s, a, cand, ncand, nreal, kv);
   } else if (nreal <= 64) {
     hipLaunchKernelGGL((evict_pick<64, 1, POL, KV>), dim3(heads), dim3(64), 0, s, a, cand, ncand, nreal, kv);
   } else if (nreal <= 256) {
@@ -851,12 +854,13 @@ hipError_t launch_evict(const EvictArgs &a, void *ws, size_t ws_bytes, hipStream
                lg->B * lg->Hkv != a.groups || lg->T != a.T || lg->n_occ != a.n_occ || lg->nsplit > 64))
       return hipErrorInvalidValue;
     // fuse the K/V write into the pick (evict-only bookkeeping): native
-    // caches up to KV_FUSE_T tokens; 8/4-bit caches for one token, where the
-    // two quantised rows per head cost less than a launch (from four tokens
-    // on, the write kernel's one wavefront per row is faster)
+    // caches up to KV_FUSE_T tokens; 8/4-bit caches up to QKV_FUSE_T tokens,
+    // whose 2T quantised rows per head the pick's wavefronts take one each
+    // (with T = 1 a two-wavefront pick; else eight)
     const bool fuse = kv && kv_done && !kv->token_pos &&
                       ((kv->cache_fmt == FMT_NATIVE && a.T <= KV_FUSE_T) ||
-                       (kv->dtype == DT_BF16 && a.T == 1 && kv->D <= 128));
+                       (kv->dtype == DT_BF16 && a.T <= QKV_FUSE_T && kv->D <= 128 &&
+                        n_slices(a.C) * a.T <= 512));
     const KvWriteArgs *kvp = fuse ? kv : nullptr;
     if (fuse) *kv_done = true;
     if (a.policy == H2O_POLICY_NORM) return launch_two_pass<H2O_POLICY_NORM>(a, cand, kvp, lg, s);
