@@ -472,10 +472,14 @@ __global__ __launch_bounds__(256, 2) void attn_a_dec(AttnArgs a) {
         *reinterpret_cast<float4 *>(a.lg + (static_cast<size_t>(grp) * R + n) * a.lg_stride + j0 + 16 * wave +
                                     4 * g4) = make_float4(c[0], c[1], c[2], c[3]);
     }
+    // Tiles below n_occ need no mask: rows past R compute values that are
+    // never written.
+    if (j0 + 64 > n_occ) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ja = j0 + 16 * wave + 4 * g4 + i - n_occ;  // chunk index, < 0 for cache
-      c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int ja = j0 + 16 * wave + 4 * g4 + i - n_occ;  // chunk index, < 0 for cache
+        c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
+      }
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
     mx = max_xor32(max_xor16(mx));
@@ -493,7 +497,7 @@ __global__ __launch_bounds__(256, 2) void attn_a_dec(AttnArgs a) {
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(c[i], sl2, neg_m));
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
     const i16x4 pb = __builtin_bit_cast(
-        i16x4, make_uint2(pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3])));
+        i16x4, make_uint2(pack_bf16_hw(p[0], p[1]), pack_bf16_hw(p[2], p[3])));
     // V^T operand: d = 16*dblk + n, keys 16*wave + 4*g4 + 0..3
     const int vrow = 16 * wave + 4 * g4 + (n >> 2);
 #pragma unroll

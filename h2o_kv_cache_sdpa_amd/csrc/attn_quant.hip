@@ -513,26 +513,83 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Short chunks (at most 16 packed rows per KV group): the same codes pipeline,
-// but each wavefront takes 16 keys of every tile on 16x16 MFMAs, as the native
-// short-chunk pass does; the four wavefronts merge at the end.
+// Short chunks (at most 16 packed rows per KV group).  Each wavefront takes
+// 16 keys of every 64-key tile of its split on 16x16 MFMAs, and the four
+// wavefronts merge at the end.  The codes go HBM -> registers with plain
+// loads, NPF tiles ahead, and widen in registers straight into the MFMA
+// operands: nothing passes through LDS between load and use, and no
+// wavefront waits for another inside the tile loop.  The pace is set by the
+// per-tile instruction chain (widening, products, softmax), not by the loads:
+// with the loads taken out the pass is about as slow, and rings deeper than
+// two tiles or eight wavefronts per block measured slower.
+//
+// Head-dimension order inside the products.  One permutation of d applied
+// to both operands of S = K Q^T leaves every dot product unchanged, and one
+// applied to V's columns only relabels O's; both are chosen so that a lane's
+// share of an operand is contiguous in a code row:
+//   S (steps st = 0..3 of 16x16x32): lane (n, g) = (lane % 16, lane / 16)
+//     supplies key n and query row n at d = 32 g + 8 st + e, e = 0..7;
+//   O^T += V^T P^T (blocks k = 0..7 of 16x16x16): lane (m, g) supplies
+//     d = 8 m + k of keys 4 g + i, i = 0..3 (bytes 8m.. of an 8-bit code row,
+//     4m.. of a 4-bit one); its accumulator register i of block k then holds
+//     d = 32 g + 8 i + k of query row lane % 16.
 // ---------------------------------------------------------------------------
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-template <int FMT, bool LG>
-__global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
-  using Q = QTile<FMT>;
-  // widened bf16 tiles and their per-key factors, double-buffered
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
-  __shared__ __attribute__((aligned(256))) float fac0[4][64];
-  __shared__ __attribute__((aligned(256))) float fac1[4][64];
-  __shared__ float red_m[4][16], red_l[4][16];
+// bf16 patterns of two fp32 values that bf16 holds exactly, as one word
+__device__ __forceinline__ uint32_t hi16_pair(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// 8 consecutive codes of a row (8-bit: 8 bytes; 4-bit: 4 bytes, low nibble
+// first) -> 8 bf16, as they are (no offset).
+template <int FMT>
+__device__ __forceinline__ uint4 widen8(const char *p) {
+  if constexpr (FMT == FMT_INT8) {
+    const uint2 x = *reinterpret_cast<const uint2 *>(p);
+    const int32_t w[2] = {static_cast<int32_t>(x.x), static_cast<int32_t>(x.y)};
+    uint32_t r[4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      r[2 * h] = hi16_pair(static_cast<float>((w[h] << 24) >> 24), static_cast<float>((w[h] << 16) >> 24));
+      r[2 * h + 1] = hi16_pair(static_cast<float>((w[h] << 8) >> 24), static_cast<float>(w[h] >> 24));
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+  } else {
+    const uint32_t x = *reinterpret_cast<const uint32_t *>(p);
+    uint32_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      r[q] = hi16_pair(static_cast<float>((x >> (8 * q)) & 15u), static_cast<float>((x >> (8 * q + 4)) & 15u));
+    return make_uint4(r[0], r[1], r[2], r[3]);
+  }
+}
+
+// One lane's share of one tile wholly in the cache, as loaded.
+template <int FMT>
+struct DecShare {
+  static constexpr int KW = FMT == FMT_INT8 ? 2 : 1;  // 16-byte words of key codes (key n)
+  static constexpr int VW = FMT == FMT_INT8 ? 8 : 4;  // 32-bit words of value codes (keys 4g + i)
+  static constexpr int NF = FMT == FMT_INT8 ? 2 : 4;  // factor arrays: ks, vs (, kz, vz)
+  uint4 k[KW];
+  uint32_t v[VW];
+  uint2 f[NF];  // fp16 factors of keys 4g .. 4g + 3
+};
+
+template <int FMT, bool LG, int NPF, int NW>
+__global__ __launch_bounds__(64 * NW, NW / 2) void attn_a_qdec(AttnArgs a) {
+  using Sh = DecShare<FMT>;
+  constexpr int CODE_ROW = QTile<FMT>::CODE_ROW;
+  constexpr int RS = D + 4;  // row stride of the merge rows (floats): 16 rows meet distinct banks
+  __shared__ __attribute__((aligned(16))) float red_o[NW][16 * RS];
+  __shared__ float red_m[NW][16], red_l[NW][16];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g4 = lane >> 4;  // row of the lane; key / d group
+  const int n = lane & 15, g4 = lane >> 4;  // row / key of the lane; key / d group
+  // wavefront w takes keys 16 (w % 4) .. + 15 of the tiles t = tpar (mod TS)
+  constexpr int TS = NW / 4;
+  const int wq = wave & 3, tpar = wave >> 2;
   const int R = a.qg * a.T;                 // <= 16
   const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
   const int split = wi_all % a.nsplit;
@@ -544,14 +601,14 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
   const int n_occ = a.n_occ;
 
-  bf16x8 qf[4];
+  bf16x8 qf[4];  // step st: d = 32 g4 + 8 st .. + 7 of row n
   float qsum = 0.f;
   {
-    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) + li * D;
+    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) + li * D + 32 * g4;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_ok) v = *reinterpret_cast<const uint4 *>(qrow + 32 * st + 8 * g4);
+      if (row_ok) v = *reinterpret_cast<const uint4 *>(qrow + 8 * st);
       qf[st] = __builtin_bit_cast(bf16x8, v);
       if constexpr (FMT == FMT_INT4) {
 #pragma unroll
@@ -573,121 +630,51 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   split_tiles(ntiles_all, a.nsplit, split, t_lo, ntiles);
   const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
   const size_t new_row0 = static_cast<size_t>(grp) * a.T;
-  // Codes move HBM -> registers with plain vector loads, one tile ahead of
-  // their use: thread tid holds the 32 codes of key row tid / 4, quarter
-  // tid % 4, of K and of V (int8: 2 x 16 bytes each, int4: 16 bytes), and
-  // every lane of wavefront w the fp16 factors of key 16w + lane % 16.
-  // (Prefetching two or three tiles ahead measured slower: the per-tile
-  // chain of widening, LDS round trip and products sets the pace, not the
-  // loads in flight.)  Wavefront w widens, stores and reads back only the
-  // rows of its own keys 16w .. 16w + 15, so the wavefronts never wait for
-  // each other inside the tile loop.
-  constexpr int CW = Q::CODE_ROW / 4 / 16;  // 16-byte words of one thread's share
-  struct Codes {
-    uint4 k[CW], v[CW];
-    uint16_t f[Q::NFAC];
-  };
+  const char *kcb = static_cast<const char *>(a.kc), *vcb = static_cast<const char *>(a.vc);
   const uint16_t *fsrc[4] = {a.ks, a.vs, a.kz, a.vz};
-  const int crow = tid >> 2, cq = tid & 3;   // crow = 16 * wave + lane / 4
-  const int fkey = 16 * wave + (lane & 15);  // key of the factors lane < 16 holds
-  // Tiles 0 .. nfull-1 of the split lie wholly in the cache: their loads
-  // are unconditional, so the compiler can count them (a tile past nfull
-  // reloads tile nfull - 1, an L2 hit; every lane loads the factors of key
-  // fkey).  The rest (the tile that straddles n_occ, chunk rows)
-  // take a direct path after the main loop.
+  const int kk0 = 16 * wq + 4 * g4;  // tile key of the lane's first logit
+
+  // Tiles 0 .. nfull-1 of the split lie wholly in the cache and take the
+  // prefetched path; the rest (the tile that straddles n_occ, chunk keys)
+  // load as they go.
   const int nfull = max(0, min(ntiles, n_occ / 64 - t_lo));
-  auto load_codes = [&](int tile, Codes &c) {
-    const int j0 = (t_lo + (tile < nfull ? tile : nfull - 1)) * 64;
-    const size_t off = (cache_row0 + j0 + crow) * Q::CODE_ROW + cq * (Q::CODE_ROW / 4);
+  auto load_share = [&](int tile, Sh &s) {
+    const size_t jw = cache_row0 + static_cast<size_t>(t_lo + tile) * 64 + 16 * wq;
+    const char *kp = kcb + (jw + n) * CODE_ROW + g4 * (CODE_ROW / 4);
 #pragma unroll
-    for (int w = 0; w < CW; ++w) {
-      c.k[w] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.kc) + off + 16 * w);
-      c.v[w] = *reinterpret_cast<const uint4 *>(static_cast<const char *>(a.vc) + off + 16 * w);
-    }
-#pragma unroll
-    for (int f = 0; f < Q::NFAC; ++f) c.f[f] = fsrc[f][cache_row0 + j0 + fkey];
-  };
-  auto store = [&](char *kb, char *vb, const uint4 (&kw)[4], const uint4 (&vw)[4]) {
+    for (int w = 0; w < Sh::KW; ++w) s.k[w] = *reinterpret_cast<const uint4 *>(kp + 16 * w);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4 *>(kb + kq_off(crow, 4 * cq + i)) = kw[i];
-      *reinterpret_cast<uint4 *>(vb + vq_off(crow, 4 * cq + i)) = vw[i];
-    }
-  };
-  auto store_fac = [&](float (*fac)[64], bool cached, const uint16_t *f) {
-    fac[0][fkey] = cached ? f16_to_f32(f[0]) * a.sl2 : a.sl2;
-    fac[2][fkey] = cached ? f16_to_f32(f[1]) : 1.f;
-    if constexpr (FMT == FMT_INT4) {  // widened key codes are 16 + n: key zero point z - 16 s
-      fac[1][fkey] = cached ? (f16_to_f32(f[2]) - 16.f * f16_to_f32(f[0])) * a.sl2 : 0.f;
-      fac[3][fkey] = cached ? f16_to_f32(f[3]) : 0.f;
-    }
-  };
-  // a tile wholly in the cache, from the prefetched registers
-  auto widen_full = [&](const Codes &c, char *kb, char *vb, float (*fac)[64]) {
-    uint4 kw[4], vw[4];
-    widen32<FMT, true>(reinterpret_cast<const char *>(c.k), kw);
-    widen32<FMT>(reinterpret_cast<const char *>(c.v), vw);
-    store(kb, vb, kw, vw);
-    store_fac(fac, true, c.f);  // four lanes per key write the same values
-  };
-  // any other tile, loading as it goes: codes of rows below n_occ, new keys
-  // (bf16) above, zeros past the chunk
-  auto widen_direct = [&](int tile, char *kb, char *vb, float (*fac)[64]) {
-    const int j0 = (t_lo + tile) * 64;
-    const int j = j0 + crow;
-    uint4 kw[4], vw[4];
-    if (j < n_occ) {
-      const size_t off = (cache_row0 + j) * Q::CODE_ROW + cq * (Q::CODE_ROW / 4);
-      widen32<FMT, true>(static_cast<const char *>(a.kc) + off, kw);
-      widen32<FMT>(static_cast<const char *>(a.vc) + off, vw);
-    } else {
-      const int t = j - n_occ;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        kw[i] = vw[i] = make_uint4(0, 0, 0, 0);
-        if (t < a.T) {
-          const size_t e = (new_row0 + t) * D + 32 * cq + 8 * i;
-          kw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.kn) + e);
-          vw[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.vn) + e);
-        }
+      const char *vp = vcb + (jw + 4 * g4 + i) * CODE_ROW + n * (CODE_ROW / 16);
+      if constexpr (FMT == FMT_INT8) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(vp);
+        s.v[2 * i] = x.x;
+        s.v[2 * i + 1] = x.y;
+      } else {
+        s.v[i] = *reinterpret_cast<const uint32_t *>(vp);
       }
     }
-    store(kb, vb, kw, vw);
-    if (lane < 16) {
-      const bool cached = j0 + fkey < n_occ;
-      uint16_t f[4] = {0, 0, 0, 0};
-      if (cached) {
 #pragma unroll
-        for (int q = 0; q < Q::NFAC; ++q) f[q] = fsrc[q][cache_row0 + j0 + fkey];
-      }
-      store_fac(fac, cached, f);
-    }
+    for (int f = 0; f < Sh::NF; ++f) __builtin_memcpy(&s.f[f], fsrc[f] + jw + 4 * g4, sizeof(uint2));
   };
 
   f32x4 o[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) o[k] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f, u_run = 0.f;
-  const int krow = 16 * wave + n;
-  const int kk0 = 16 * wave + 4 * g4;  // tile key of the lane's first value
 
-  auto compute = [&](int tile, const char *kb, const char *vb, const float (*fac)[64]) {
+  // One tile: kw the lane's K operands (bf16), sk / zk / sv / zv the factors
+  // of keys kk0 + i, vop(k) the lane's V operand of block k.
+  // masked false (tiles wholly below n_occ): every key is visible to every
+  // row, and rows past R compute values that are never written.
+  auto tile_body = [&](int tile, const uint4 (&kw)[4], const float (&sk)[4], const float (&zk)[4],
+                       const float (&sv)[4], const float (&zv)[4], auto &&vop, auto masked) {
     const int j0 = (t_lo + tile) * 64;
     f32x4 c = f32x4{};
 #pragma unroll
     for (int st = 0; st < 4; ++st)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(kb + kq_off(krow, 4 * st + g4)), qf[st], c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kw[st]), qf[st], c, 0, 0, 0);
     // c[i]: tile key kk0 + i of row n; factors bring it to log2 units
-    const float4 s4 = *reinterpret_cast<const float4 *>(&fac[0][kk0]);
-    const float sk[4] = {s4.x, s4.y, s4.z, s4.w};
-    float zk[4] = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (FMT == FMT_INT4) {
-      const float4 z4 = *reinterpret_cast<const float4 *>(&fac[1][kk0]);
-      zk[0] = z4.x;
-      zk[1] = z4.y;
-      zk[2] = z4.z;
-      zk[3] = z4.w;
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = (FMT == FMT_INT4) ? fmaf(c[i], sk[i], zk[i] * qsum) : c[i] * sk[i];
     if constexpr (LG) {
@@ -695,10 +682,12 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
         *reinterpret_cast<float4 *>(a.lg + (static_cast<size_t>(grp) * R + n) * a.lg_stride + j0 + kk0) =
             make_float4(c[0], c[1], c[2], c[3]);
     }
+    if constexpr (decltype(masked)::value) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ja = j0 + kk0 + i - n_occ;
-      c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) {
+        const int ja = j0 + kk0 + i - n_occ;
+        c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
+      }
     }
     float mx = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
     mx = max_xor32(max_xor16(mx));
@@ -711,62 +700,148 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
       m_run = mx;
     }
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    const float4 v4 = *reinterpret_cast<const float4 *>(&fac[2][kk0]);
-    const float sv[4] = {v4.x, v4.y, v4.z, v4.w};
     float p[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(c[i] + neg_m);
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    if constexpr (FMT == FMT_INT4) {
-      const float4 w4 = *reinterpret_cast<const float4 *>(&fac[3][kk0]);
-      u_run = fmaf(p[0], w4.x, fmaf(p[1], w4.y, fmaf(p[2], w4.z, fmaf(p[3], w4.w, u_run))));
-    }
+    if constexpr (FMT == FMT_INT4) u_run = fmaf(p[0], zv[0], fmaf(p[1], zv[1], fmaf(p[2], zv[2], fmaf(p[3], zv[3], u_run))));
     const i16x4 pb = __builtin_bit_cast(
-        i16x4, make_uint2(pack_bf16_rne(p[0] * sv[0], p[1] * sv[1]), pack_bf16_rne(p[2] * sv[2], p[3] * sv[3])));
-    const int vrow = 16 * wave + 4 * g4 + (n >> 2);
+        i16x4, make_uint2(pack_bf16_hw(p[0] * sv[0], p[1] * sv[1]), pack_bf16_hw(p[2] * sv[2], p[3] * sv[3])));
 #pragma unroll
-    for (int dblk = 0; dblk < 8; ++dblk) {
-      const int col = 16 * dblk + 4 * (n & 3);
-      const i16x4 va = lds_tr(vb + vq_off(vrow, col >> 3) + 2 * (col & 7));
-      o[dblk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dblk], 0, 0, 0);
+    for (int k = 0; k < 8; ++k) o[k] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop(k), pb, o[k], 0, 0, 0);
+  };
+
+  // a tile wholly in the cache, from its loaded share
+  auto full_tile = [&](int tile, const Sh &s) {
+    uint4 kw[4];
+    widen32<FMT, FMT == FMT_INT4>(reinterpret_cast<const char *>(s.k), kw);
+    float sk[4], zk[4], sv[4], zv[4];
+    const f16x4 fks = __builtin_bit_cast(f16x4, s.f[0]), fvs = __builtin_bit_cast(f16x4, s.f[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sk[i] = static_cast<float>(fks[i]) * a.sl2;
+      sv[i] = static_cast<float>(fvs[i]);
+      zk[i] = zv[i] = 0.f;
+    }
+    if constexpr (FMT == FMT_INT4) {
+      // the widened key codes are 16 + n: k = s n + z = s (16 + n) + (z - 16 s)
+      const f16x4 fkz = __builtin_bit_cast(f16x4, s.f[2]), fvz = __builtin_bit_cast(f16x4, s.f[3]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        zk[i] = (static_cast<float>(fkz[i]) - 16.f * static_cast<float>(fks[i])) * a.sl2;
+        zv[i] = static_cast<float>(fvz[i]);
+      }
+    }
+    if constexpr (FMT == FMT_INT8) {
+      tile_body(tile, kw, sk, zk, sv, zv, [&](int k) {
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int32_t w = static_cast<int32_t>(s.v[2 * i + (k >> 2)]);
+          f[i] = static_cast<float>((w << (24 - 8 * (k & 3))) >> 24);
+        }
+        return __builtin_bit_cast(i16x4, make_uint2(hi16_pair(f[0], f[1]), hi16_pair(f[2], f[3])));
+      }, std::false_type{});
+    } else {
+      uint32_t nib[4];  // the lane's nibble k of row i sits in byte k / 2 of nib[i] (>> 4 if k odd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nib[i] = s.v[i];
+      tile_body(tile, kw, sk, zk, sv, zv, [&](int k) {
+        float f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t x = (k & 1) ? ((nib[i] >> 4) & 0x0f0f0f0fu) : (nib[i] & 0x0f0f0f0fu);
+          f[i] = static_cast<float>((x >> (8 * (k >> 1))) & 0xffu);
+        }
+        return __builtin_bit_cast(i16x4, make_uint2(hi16_pair(f[0], f[1]), hi16_pair(f[2], f[3])));
+      }, std::false_type{});
     }
   };
 
-  // Tile t: widen into buffer t & 1, refill the registers with tile t + 1,
-  // compute.  Lanes read rows that other lanes of their wavefront wrote;
-  // wave_lds_sync keeps the reads of tile t after its writes, and (one tile
-  // on) the reads of tile t - 1 before the writes of tile t + 1 into the
-  // same buffer.  Tiles go in pairs (buffers 0, 1) with no branch inside a
-  // pair, so the compiler may overlap one tile's widening with the other's
-  // products.
-  if (nfull > 0) {
-    Codes cr;
-    load_codes(0, cr);
-    int t = 0;
-    for (; t + 2 <= nfull; t += 2) {
-      widen_full(cr, kb0, vb0, fac0);
-      load_codes(t + 1, cr);
-      wave_lds_sync();
-      compute(t, kb0, vb0, fac0);
-      widen_full(cr, kb1, vb1, fac1);
-      load_codes(t + 2, cr);
-      wave_lds_sync();
-      compute(t + 1, kb1, vb1, fac1);
+  // any other tile: codes of rows below n_occ, new keys (bf16) above, zeros
+  // past the chunk
+  auto tail_tile = [&](int tile) {
+    const int j0 = (t_lo + tile) * 64;
+    const int jk = j0 + 16 * wq + n;  // key row of the lane's K operand
+    uint4 kw[4];
+    if (jk < n_occ) {
+      widen32<FMT, FMT == FMT_INT4>(kcb + (cache_row0 + jk) * CODE_ROW + g4 * (CODE_ROW / 4), kw);
+    } else {
+      const int t = jk - n_occ;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        kw[st] = make_uint4(0, 0, 0, 0);
+        if (t < a.T)
+          kw[st] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.kn) + (new_row0 + t) * D +
+                                                    32 * g4 + 8 * st);
+      }
     }
-    if (t < nfull) {
-      widen_full(cr, kb0, vb0, fac0);
-      wave_lds_sync();
-      compute(t, kb0, vb0, fac0);
+    uint4 vrow[4];  // d = 8n .. 8n + 7 of key kk0 + i, bf16
+    float sk[4], zk[4], sv[4], zv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = j0 + kk0 + i;
+      if (j < n_occ) {
+        const size_t row = cache_row0 + j;
+        vrow[i] = widen8<FMT>(vcb + row * CODE_ROW + n * (CODE_ROW / 16));
+        const float s_k = f16_to_f32(a.ks[row]);
+        sk[i] = s_k * a.sl2;
+        sv[i] = f16_to_f32(a.vs[row]);
+        zk[i] = zv[i] = 0.f;
+        if constexpr (FMT == FMT_INT4) {
+          zk[i] = (f16_to_f32(a.kz[row]) - 16.f * s_k) * a.sl2;
+          zv[i] = f16_to_f32(a.vz[row]);
+        }
+      } else {
+        const int t = j - n_occ;
+        vrow[i] = make_uint4(0, 0, 0, 0);
+        if (t < a.T)
+          vrow[i] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.vn) + (new_row0 + t) * D + 8 * n);
+        sk[i] = a.sl2;
+        sv[i] = 1.f;
+        zk[i] = zv[i] = 0.f;
+      }
     }
+    tile_body(tile, kw, sk, zk, sv, zv, [&](int k) {
+      auto el = [&](const uint4 &r) {
+        const uint32_t w = (k >> 1) == 0 ? r.x : (k >> 1) == 1 ? r.y : (k >> 1) == 2 ? r.z : r.w;
+        return (k & 1) ? (w >> 16) : (w & 0xffffu);
+      };
+      return __builtin_bit_cast(i16x4, make_uint2(el(vrow[0]) | (el(vrow[1]) << 16), el(vrow[2]) | (el(vrow[3]) << 16)));
+    }, std::true_type{});
+  };
+
+  // Full tiles through a ring of NPF shares: the share of the wavefront's
+  // u-th tile is loaded NPF of its tiles before its use.  Inside the loop
+  // every load is unconditional, so the compiler counts the loads in flight
+  // exactly.
+  const int mfull = nfull > tpar ? (nfull - tpar + TS - 1) / TS : 0;    // the wavefront's full tiles
+  const int mtiles = ntiles > tpar ? (ntiles - tpar + TS - 1) / TS : 0;  // and all its tiles
+  if (mfull > 0) {
+    Sh sh[NPF];
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) load_share(min(p, mfull - 1) * TS + tpar, sh[p]);
+    int u = 0;
+    for (; u + 2 * NPF <= mfull; u += NPF) {
+#pragma unroll
+      for (int p = 0; p < NPF; ++p) {
+        full_tile((u + p) * TS + tpar, sh[p]);
+        load_share((u + p + NPF) * TS + tpar, sh[p]);
+      }
+    }
+    // fewer than 2 NPF full tiles left, the first NPF of them (or all) loaded
+#pragma unroll
+    for (int p = 0; p < NPF; ++p) {
+      if (u + p < mfull) {
+        full_tile((u + p) * TS + tpar, sh[p]);
+        if (u + p + NPF < mfull) load_share((u + p + NPF) * TS + tpar, sh[p]);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < NPF; ++p)
+      if (u + NPF + p < mfull) full_tile((u + NPF + p) * TS + tpar, sh[p]);
   }
-  for (int t = nfull; t < ntiles; ++t) {
-    char *kb = (t & 1) ? kb1 : kb0;
-    char *vb = (t & 1) ? vb1 : vb0;
-    float (*fac)[64] = (t & 1) ? fac1 : fac0;
-    widen_direct(t, kb, vb, fac);
-    wave_lds_sync();
-    compute(t, kb, vb, fac);
-  }
+  for (int u = mfull; u < mtiles; ++u) tail_tile(u * TS + tpar);
 
   // ---- merge the four wavefronts (u: the zero-point term, the same for every d) ----
   float l_w = l_run + __shfl_xor(l_run, 16);
@@ -777,19 +852,22 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
     red_m[wave][n] = m_run;
     red_l[wave][n] = l_w;
   }
-  __syncthreads();  // also: every wavefront is done with the tiles
+  __syncthreads();
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][n]);
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][n]);
   const float my_scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  auto red_o = [&](int w) { return reinterpret_cast<float *>(w < 2 ? kb0 : vb0) + (w & 1) * 16 * D; };
   {
-    float *mine = red_o(wave);
+    float *mine = red_o[wave] + n * RS + 32 * g4;  // d = 32 g4 + 8 i + k at mine[8 i + k]
 #pragma unroll
-    for (int dblk = 0; dblk < 8; ++dblk)
-      *reinterpret_cast<float4 *>(mine + n * D + 16 * dblk + 4 * g4) =
-          make_float4((o[dblk][0] + u_w) * my_scale, (o[dblk][1] + u_w) * my_scale,
-                      (o[dblk][2] + u_w) * my_scale, (o[dblk][3] + u_w) * my_scale);
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<float4 *>(mine + 8 * i) =
+          make_float4((o[0][i] + u_w) * my_scale, (o[1][i] + u_w) * my_scale, (o[2][i] + u_w) * my_scale,
+                      (o[3][i] + u_w) * my_scale);
+      *reinterpret_cast<float4 *>(mine + 8 * i + 4) =
+          make_float4((o[4][i] + u_w) * my_scale, (o[5][i] + u_w) * my_scale, (o[6][i] + u_w) * my_scale,
+                      (o[7][i] + u_w) * my_scale);
+    }
   }
   __syncthreads();
   const int rr = tid >> 4, d0 = 8 * (tid & 15);
@@ -800,10 +878,10 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
 #pragma unroll
     for (int e4 = 0; e4 < 2; ++e4) {
-      const float4 v = *reinterpret_cast<const float4 *>(red_o(w) + rr * D + d0 + 4 * e4);
+      const float4 v = *reinterpret_cast<const float4 *>(red_o[w] + rr * RS + d0 + 4 * e4);
       acc[4 * e4] += v.x;
       acc[4 * e4 + 1] += v.y;
       acc[4 * e4 + 2] += v.z;
@@ -812,9 +890,9 @@ __global__ __launch_bounds__(256, 2) void attn_a_qdec(AttnArgs a) {
   }
   float Mr = -INFINITY, lr_tot = 0.f;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) Mr = fmaxf(Mr, red_m[w][rr]);
+  for (int w = 0; w < NW; ++w) Mr = fmaxf(Mr, red_m[w][rr]);
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float mw = red_m[w][rr];
     lr_tot += (mw == -INFINITY) ? 0.f : red_l[w][rr] * __builtin_amdgcn_exp2f(mw - Mr);
   }
@@ -847,17 +925,20 @@ hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s) {
   const int nA = groups * ((R + 127) / 128) * a.nsplit;
   KernelTimer timer(H2O_K_ATTN_A, s);
   if (R <= 16) {  // short chunks: 16 keys of each tile per wavefront
+    // tiles each wavefront keeps in flight (4 KB of 8-bit / 2 KB of 4-bit
+    // codes each) and wavefronts per block
+    constexpr int PF8 = 2, PF4 = 2, NWD = 4;
     const int nD = groups * a.nsplit;
     if (a.cache_fmt == FMT_INT8) {
       if (a.lg) {
-        hipLaunchKernelGGL((attn_a_qdec<FMT_INT8, true>), dim3(nD), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_a_qdec<FMT_INT8, true, PF8, NWD>), dim3(nD), dim3(64 * NWD), 0, s, a);
       } else {
-        hipLaunchKernelGGL((attn_a_qdec<FMT_INT8, false>), dim3(nD), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_a_qdec<FMT_INT8, false, PF8, NWD>), dim3(nD), dim3(64 * NWD), 0, s, a);
       }
     } else if (a.lg) {
-      hipLaunchKernelGGL((attn_a_qdec<FMT_INT4, true>), dim3(nD), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_a_qdec<FMT_INT4, true, PF4, NWD>), dim3(nD), dim3(64 * NWD), 0, s, a);
     } else {
-      hipLaunchKernelGGL((attn_a_qdec<FMT_INT4, false>), dim3(nD), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_a_qdec<FMT_INT4, false, PF4, NWD>), dim3(nD), dim3(64 * NWD), 0, s, a);
     }
     return hipGetLastError();
   }

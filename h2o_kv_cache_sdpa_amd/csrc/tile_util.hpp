@@ -114,6 +114,14 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
 }
 
+// The same rounding (to nearest even) by one v_cvt_pk_bf16_f32, for MFMA
+// operands inside tile loops; pack_bf16_rne's NaN test compiles to a branch.
+__device__ __forceinline__ uint32_t pack_bf16_hw(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
 // Logits of one 64-key tile of S^T = K Q^T as laid out by the key permutation
 // above: register r of c0 holds key 16*(r/8) + 8*hl + r%8 of the tile, c1 the
 // same + 32, all for the lane's query row.  dst points at key 8*hl of the
