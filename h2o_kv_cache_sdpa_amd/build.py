@@ -29,7 +29,7 @@ ASAN_EXE = os.path.join(DEBUG_BUILD, "abi_asan")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ROCM_LIB = "/opt/rocm/lib"
 
-SOURCES = ["h2o_abi.cpp", "profile.cpp", "attn_simple.hip", "attn_mfma.hip", "attn_native.hip", "attn_quant.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "evict.hip", "kvwrite.hip"]
+SOURCES = ["h2o_abi.cpp", "profile.cpp", "attn_simple.hip", "attn_mfma.hip", "attn_native.hip", "attn_quant.hip", "attn_short.hip", "attn_bwd.hip", "attn_bwd_dq.hip", "evict.hip", "kvwrite.hip"]
 
 # Packed fp32 VALU forms are disabled: every fp32 operation is issued as a
 # scalar-per-lane instruction.  No fast-math: the quantisers rely on IEEE

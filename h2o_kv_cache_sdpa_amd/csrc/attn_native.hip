@@ -368,238 +368,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Pass A for short chunks: at most 16 packed query rows per KV group
-// (q_g * T <= 16).  The 128-row layout above would spend its matrix work on
-// empty rows, so here each wavefront takes 16 keys of every 64-key tile:
-// S^T = K Q^T on 16x16x32 MFMAs (keys x rows), O^T += V^T P^T on 16x16x16
-// MFMAs whose P^T operand is the S^T result of the same lanes and whose V^T
-// operand is a transpose read of the V tile.  Each wavefront keeps its own
-// running max and sum; the four merge through LDS at the end (the same
-// rescaling the key-split combine applies).  Tiles move by buffer-load DMA
-// into double buffers as in the 128-row pass.
-// ---------------------------------------------------------------------------
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-template <bool LG>
-__global__ __launch_bounds__(256, 2) void attn_a_dec(AttnArgs a) {
-  __shared__ __attribute__((aligned(1024))) char kb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char kb1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char vb1[TILE_BYTES];
-  __shared__ float red_m[4][16], red_l[4][16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n = lane & 15, g4 = lane >> 4;  // row of the lane; key / d group
-  const int R = a.qg * a.T;                 // <= 16
-  const int wi_all = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = wi_all % a.nsplit;
-  const int grp = wi_all / a.nsplit;
-  const int g = grp % a.Hkv, b = grp / a.Hkv;
-  const bool row_ok = n < R;
-  const int i_q = row_ok ? n / a.qg : 0;
-  const int h_q = g * a.qg + (row_ok ? n % a.qg : 0);
-  const size_t li = (static_cast<size_t>(b) * a.Hq + h_q) * a.T + i_q;
-  const int n_occ = a.n_occ;
-  const float sl2 = a.sl2;
-
-  // Q row n, d = 32*st + 8*g4 .. +7: B operand of S^T = K Q^T, step st
-  bf16x8 qf[4];
-  {
-    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) + li * D;
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (row_ok) v = *reinterpret_cast<const uint4 *>(qrow + 32 * st + 8 * g4);
-      qf[st] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  const int key_end = n_occ + (R - 1) / a.qg + 1;
-  const int ntiles_all = (key_end + 63) / 64;
-  int t_lo, ntiles;  // key tiles t_lo .. t_lo + ntiles - 1 of this split (ntiles 0: none)
-  split_tiles(ntiles_all, a.nsplit, split, t_lo, ntiles);
-  const size_t cache_row0 = static_cast<size_t>(grp) * a.C;
-  const size_t new_row0 = static_cast<size_t>(grp) * a.T;
-  const rsrc_t kc_rs = make_rsrc(static_cast<const char *>(a.kc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
-  const rsrc_t vc_rs = make_rsrc(static_cast<const char *>(a.vc) + cache_row0 * ROW_BYTES, n_occ * ROW_BYTES);
-  const rsrc_t kn_rs = make_rsrc(static_cast<const char *>(a.kn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
-  const rsrc_t vn_rs = make_rsrc(static_cast<const char *>(a.vn) + new_row0 * ROW_BYTES, a.T * ROW_BYTES);
-  auto lane_off = [&](int q, bool is_v) -> uint32_t {
-    const int row = (wave * 4 + q) * 4 + (lane >> 4);
-    const int c = is_v ? v_chunk_at(row, lane & 15) : kq_chunk_at(row, lane & 15);
-    return static_cast<uint32_t>(row * ROW_BYTES + 16 * c);
-  };
-  auto issue_tile = [&](int tile, char *dst, rsrc_t crs, rsrc_t nrs, bool is_v) {
-    const int j0 = (t_lo + tile) * 64;
-    if (j0 + 64 <= n_occ) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dma16(crs, lane_off(q, is_v), j0 * ROW_BYTES, dst + (wave * 4 + q) * 1024);
-    } else if (j0 >= n_occ) {  // chunk rows only
-#pragma unroll
-      for (int q = 0; q < 4; ++q)  // offset in voffset: rows past T fail the range check, read 0
-        dma16(nrs, lane_off(q, is_v) + (j0 - n_occ) * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
-    } else {  // the tile that straddles n_occ
-      const int dt = j0 - n_occ;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = (wave * 4 + q) * 4 + (lane >> 4);
-        const uint32_t lo = lane_off(q, is_v);
-        if (dt + row >= 0) {
-          dma16(nrs, lo + dt * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
-        } else {
-          dma16(crs, lo + j0 * ROW_BYTES, 0, dst + (wave * 4 + q) * 1024);
-        }
-      }
-    }
-  };
-
-  f32x4 o[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) o[k] = f32x4{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const int krow = 16 * wave + n;  // tile row of the lane's K operand
-
-  auto compute = [&](int t, const char *kb, const char *vb) {
-    const int j0 = (t_lo + t) * 64;
-    f32x4 c = f32x4{};
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds16(kb + kq_off(krow, 4 * st + g4)), qf[st], c, 0, 0, 0);
-    // c[i]: key j0 + 16*wave + 4*g4 + i of row n
-    if constexpr (LG) {
-      if (row_ok)
-        *reinterpret_cast<float4 *>(a.lg + (static_cast<size_t>(grp) * R + n) * a.lg_stride + j0 + 16 * wave +
-                                    4 * g4) = make_float4(c[0], c[1], c[2], c[3]);
-    }
-    // Tiles below n_occ need no mask: rows past R compute values that are
-    // never written.
-    if (j0 + 64 > n_occ) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ja = j0 + 16 * wave + 4 * g4 + i - n_occ;  // chunk index, < 0 for cache
-        c[i] = (row_ok && ja <= i_q) ? c[i] : -INFINITY;
-      }
-    }
-    float mx = __builtin_fmaxf(__builtin_fmaxf(c[0], c[1]), __builtin_fmaxf(c[2], c[3]));
-    mx = max_xor32(max_xor16(mx));
-    mx *= sl2;
-    if (mx > m_run + RESCALE_SLACK) {  // uniform across the row's four lanes
-      const float alpha = (m_run == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - mx);
-      l_run *= alpha;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) o[k] *= alpha;
-      m_run = mx;
-    }
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(c[i], sl2, neg_m));
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    const i16x4 pb = __builtin_bit_cast(
-        i16x4, make_uint2(pack_bf16_hw(p[0], p[1]), pack_bf16_hw(p[2], p[3])));
-    // V^T operand: d = 16*dblk + n, keys 16*wave + 4*g4 + 0..3
-    const int vrow = 16 * wave + 4 * g4 + (n >> 2);
-#pragma unroll
-    for (int dblk = 0; dblk < 8; ++dblk) {
-      const int col = 16 * dblk + 4 * (n & 3);
-      const i16x4 va = lds_tr(vb + v_off(vrow, col >> 3) + 2 * (col & 7));
-      o[dblk] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, o[dblk], 0, 0, 0);
-    }
-  };
-
-  if (ntiles > 0) {
-    issue_tile(0, kb0, kc_rs, kn_rs, false);
-    issue_tile(0, vb0, vc_rs, vn_rs, true);
-  }
-  for (int t = 0; t < ntiles; t += 2) {
-    wait_dma_and_sync();
-    if (t + 1 < ntiles) {
-      issue_tile(t + 1, kb1, kc_rs, kn_rs, false);
-      issue_tile(t + 1, vb1, vc_rs, vn_rs, true);
-    }
-    compute(t, kb0, vb0);
-    if (t + 1 >= ntiles) break;
-    wait_dma_and_sync();
-    if (t + 2 < ntiles) {
-      issue_tile(t + 2, kb0, kc_rs, kn_rs, false);
-      issue_tile(t + 2, vb0, vc_rs, vn_rs, true);
-    }
-    compute(t + 1, kb1, vb1);
-  }
-
-  // ---- merge the four wavefronts: M = max m_w, l = sum l_w 2^(m_w - M), O likewise ----
-  float l_w = l_run + __shfl_xor(l_run, 16);
-  l_w += __shfl_xor(l_w, 32);
-  if (g4 == 0) {
-    red_m[wave][n] = m_run;
-    red_l[wave][n] = l_w;
-  }
-  __syncthreads();  // also: every wavefront is done with the tiles
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = __builtin_fmaxf(M, red_m[w][n]);
-  const float my_scale = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - M);
-  // O^T of wavefront w: lane (n, g4), o[dblk][i] = O[row n][16*dblk + 4*g4 + i];
-  // staged as [16 rows][128] floats per wavefront, waves 0-1 in kb0, 2-3 in kb1
-  auto red_o = [&](int w) {
-    return reinterpret_cast<float *>(w < 2 ? kb0 : kb1) + (w & 1) * 16 * D;
-  };
-  {
-    float *mine = red_o(wave);
-#pragma unroll
-    for (int dblk = 0; dblk < 8; ++dblk)
-      *reinterpret_cast<float4 *>(mine + n * D + 16 * dblk + 4 * g4) =
-          make_float4(o[dblk][0] * my_scale, o[dblk][1] * my_scale, o[dblk][2] * my_scale, o[dblk][3] * my_scale);
-  }
-  __syncthreads();
-  // 256 threads: row tid / 16, d = 8 * (tid % 16) .. +7 (summed in wavefront order)
-  const int rr = tid >> 4, d0 = 8 * (tid & 15);
-  if (rr >= R) return;
-  const int ri = rr / a.qg, rh = g * a.qg + rr % a.qg;
-  const size_t lr = (static_cast<size_t>(b) * a.Hq + rh) * a.T + ri;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-#pragma unroll
-    for (int e4 = 0; e4 < 2; ++e4) {
-      const float4 v = *reinterpret_cast<const float4 *>(red_o(w) + rr * D + d0 + 4 * e4);
-      acc[4 * e4] += v.x;
-      acc[4 * e4 + 1] += v.y;
-      acc[4 * e4 + 2] += v.z;
-      acc[4 * e4 + 3] += v.w;
-    }
-  }
-  float Mr = -INFINITY, lr_tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) Mr = __builtin_fmaxf(Mr, red_m[w][rr]);
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const float mw = red_m[w][rr];
-    lr_tot += (mw == -INFINITY) ? 0.f : red_l[w][rr] * __builtin_amdgcn_exp2f(mw - Mr);
-  }
-  if (a.nsplit > 1) {
-    const size_t pr = static_cast<size_t>(split) * a.B * a.Hq * a.T + lr;
-    float *po = a.part + pr * D + d0;
-    *reinterpret_cast<float4 *>(po) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    *reinterpret_cast<float4 *>(po + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    if (d0 == 0) *reinterpret_cast<float2 *>(a.part_ml + 2 * pr) = make_float2(Mr, lr_tot);
-    return;
-  }
-  const float inv = 1.f / lr_tot;
-  uint16_t *orow = static_cast<uint16_t *>(a.out) + lr * D + d0;
-  *reinterpret_cast<uint4 *>(orow) =
-      make_uint4(pack_bf16_rne(acc[0] * inv, acc[1] * inv), pack_bf16_rne(acc[2] * inv, acc[3] * inv),
-                 pack_bf16_rne(acc[4] * inv, acc[5] * inv), pack_bf16_rne(acc[6] * inv, acc[7] * inv));
-  if (d0 == 0) {
-    const float L = Mr + log2f(lr_tot);
-    a.lse2[lr] = L;
-    if (a.lse_nat) a.lse_nat[lr] = L * 0.69314718055994530942f;
-  }
-}
-
 // Merge of the key splits of pass A: per row, M = max_s m_s,
 // l = sum_s l_s 2^(m_s - M), out = sum_s 2^(m_s - M) O_s / l, L = M + log2 l
 // (the same rescaling the online softmax applies between tiles).  A row is
@@ -1156,25 +924,23 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
   const int groups = a.B * a.Hkv;
   const int R = a.qg * a.T;
   const int nA = groups * ((R + 127) / 128) * a.nsplit;
+  hipError_t e;
   {
     KernelTimer timer(H2O_K_ATTN_A, s);
-    if (R <= 16) {  // short chunks: one 16-row block per group, keys split over the wavefronts
-      const int nD = groups * a.nsplit;
-      if (a.lg) {
-        hipLaunchKernelGGL(attn_a_dec<true>, dim3(nD), dim3(256), 0, s, a);
-      } else {
-        hipLaunchKernelGGL(attn_a_dec<false>, dim3(nD), dim3(256), 0, s, a);
-      }
-    } else if (R >= 256 && !a.lg) {  // long chunks: 256 rows per block share each tile
-      const int n8 = groups * ((R + 255) / 256) * a.nsplit;
-      hipLaunchKernelGGL((attn_a_native<false, 8>), dim3(n8), dim3(512), 0, s, a);
-    } else if (a.lg) {
-      hipLaunchKernelGGL((attn_a_native<true, 4>), dim3(nA), dim3(256), 0, s, a);
+    if (R <= 16) {  // short chunks: 16 keys of each tile per wavefront (attn_short.hip)
+      e = launch_attn_a_short_d128(a, s);
     } else {
-      hipLaunchKernelGGL((attn_a_native<false, 4>), dim3(nA), dim3(256), 0, s, a);
+      if (R >= 256 && !a.lg) {  // long chunks: 256 rows per block share each tile
+        const int n8 = groups * ((R + 255) / 256) * a.nsplit;
+        hipLaunchKernelGGL((attn_a_native<false, 8>), dim3(n8), dim3(512), 0, s, a);
+      } else if (a.lg) {
+        hipLaunchKernelGGL((attn_a_native<true, 4>), dim3(nA), dim3(256), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((attn_a_native<false, 4>), dim3(nA), dim3(256), 0, s, a);
+      }
+      e = hipGetLastError();
     }
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // with stored logits the weight-sum kernel also merges the key splits
   if (a.nsplit > 1 && !a.lg) {

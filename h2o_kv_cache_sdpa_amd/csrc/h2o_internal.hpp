@@ -115,6 +115,9 @@ hipError_t launch_attn_b_native(const AttnArgs &a, hipStream_t s);
 hipError_t launch_attn_b_logits(const AttnArgs &a, hipStream_t s);
 // Pass A alone for int8 / int4 caches, bf16, D = 128.
 hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s);
+// Pass A alone for short chunks (qg * T <= 16), bf16 queries, D = 128, every
+// cache format; the caller brackets it with its kernel timer.
+hipError_t launch_attn_a_short_d128(const AttnArgs &a, hipStream_t s);
 // Key splits pass A uses for these sizes (1 unless the row blocks alone
 // cannot fill the chip); the workspace must hold attn_split_floats() floats.
 int attn_splits(int B, int Hq, int Hkv, int D, int T, int n_occ, int dtype, int cache_fmt);
