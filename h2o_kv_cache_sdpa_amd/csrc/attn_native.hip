@@ -57,9 +57,8 @@ constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
 // Pass A: 128 packed query rows per block, 4 wavefronts x 32 rows
 // ---------------------------------------------------------------------------
 
-// LG: also store the raw logits of every tile (short chunks; a.lg).
 // NW: wavefronts per block (4 or 8), 32 rows each; a K/V tile serves them all.
-template <bool LG, int NW>
+template <int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
   constexpr int ROWS = 32 * NW;  // packed rows per block
   constexpr int SPW = 16 / NW;   // 1 KB DMA segments of a 16 KB tile per wavefront
@@ -191,9 +190,6 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_native(AttnArgs a) {
   auto tile_step = [&](int t, f32x16 c0, f32x16 c1, const char *kb_next, f32x16 &n0, f32x16 &n1,
                        const char *vb, auto &&dma) {
     const int j0 = (t_lo + t) * 64;
-    if constexpr (LG) {
-      if (row_ok) store_logits(a.lg + (static_cast<size_t>(grp) * R + my_row) * a.lg_stride + j0 + 8 * hl, c0, c1);
-    }
     if (wave_ragged || j0 + 63 - n_occ > wave_i_min) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -930,13 +926,11 @@ hipError_t launch_attn_native_d128(const AttnArgs &a, hipStream_t s) {
     if (R <= 16) {  // short chunks: 16 keys of each tile per wavefront (attn_short.hip)
       e = launch_attn_a_short_d128(a, s);
     } else {
-      if (R >= 256 && !a.lg) {  // long chunks: 256 rows per block share each tile
+      if (R >= 256) {  // long chunks: 256 rows per block share each tile
         const int n8 = groups * ((R + 255) / 256) * a.nsplit;
-        hipLaunchKernelGGL((attn_a_native<false, 8>), dim3(n8), dim3(512), 0, s, a);
-      } else if (a.lg) {
-        hipLaunchKernelGGL((attn_a_native<true, 4>), dim3(nA), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_a_native<8>), dim3(n8), dim3(512), 0, s, a);
       } else {
-        hipLaunchKernelGGL((attn_a_native<false, 4>), dim3(nA), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((attn_a_native<4>), dim3(nA), dim3(256), 0, s, a);
       }
       e = hipGetLastError();
     }

@@ -40,9 +40,8 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// LG: also store every tile's logits (in log2 units) for short chunks (a.lg).
 // NW: wavefronts per block (4 or 8), 32 rows each; a widened tile serves them all.
-template <int FMT, bool LG, int NW>
+template <int FMT, int NW>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
   constexpr int ROWS = 32 * NW;
   using Q = QTile<FMT>;
@@ -243,6 +242,9 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
       const float4 y = *reinterpret_cast<const float4 *>(&fac[row][base + 4]);
       return f32x8{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
     };
+    // The logits in log2 units relative to the running maximum, which the
+    // factor FMA subtracts (m_run = -inf: the logits themselves).
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     {
       const f32x8 s0a = fac8(0, 8 * hl), s0b = fac8(0, 16 + 8 * hl);
       const f32x8 s1a = fac8(0, 32 + 8 * hl), s1b = fac8(0, 48 + 8 * hl);
@@ -251,30 +253,27 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
           const f32x8 z0a = fac8(1, 8 * hl), z0b = fac8(1, 16 + 8 * hl);
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            c0[r] = fmaf(c0[r], s0a[r], z0a[r] * qsum);
-            c0[8 + r] = fmaf(c0[8 + r], s0b[r], z0b[r] * qsum);
+            c0[r] = fmaf(c0[r], s0a[r], fmaf(z0a[r], qsum, neg_m));
+            c0[8 + r] = fmaf(c0[8 + r], s0b[r], fmaf(z0b[r], qsum, neg_m));
           }
         }
         {
           const f32x8 z1a = fac8(1, 32 + 8 * hl), z1b = fac8(1, 48 + 8 * hl);
 #pragma unroll
           for (int r = 0; r < 8; ++r) {
-            c1[r] = fmaf(c1[r], s1a[r], z1a[r] * qsum);
-            c1[8 + r] = fmaf(c1[8 + r], s1b[r], z1b[r] * qsum);
+            c1[r] = fmaf(c1[r], s1a[r], fmaf(z1a[r], qsum, neg_m));
+            c1[8 + r] = fmaf(c1[8 + r], s1b[r], fmaf(z1b[r], qsum, neg_m));
           }
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          c0[r] *= s0a[r];
-          c0[8 + r] *= s0b[r];
-          c1[r] *= s1a[r];
-          c1[8 + r] *= s1b[r];
+          c0[r] = fmaf(c0[r], s0a[r], neg_m);
+          c0[8 + r] = fmaf(c0[8 + r], s0b[r], neg_m);
+          c1[r] = fmaf(c1[r], s1a[r], neg_m);
+          c1[8 + r] = fmaf(c1[8 + r], s1b[r], neg_m);
         }
       }
-    }
-    if constexpr (LG) {
-      if (row_ok) store_logits(a.lg + (static_cast<size_t>(grp) * R + my_row) * a.lg_stride + j0 + 8 * hl, c0, c1);
     }
     if (wave_ragged || j0 + 63 - n_occ > wave_i_min) {
 #pragma unroll
@@ -289,16 +288,24 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     for (int r = 1; r < 15; ++r) mx = __builtin_fmaxf(__builtin_fmaxf(mx, c1[r]), c0[r + 1]);
     mx = __builtin_fmaxf(mx, c1[15]);
     mx = max_xor32(mx);  // the other half-wave holds the other 32 keys of the lane's row
-    if (__ballot(mx > m_run + RESCALE_SLACK)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    // Lazy rescale, only when a row's maximum passes m_run + RESCALE_SLACK
+    // (or its first visible key arrives): m_run moves up by mx, and the
+    // tile's relative logits move down by the same amount.
+    const bool need = (m_run == -INFINITY) ? (mx != -INFINITY) : (mx > RESCALE_SLACK);
+    if (__ballot(need)) {
+      const float shift = need ? mx : 0.f;
+      const float alpha = (need && m_run != -INFINITY) ? __builtin_amdgcn_exp2f(-mx) : 1.f;
       l_run *= alpha;
       u_run *= alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[k] *= alpha;
-      m_run = m_new;
+      if (need) m_run = mx - neg_m;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        c0[r] -= shift;
+        c1[r] -= shift;
+      }
     }
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
     float ls = 0.f, us = 0.f;
     bf16x8 pb[4];
     {
@@ -313,10 +320,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        const float p00 = __builtin_amdgcn_exp2f(c0[r] + neg_m);
-        const float p01 = __builtin_amdgcn_exp2f(c0[8 + r] + neg_m);
-        const float p10 = __builtin_amdgcn_exp2f(c1[r] + neg_m);
-        const float p11 = __builtin_amdgcn_exp2f(c1[8 + r] + neg_m);
+        const float p00 = __builtin_amdgcn_exp2f(c0[r]);
+        const float p01 = __builtin_amdgcn_exp2f(c0[8 + r]);
+        const float p10 = __builtin_amdgcn_exp2f(c1[r]);
+        const float p11 = __builtin_amdgcn_exp2f(c1[8 + r]);
         ls += (p00 + p01) + (p10 + p11);
         if constexpr (FMT == FMT_INT4) {
           us = fmaf(p00, w0a[r], us);
@@ -440,13 +447,11 @@ hipError_t launch_attn_a_quant_d128(const AttnArgs &a, hipStream_t s) {
   if (R <= 16) return launch_attn_a_short_d128(a, s);  // short chunks: all formats, attn_short.hip
   auto launch_long = [&](auto fmt_tag) {
     constexpr int FMT = decltype(fmt_tag)::value;
-    if (a.lg) {
-      hipLaunchKernelGGL((attn_a_quant<FMT, true, 4>), dim3(nA), dim3(256), 0, s, a);
-    } else if (R >= 256) {  // long chunks: 256 rows per block share each widened tile
+    if (R >= 256) {  // long chunks: 256 rows per block share each widened tile
       const int n8 = groups * ((R + 255) / 256) * a.nsplit;
-      hipLaunchKernelGGL((attn_a_quant<FMT, false, 8>), dim3(n8), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((attn_a_quant<FMT, 8>), dim3(n8), dim3(512), 0, s, a);
     } else {
-      hipLaunchKernelGGL((attn_a_quant<FMT, false, 4>), dim3(nA), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((attn_a_quant<FMT, 4>), dim3(nA), dim3(256), 0, s, a);
     }
   };
   if (a.cache_fmt == FMT_INT8) {

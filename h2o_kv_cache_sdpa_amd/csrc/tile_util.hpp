@@ -122,20 +122,5 @@ __device__ __forceinline__ uint32_t pack_bf16_hw(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
-// Logits of one 64-key tile of S^T = K Q^T as laid out by the key permutation
-// above: register r of c0 holds key 16*(r/8) + 8*hl + r%8 of the tile, c1 the
-// same + 32, all for the lane's query row.  dst points at key 8*hl of the
-// tile in that row (16-byte aligned).
-__device__ __forceinline__ void store_logits(float *dst, const f32x16 &c0, const f32x16 &c1) {
-  auto st8 = [&](float *p, const f32x16 &c, int r0) {
-    *reinterpret_cast<float4 *>(p) = make_float4(c[r0], c[r0 + 1], c[r0 + 2], c[r0 + 3]);
-    *reinterpret_cast<float4 *>(p + 4) = make_float4(c[r0 + 4], c[r0 + 5], c[r0 + 6], c[r0 + 7]);
-  };
-  st8(dst, c0, 0);
-  st8(dst + 16, c0, 8);
-  st8(dst + 32, c1, 0);
-  st8(dst + 48, c1, 8);
-}
-
 }  // namespace
 }  // namespace h2o
