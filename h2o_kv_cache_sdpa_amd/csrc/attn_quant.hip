@@ -215,7 +215,11 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
 
   // One tile from the bf16 tiles: S^T = K Q^T, factors, mask, online softmax,
   // O^T += V^T (P s_v)^T.
-  auto compute_tile = [&](int tile, const char *kb, const char *vb, const float (*fac)[64]) {
+  // mid() runs right after the S MFMAs are issued: with 8 wavefronts it widens
+  // the next tile, whose vector and LDS work then overlaps this tile's matrix
+  // work (before, every wavefront widened first and then computed, so the two
+  // wavefronts of a SIMD were in the same phase at once).
+  auto compute_tile = [&](int tile, const char *kb, const char *vb, const float (*fac)[64], auto &&mid) {
     const int j0 = (t_lo + tile) * 64;
     uint32_t ka = k_lane;
     asm volatile("" : "+v"(ka));
@@ -236,6 +240,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
       k1 = nk1;
       __builtin_amdgcn_sched_barrier(0);
     }
+    mid();
+    __builtin_amdgcn_sched_barrier(0);
     // register r of c0 / c1 holds key 16*(r/8) + 8*hl + r%8 (+ 32 for c1)
     auto fac8 = [&](int row, int base) {
       const float4 x = *reinterpret_cast<const float4 *>(&fac[row][base]);
@@ -362,18 +368,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
       if (t + 1 < ntiles) issue_codes(t + 1, kc1, vc1, fc1);
       widen_tile(t, kc0, vc0, fc0, kb, vb, fac);
       lds_barrier();
-      compute_tile(t, kb, vb, fac);
+      compute_tile(t, kb, vb, fac, [] {});
       if (t + 1 >= ntiles) break;
       wait_dma_and_sync();  // codes(t+1) in slot 1
       if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
       widen_tile(t + 1, kc1, vc1, fc1, kb, vb, fac);
       lds_barrier();
-      compute_tile(t + 1, kb, vb, fac);
+      compute_tile(t + 1, kb, vb, fac, [] {});
     }
   } else {
     // ---- tile t (codes slot and bf16 buffer t & 1), one barrier each:
     //      [widen(t) done, codes(t+1) landed, compute(t-1) done] barrier,
-    //      DMA codes(t+2) into the slot widen(t) read, widen(t+1), compute(t)
+    //      DMA codes(t+2) into the slot widen(t) read, compute(t) with
+    //      widen(t+1) after its S MFMAs (buffer (t+1) & 1 was last read by
+    //      compute(t-1), before the barrier)
     if (ntiles > 0) {
       issue_codes(0, kc0, vc0, fc0);
       wait_dma_and_sync();
@@ -383,13 +391,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_a_quant(AttnArgs a) {
     for (int t = 0; t < ntiles; t += 2) {
       wait_dma_and_sync();
       if (t + 2 < ntiles) issue_codes(t + 2, kc0, vc0, fc0);
-      if (t + 1 < ntiles) widen_tile(t + 1, kc1, vc1, fc1, kbs[1], vbs[1], facs[1]);
-      compute_tile(t, kbs[0], vbs[0], facs[0]);
+      compute_tile(t, kbs[0], vbs[0], facs[0], [&] {
+        if (t + 1 < ntiles) widen_tile(t + 1, kc1, vc1, fc1, kbs[1], vbs[1], facs[1]);
+      });
       if (t + 1 >= ntiles) break;
       wait_dma_and_sync();
       if (t + 3 < ntiles) issue_codes(t + 3, kc1, vc1, fc1);
-      if (t + 2 < ntiles) widen_tile(t + 2, kc0, vc0, fc0, kbs[0], vbs[0], facs[0]);
-      compute_tile(t + 1, kbs[1], vbs[1], facs[1]);
+      compute_tile(t + 1, kbs[1], vbs[1], facs[1], [&] {
+        if (t + 2 < ntiles) widen_tile(t + 2, kc0, vc0, fc0, kbs[0], vbs[0], facs[0]);
+      });
     }
   }
 
