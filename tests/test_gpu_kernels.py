@@ -72,6 +72,11 @@ SDPA_CASES = [
     ("bf16", "int8", 1, 32, 8, 128, 8192, 1, 8192),     # int8 decode
     ("bf16", "int4", 1, 8, 2, 128, 900, 2, 64),
     ("bf16", "native", 1, 4, 1, 128, 64, 1, 0),         # one key in all
+    # capacities that are not a multiple of 4: each group's fp16 factor rows
+    # start 2-byte aligned (the short pass loads a lane's four factors at once)
+    ("bf16", "int8", 2, 16, 4, 128, 2051, 1, 2051),
+    ("bf16", "int4", 1, 16, 4, 128, 1999, 4, 1998),
+    ("bf16", "native", 1, 32, 8, 128, 3001, 2, 2999),
     # prefill: the first chunk fills an empty cache (a causal square)
     ("bf16", "native", 1, 8, 2, 128, 2048, 2048, 0),
     ("bf16", "int8", 1, 8, 2, 128, 1024, 1024, 0),
