@@ -198,6 +198,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void attn_a_short(AttnArgs a) {
     // already in log2 units for 8/4-bit ones.
     auto store_logits4 = [&] {
       if constexpr (LG) {
+        H2O_DEVICE_CHECK(grp < a.B * a.Hkv && j0 + kk0 + 3 < a.lg_stride);
         if (row_ok)
           *reinterpret_cast<float4 *>(a.lg + (static_cast<size_t>(grp) * R + n) * a.lg_stride + j0 + kk0) =
               make_float4(c[0], c[1], c[2], c[3]);
@@ -451,6 +452,7 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void attn_a_short(AttnArgs a) {
     lr_tot += (mw == -INFINITY) ? 0.f : red_l[w][rr] * __builtin_amdgcn_exp2f(mw - Mr);
   }
   const size_t plane = static_cast<size_t>(a.B) * a.Hq * a.T;
+  H2O_DEVICE_CHECK(lr < plane && split < a.nsplit);
   if (a.nsplit > 1) {
     const size_t pr = static_cast<size_t>(split) * plane + lr;
     float *po = a.part + pr * D + d0;
