@@ -77,6 +77,10 @@ SDPA_CASES = [
     ("bf16", "int8", 2, 16, 4, 128, 2051, 1, 2051),
     ("bf16", "int4", 1, 16, 4, 128, 1999, 4, 1998),
     ("bf16", "native", 1, 32, 8, 128, 3001, 2, 2999),
+    # short chunks with other group sizes: q_g = 1, 2, 8 (16 rows each)
+    ("bf16", "int4", 1, 8, 8, 128, 1000, 16, 1000),
+    ("bf16", "int8", 1, 16, 8, 128, 777, 8, 700),
+    ("bf16", "native", 1, 64, 8, 128, 1500, 2, 1500),
     # prefill: the first chunk fills an empty cache (a causal square)
     ("bf16", "native", 1, 8, 2, 128, 2048, 2048, 0),
     ("bf16", "int8", 1, 8, 2, 128, 1024, 1024, 0),
