@@ -58,8 +58,6 @@ __device__ __forceinline__ int kq_chunk_at(int row, int pos) { return pos ^ (row
 
 // V tile: chunk c of row r at r*256 + 16*(c ^ 4*(r & 3)) -- the 4 rows x 4
 // chunks a transpose read touches per half-wave land on 16 distinct groups.
-// (The short-chunk passes' transpose reads of 8 rows x 2 chunks meet 2 lanes
-// per bank: spreading those too cost the 128-row kernels registers.)
 __device__ __forceinline__ int v_off(int row, int chunk) {
   return row * ROW_BYTES + ((chunk ^ ((row & 3) << 2)) << 4);
 }
