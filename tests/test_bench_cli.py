@@ -24,3 +24,10 @@ def test_help_lists_every_mode():
     assert r.returncode == 0
     for flag in ("--sweep-small-t", "--prefill", "--backward", "--replay", "--policy", "--traffic-from"):
         assert flag in r.stdout
+
+
+def test_more_than_one_gpu_is_refused_in_every_mode():
+    for mode in (("--prefill",), ("--sweep-small-t",), ("--replay",), ("--backward",)):
+        r = _run("--gpus", "4", *mode)
+        assert r.returncode == 2, mode
+        assert json.loads(r.stdout.strip().splitlines()[-1])["n_gpus"] == 4
