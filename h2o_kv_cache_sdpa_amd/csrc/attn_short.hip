@@ -173,6 +173,9 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void attn_a_short(AttnArgs a) {
         s.v[i] = *reinterpret_cast<const uint32_t *>(vp);
       }
     }
+    // four consecutive fp16 factors, 8-byte aligned only when C % 4 == 0; the
+    // copy states 2-byte alignment and the compiler still issues one 8-byte load
+    // (the parity tests include capacities that are not a multiple of 4)
 #pragma unroll
     for (int f = 0; f < Sh::NF; ++f) __builtin_memcpy(&s.f[f], fsrc[f] + jw + 4 * g4, sizeof(uint2));
   };
