@@ -81,6 +81,10 @@ SDPA_CASES = [
     ("bf16", "int4", 1, 8, 8, 128, 1000, 16, 1000),
     ("bf16", "int8", 1, 16, 8, 128, 777, 8, 700),
     ("bf16", "native", 1, 64, 8, 128, 1500, 2, 1500),
+    # 8/4-bit short chunks with no full cache tile: an empty cache, and one
+    # tile that mixes cached codes with the chunk's own keys
+    ("bf16", "int8", 1, 8, 2, 128, 64, 1, 0),
+    ("bf16", "int4", 1, 8, 2, 128, 100, 3, 37),
     # prefill: the first chunk fills an empty cache (a causal square)
     ("bf16", "native", 1, 8, 2, 128, 2048, 2048, 0),
     ("bf16", "int8", 1, 8, 2, 128, 1024, 1024, 0),
