@@ -383,62 +383,64 @@ def _resident_setup(w, policy, dev):
 
 
 def sweep_small_t(args):
-    """HBM-bound regime: chunk lengths 1..128 on the 32K-slot cache."""
+    """HBM-bound regime: chunk lengths 1..128 on full caches (32K slots unless
+    --sweep-slots names other sizes)."""
     import torch
 
     from h2o_kv_cache_sdpa_amd import api
     from h2o_kv_cache_sdpa_amd import workloads as W
     dev = torch.device("cuda:0")
     base = W.WORKLOADS[3]
-    for fmt in args.sweep_fmts.split(","):
-        for T in (int(t) for t in args.sweep_ts.split(",")):
-            w = base.scaled(T=T, cache_fmt=fmt, name=f"small_t_{fmt}_32k_t{T}")
-            gc, chunks = _resident_setup(w, "h2o", dev)
-            out, wsum, slot_log = gc.new_outputs(w.C)
-            bufs = gc.bufs()
-            stream = torch.cuda.current_stream()
-            reps = args.sweep_reps
+    cases = [(fmt, C, T) for fmt in args.sweep_fmts.split(",") for C in (int(c) for c in args.sweep_slots.split(","))
+             for T in (int(t) for t in args.sweep_ts.split(","))]
+    for fmt, C, T in cases:
+        w = base.scaled(T=T, C=C, cache_fmt=fmt, name=f"small_t_{fmt}_{C // 1024}k_t{T}")
+        gc, chunks = _resident_setup(w, "h2o", dev)
+        out, wsum, slot_log = gc.new_outputs(w.C)
+        bufs = gc.bufs()
+        stream = torch.cuda.current_stream()
+        reps = args.sweep_reps
 
-            first = CheckOnce()
+        first = CheckOnce()
 
-            def step(i):
-                q, kn, vn = chunks[i % N_CHUNKS]
-                api.h2o_chunk_step(gc.dims, bufs, w.C, gc.pos, q, kn, vn, out, wsum, slot_log, gc.ws, stream,
-                               check=first(i))
-                gc.pos += T
+        def step(i):
+            q, kn, vn = chunks[i % N_CHUNKS]
+            api.h2o_chunk_step(gc.dims, bufs, w.C, gc.pos, q, kn, vn, out, wsum, slot_log, gc.ws, stream,
+                           check=first(i))
+            gc.pos += T
 
-            for i in range(min(10, reps)):
-                step(i)
-            torch.cuda.synchronize()
-            # step time without per-kernel events
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            t0 = time.perf_counter()
-            for i in range(reps):
-                step(i)
-            host_ms = (time.perf_counter() - t0) * 1e3 / reps
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            # per-kernel breakdown in a second, event-bracketed run
-            api.profile_reset()
-            api.profile_enable(True)
-            for i in range(reps):
-                step(i)
-            torch.cuda.synchronize()
-            api.profile_enable(False)
-            prof = api.profile_read()
-            nbytes = step_bytes(w, w.C)
-            print(json.dumps({
-                "sweep": "small_t", "workload": w.name, "cache_fmt": fmt, "chunk": T, "cache_slots": w.C,
-                "ms_per_step": ms, "tokens_per_s": w.B * T / (ms * 1e-3),
-                "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
-                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                "host_enqueue_ms": host_ms,
-                "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()},
-            }), flush=True)
-            del gc, chunks, out, wsum, slot_log
-            torch.cuda.empty_cache()
+        for i in range(min(10, reps)):
+            step(i)
+        torch.cuda.synchronize()
+        # step time without per-kernel events
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        t0 = time.perf_counter()
+        for i in range(reps):
+            step(i)
+        host_ms = (time.perf_counter() - t0) * 1e3 / reps
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        # per-kernel breakdown in a second, event-bracketed run
+        api.profile_reset()
+        api.profile_enable(True)
+        for i in range(reps):
+            step(i)
+        torch.cuda.synchronize()
+        api.profile_enable(False)
+        prof = api.profile_read()
+        nbytes = step_bytes(w, w.C)
+        print(json.dumps({
+            "sweep": "small_t", "workload": w.name, "cache_fmt": fmt, "chunk": T, "cache_slots": w.C,
+            "ms_per_step": ms, "tokens_per_s": w.B * T / (ms * 1e-3),
+            "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+            "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "host_enqueue_ms": host_ms,
+            "kernel_ms": {k: (v[0] / v[1] if v[1] else None) for k, v in prof.items()},
+        }), flush=True)
+        del gc, chunks, out, wsum, slot_log
+        torch.cuda.empty_cache()
 
 
 def replay(args):
@@ -662,6 +664,7 @@ def main():
     ap.add_argument("--sweep-fmts", default="native,int8,int4", help="cache formats of --sweep-small-t")
     ap.add_argument("--sweep-ts", default="1,4,16,64,128", help="chunk lengths of --sweep-small-t")
     ap.add_argument("--sweep-reps", type=int, default=200, help="timed steps per --sweep-small-t case")
+    ap.add_argument("--sweep-slots", default="32768", help="cache sizes (slots) of --sweep-small-t")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU only; the chunk step shards "
